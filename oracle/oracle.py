@@ -1,0 +1,221 @@
+"""ctypes wrapper around the plain-C NVFP4 oracle (``nvfp4_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg. The product path never imports it.
+
+Arrays are numpy; bf16 inputs must be widened to float32 by the caller (exact).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "nvfp4_oracle.c")
+LIB = os.path.join(HERE, "libnvfp4_oracle.so")
+
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc into ``oracle/libnvfp4_oracle.so``."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        f32 = ctypes.c_float
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [ctypes.c_int]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_bf16_rne.argtypes = [f32]
+        L.oracle_tensor_scale.restype = f32
+        L.oracle_tensor_scale.argtypes = [P, i64]
+        L.oracle_max_byte.restype = ctypes.c_int
+        L.oracle_max_byte.argtypes = [f32, f32]
+        L.oracle_e2m1_code.restype = ctypes.c_int
+        L.oracle_e2m1_code.argtypes = [f32, ctypes.c_int, f32]
+        L.oracle_dequant_value.restype = f32
+        L.oracle_dequant_value.argtypes = [ctypes.c_int, ctypes.c_int, f32]
+        L.oracle_scales_max.restype = None
+        L.oracle_scales_max.argtypes = [P, i64, i64, f32, P]
+        L.oracle_quantize.restype = None
+        L.oracle_quantize.argtypes = [P, i64, i64, f32, P, P]
+        L.oracle_dequantize.restype = None
+        L.oracle_dequantize.argtypes = [P, P, i64, i64, f32, P]
+        L.oracle_block_sq_error.restype = f32
+        L.oracle_block_sq_error.argtypes = [P, ctypes.c_int, f32]
+        L.oracle_scales_mse.restype = None
+        L.oracle_scales_mse.argtypes = [P, i64, i64, f32, P, P]
+        L.oracle_block_hessian.restype = None
+        L.oracle_block_hessian.argtypes = [P, i64, i64, P, i64, P]
+        L.oracle_block_lh_objective.restype = ctypes.c_double
+        L.oracle_block_lh_objective.argtypes = [P, ctypes.c_int, f32, P]
+        L.oracle_scales_local_hessian.restype = None
+        L.oracle_scales_local_hessian.argtypes = [P, i64, i64, f32, P, P, P]
+        L.oracle_route_groups.restype = ctypes.c_int
+        L.oracle_route_groups.argtypes = [P, i64, i64, i64, P, P]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    return a
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().oracle_e4m3_value(int(byte))
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(int(code))
+
+
+def bf16_rne(f: float) -> int:
+    return lib().oracle_bf16_rne(float(np.float32(f)))
+
+
+def bf16_rne_array(y: np.ndarray) -> np.ndarray:
+    """Vector form of the oracle's bf16 rounding (calls the C routine element by element)."""
+    flat = _f32(y).ravel()
+    out = np.empty(flat.size, dtype=np.uint16)
+    f = lib().oracle_bf16_rne
+    for i in range(flat.size):
+        out[i] = f(float(flat[i]))
+    return out.reshape(np.shape(y))
+
+
+def tensor_scale(x) -> np.float32:
+    a = _f32(x)
+    return np.float32(lib().oracle_tensor_scale(_p(a), a.size))
+
+
+def max_byte(amax: float, S: float) -> int:
+    return lib().oracle_max_byte(float(np.float32(amax)), float(np.float32(S)))
+
+
+def e2m1_code(x: float, byte: int, S: float) -> int:
+    return lib().oracle_e2m1_code(float(np.float32(x)), int(byte), float(np.float32(S)))
+
+
+def dequant_value(code: int, byte: int, S: float) -> np.float32:
+    return np.float32(lib().oracle_dequant_value(int(code), int(byte), float(np.float32(S))))
+
+
+def scales_max(x, S) -> np.ndarray:
+    a = _f32(x)
+    rows, cols = a.shape
+    out = np.empty((rows, cols // 16), dtype=np.uint8)
+    lib().oracle_scales_max(_p(a), rows, cols, float(np.float32(S)), _p(out))
+    return out
+
+
+def quantize(x, S, scales) -> np.ndarray:
+    a = _f32(x)
+    rows, cols = a.shape
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((rows, cols // 2), dtype=np.uint8)
+    lib().oracle_quantize(_p(a), rows, cols, float(np.float32(S)), _p(sc), _p(out))
+    return out
+
+
+def dequantize(codes, scales, S, rows, cols) -> np.ndarray:
+    cd = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.empty((rows, cols), dtype=np.float32)
+    lib().oracle_dequantize(_p(cd), _p(sc), rows, cols, float(np.float32(S)), _p(out))
+    return out
+
+
+def fakequant(x, S, scales=None):
+    """Returns (dequantised fp32, codes, scales); max scaling when scales is None."""
+    a = _f32(x)
+    rows, cols = a.shape
+    sc = scales_max(a, S) if scales is None else np.ascontiguousarray(scales, dtype=np.uint8)
+    cd = quantize(a, S, sc)
+    return dequantize(cd, sc, S, rows, cols), cd, sc
+
+
+def block_sq_error(x16, byte, S) -> np.float32:
+    a = _f32(x16)
+    return np.float32(lib().oracle_block_sq_error(_p(a), int(byte), float(np.float32(S))))
+
+
+def scales_mse(w, S, with_obj: bool = False):
+    a = _f32(w)
+    rows, cols = a.shape
+    out = np.empty((rows, cols // 16), dtype=np.uint8)
+    obj = np.empty((rows, cols // 16), dtype=np.float32)
+    lib().oracle_scales_mse(_p(a), rows, cols, float(np.float32(S)), _p(out), _p(obj))
+    return (out, obj) if with_obj else out
+
+
+def block_hessian(X, token_ids=None) -> np.ndarray:
+    """fp64 H [cols/16, 16, 16] of X [tokens, cols] (optionally only the rows token_ids)."""
+    a = _f32(X)
+    tokens, cols = a.shape
+    H = np.empty((cols // 16, 16, 16), dtype=np.float64)
+    if token_ids is None:
+        lib().oracle_block_hessian(_p(a), tokens, cols, None, 0, _p(H))
+    else:
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        lib().oracle_block_hessian(_p(a), tokens, cols, _p(ids), ids.size, _p(H))
+    return H
+
+
+def block_lh_objective(w16, byte, S, Hb) -> float:
+    a = _f32(w16)
+    h = _f32(Hb)
+    return lib().oracle_block_lh_objective(_p(a), int(byte), float(np.float32(S)), _p(h))
+
+
+def scales_local_hessian(w, S, H, with_obj: bool = False):
+    a = _f32(w)
+    rows, cols = a.shape
+    h = _f32(H)
+    assert h.size == (cols // 16) * 256
+    out = np.empty((rows, cols // 16), dtype=np.uint8)
+    obj = np.empty((rows, cols // 16), dtype=np.float64)
+    lib().oracle_scales_local_hessian(_p(a), rows, cols, float(np.float32(S)), _p(h),
+                                      _p(out), _p(obj))
+    return (out, obj) if with_obj else out
+
+
+def route_groups(expert_ids, experts: int):
+    ids = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    tokens, topk = ids.shape
+    offsets = np.empty(experts + 1, dtype=np.int32)
+    tok = np.empty(tokens * topk, dtype=np.int32)
+    rc = lib().oracle_route_groups(_p(ids), tokens, topk, experts, _p(offsets), _p(tok))
+    if rc != 0:
+        raise ValueError("expert id out of range")
+    return offsets, tok
