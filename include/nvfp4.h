@@ -1,0 +1,184 @@
+/*
+ * libnvfp4 — NVFP4 quantisation and block-scale selection on AMD Instinct MI355X (gfx950).
+ *
+ * NVFP4 stores a tensor as 4-bit E2M1 codes in blocks of 16 consecutive values, one FP8
+ * (E4M3) scale per block and one FP32 scale per tensor. Pages this library follows
+ * (titles translated):
+ *  [QAD] "Why NVFP4 inference loses accuracy, and what QAD actually repairs"
+ *        (czchanglian.com/news/46648), sections 1, 2.1, 2.3, 3.2, 4.2;
+ *  [BT]  "Baseten on high-quality NVFP4 quantization" (attain.fans translation),
+ *        sections "Why do we need a scale", "Block scaling", "Why blocks";
+ *  [LH]  "How much dumber does 4-bit make a model? The answer is in the scale shared by
+ *        every 16 weights" (2kiu.com/news/4970560), a write-up of NVIDIA Model Optimizer's
+ *        "Improving NVFP4 Accuracy with Local-Hessian Weight Scales": sections "NVFP4
+ *        structure", the paragraph on max / Four-Over-Six / MSE selection, and "Change the
+ *        objective".
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller; nothing is allocated,
+ *    retained or freed by the library. Host-side validation happens before any launch.
+ *  - Layout is row-major and contiguous. `cols` is the contiguous dimension and must be a
+ *    multiple of 16; blocks are 16 consecutive values along it ([BT] "Block scaling").
+ *    `batch` stacks independent tensors of identical shape (e.g. MoE experts); each has
+ *    its own tensor scale S[batch].
+ *  - Element tensors (x, w, y) must be 16-byte aligned; packed codes 8-byte aligned.
+ *  - Block scales are E4M3FN bytes [batch][rows][cols/16]: 0x01..0x7E are the 126
+ *    positive candidates of [LH]; 0x00 marks an all-zero block.
+ *  - Codes are packed two per byte [batch][rows][cols/2]: element 2j in the low nibble of
+ *    byte j. A code is sign<<3 | k, with k indexing {0, 0.5, 1, 1.5, 2, 3, 4, 6}
+ *    ([BT] "Why do we need a scale"); a zero magnitude never carries the sign bit.
+ *  - Rounding: the block byte is the E4M3 value nearest to amax_b/(6 S) ([QAD] 2.3),
+ *    saturating at 448 ([QAD] 4.2) and at least 0x01 for a non-zero block; an element's
+ *    code is the E2M1 value nearest to |x|/(s S) ([QAD] 2.1), saturating at 6. Both are
+ *    decided on the exact real quotient, ties to the even byte / even grid index.
+ *  - Dequantised value: +-fp32(G_k * s * S), one rounding of the exact product; bf16
+ *    output rounds that to nearest-even.
+ *  - Inputs must be finite; the tensor scale S must be a positive normal fp32 number.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Every call is asynchronous on it.
+ *  - Return value: NVFP4_OK or an error code below. Calls with an empty tensor (a zero
+ *    dimension) validate their shape and return NVFP4_OK without launching.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define NVFP4_API __attribute__((visibility("default")))
+#else
+#define NVFP4_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element dtypes */
+#define NVFP4_DTYPE_F32 0
+#define NVFP4_DTYPE_BF16 1
+
+/* status codes */
+#define NVFP4_OK 0
+#define NVFP4_ERR_NULL 1      /* a required pointer is NULL */
+#define NVFP4_ERR_SHAPE 2     /* negative dimension, cols % 16 != 0, or size overflow */
+#define NVFP4_ERR_DTYPE 3     /* unknown dtype */
+#define NVFP4_ERR_ALIGN 4     /* a pointer lacks the alignment stated above */
+#define NVFP4_ERR_WORKSPACE 5 /* workspace NULL or smaller than *_workspace_size */
+#define NVFP4_ERR_HIP 6       /* a HIP launch failed */
+#define NVFP4_ERR_ARG 7       /* another argument is out of range */
+
+/* Human-readable name of a status code (static string). */
+NVFP4_API const char *nvfp4_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+NVFP4_API int nvfp4_version(void);
+
+/*
+ * Per-tensor FP32 scale ([BT] "Why do we need a scale": a second, FP32 scaling level
+ * exists; its formula is not given there). For each b < batch:
+ *   S[b] = fp32(amax(|x[b]|) / 2688), 2688 = 6 * 448, so the largest block maps onto the
+ *   top E4M3 value; S[b] = 1 for an all-zero tensor; raised to FLT_MIN if smaller.
+ * x: [batch][n] elements of `dtype`, 16-byte aligned, n % 8 == 0. S: [batch] fp32 (out).
+ */
+NVFP4_API int nvfp4_global_scale(const void *x, int dtype, int64_t batch, int64_t n, float *S,
+                       void *stream);
+
+/*
+ * Max scaling ([QAD] 2.3, [LH] default selector): block byte = E4M3 nearest to
+ * amax_b / (6 S[b]). w: [batch][rows][cols]; S: [batch]; scales: [batch][rows][cols/16].
+ */
+NVFP4_API int nvfp4_scale_search_max(const void *w, int dtype, int64_t batch, int64_t rows,
+                           int64_t cols, const float *S, uint8_t *scales, void *stream);
+
+/*
+ * MSE scale search ([LH] paragraph on the MSE selector): every block tries all 126
+ * positive E4M3 bytes and keeps the first with the smallest squared weight error,
+ *   obj(c) = fp32 sum over i = 0..15 of e_i^2, e_i = fp32(dq_i(c) - w_i),
+ *   accumulated as acc = fmaf(e_i, e_i, acc) in ascending i.
+ * An all-zero block gets byte 0x00 and objective 0. obj (nullable): [batch][rows][cols/16]
+ * fp32, the winning objective.
+ */
+NVFP4_API int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, int64_t rows,
+                           int64_t cols, const float *S, uint8_t *scales, float *obj,
+                           void *stream);
+
+/*
+ * Block-diagonal calibration Gram matrix ([LH] "Change the objective": the output error
+ * ||dX||^2 = tr(d XX^T d^T) is weighted by XX^T; only its 16x16 diagonal blocks are kept):
+ *   H[g][b][i][j] (+)= sum over the tokens t of group g of x[t][16b+i] * x[t][16b+j].
+ * x: [tokens][cols] (one token per row; bf16 products are exact, accumulation is fp32).
+ * Dense form: groups == 1, group_offsets == NULL, token_ids == NULL (all tokens).
+ * Grouped form (MoE experts): group_offsets [groups+1] (device, non-decreasing, last
+ *   equal to n_ids) and token_ids [n_ids] (device, each in [0, tokens)); group g sums
+ *   rows token_ids[group_offsets[g] .. group_offsets[g+1]).
+ * H: [groups][cols/16][16][16] fp32 (out). accumulate != 0 adds to the existing H.
+ * The workspace holds per-chunk partial sums, reduced in a fixed order, so results are
+ * bitwise reproducible. workspace_bytes must be >= nvfp4_block_hessian_workspace_size().
+ */
+NVFP4_API size_t nvfp4_block_hessian_workspace_size(int64_t tokens, int64_t cols, int64_t groups,
+                                          int64_t n_ids);
+NVFP4_API int nvfp4_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
+                        int64_t groups, const int32_t *group_offsets,
+                        const int32_t *token_ids, int64_t n_ids, float *H, int accumulate,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Local-Hessian scale search ([LH] "Change the objective"): for every (row, block) of
+ * every batch entry, all 126 positive E4M3 bytes are tried and the first with the
+ * smallest d H_b d^T wins, with d_i = fp32(dq_i(c) - w_i) and H_b the block's 16x16
+ * matrix shared by all rows (the block-diagonal approximation). The objective is
+ * evaluated as y_i = sum_j H_ij d_j, obj = sum_i d_i y_i in double precision, ascending
+ * indices, separate multiply and add. A block with an all-zero H_b takes the MSE choice
+ * (objective reported as 0); an all-zero block gets 0x00.
+ * w: [batch][rows][cols]; S: [batch]; H: [batch][cols/16][16][16] fp32;
+ * scales: [batch][rows][cols/16]; obj (nullable): same shape, double.
+ */
+NVFP4_API int nvfp4_scale_search_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows,
+                                     int64_t cols, const float *S, const float *H,
+                                     uint8_t *scales, double *obj, void *stream);
+
+/*
+ * Quantise to NVFP4 ([QAD] 1, 2.1; [BT] "Block scaling"): codes from the given block bytes
+ * (scales_in != NULL, e.g. chosen by a search) or from max scaling (scales_in == NULL, in
+ * which case the chosen bytes are written to scales_out when it is non-NULL).
+ * codes: [batch][rows][cols/2] packed.
+ */
+NVFP4_API int nvfp4_quantize(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                   const float *S, const uint8_t *scales_in, uint8_t *codes,
+                   uint8_t *scales_out, void *stream);
+
+/*
+ * Dequantise packed codes ([QAD] 3.2: value times scale) into y of out_dtype.
+ */
+NVFP4_API int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *S,
+                     int64_t batch, int64_t rows, int64_t cols, void *y, int out_dtype,
+                     void *stream);
+
+/*
+ * Fake quantisation, the quantise -> dequantise round trip of [QAD] 3.2 in one pass:
+ * y has the dtype and shape of x. Block bytes as in nvfp4_quantize. codes_out and
+ * scales_out are optional (nullable) side outputs.
+ */
+NVFP4_API int nvfp4_fakequant(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                    const float *S, const uint8_t *scales_in, void *y, uint8_t *codes_out,
+                    uint8_t *scales_out, void *stream);
+
+/*
+ * Routing groups for per-expert Hessians: from a top-k routing table expert_ids
+ * [tokens][topk] (device int32), write offsets [experts+1] (prefix sums of per-expert
+ * counts) and token_ids [tokens*topk] with every expert's tokens in ascending token order
+ * (a stable counting sort). Ids outside [0, experts) are skipped (not routed); the tail
+ * of token_ids beyond offsets[experts] is then left unwritten.
+ * workspace_bytes must be >= nvfp4_route_groups_workspace_size().
+ */
+NVFP4_API size_t nvfp4_route_groups_workspace_size(int64_t tokens, int64_t topk, int64_t experts);
+NVFP4_API int nvfp4_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk,
+                       int64_t experts, int32_t *offsets, int32_t *token_ids,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -93,6 +93,11 @@ uint16_t oracle_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+void oracle_bf16_rne_array(const float *y, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_rne(y[i]);
+}
+
 /* Per-tensor FP32 scale ([BT] "Why do we need a scale": a second, FP32 level exists;
  * the formula is a reading: the largest block of the tensor maps to E4M3's top). */
 float oracle_tensor_scale(const float *x, int64_t n)

@@ -47,6 +47,8 @@ def lib():
         L.oracle_e2m1_value.argtypes = [ctypes.c_int]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_bf16_rne.argtypes = [f32]
+        L.oracle_bf16_rne_array.restype = None
+        L.oracle_bf16_rne_array.argtypes = [P, i64, P]
         L.oracle_tensor_scale.restype = f32
         L.oracle_tensor_scale.argtypes = [P, i64]
         L.oracle_max_byte.restype = ctypes.c_int
@@ -105,12 +107,10 @@ def bf16_rne(f: float) -> int:
 
 
 def bf16_rne_array(y: np.ndarray) -> np.ndarray:
-    """Vector form of the oracle's bf16 rounding (calls the C routine element by element)."""
+    """bf16 bit patterns (uint16) of fp32 values, rounded to nearest-even."""
     flat = _f32(y).ravel()
     out = np.empty(flat.size, dtype=np.uint16)
-    f = lib().oracle_bf16_rne
-    for i in range(flat.size):
-        out[i] = f(float(flat[i]))
+    lib().oracle_bf16_rne_array(_p(flat), flat.size, _p(out))
     return out.reshape(np.shape(y))
 
 

@@ -1,0 +1,194 @@
+// C-ABI entry points of libnvfp4 (declared in include/nvfp4.h). Each validates its
+// arguments on the host — dtype, shape, pointer presence and alignment, workspace size —
+// before anything is launched, then forwards to the kernel launchers.
+#include <limits.h>
+
+#include "nvfp4_internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxGridY = 65535;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// shape checks shared by the tensor entry points; *empty is set if there is nothing to do
+int check_tensor(int dtype, int64_t batch, int64_t rows, int64_t cols, bool *empty) {
+  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+  if (batch < 0 || rows < 0 || cols < 0 || (cols % 16) != 0) return NVFP4_ERR_SHAPE;
+  int64_t n1, n2, bytes;
+  if (!mul_ok(batch, rows, &n1) || !mul_ok(n1, cols, &n2) || !mul_ok(n2, 4, &bytes))
+    return NVFP4_ERR_SHAPE;
+  if (batch > kMaxGridY) return NVFP4_ERR_SHAPE;
+  *empty = (n2 == 0);
+  return NVFP4_OK;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: bad dimension (negative, cols % 16 != 0, or too large)";
+    case NVFP4_ERR_DTYPE: return "NVFP4_ERR_DTYPE: unknown dtype";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: pointer not aligned (16 B elements, 8 B codes)";
+    case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace missing or too small";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP: a HIP launch failed";
+    case NVFP4_ERR_ARG: return "NVFP4_ERR_ARG: argument out of range";
+    default: return "unknown nvfp4 status";
+  }
+}
+
+int nvfp4_version(void) { return 100; }
+
+int nvfp4_global_scale(const void *x, int dtype, int64_t batch, int64_t n, float *S, void *stream) {
+  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+  if (batch < 0 || n < 0 || (n % 8) != 0 || batch > kMaxGridY) return NVFP4_ERR_SHAPE;
+  int64_t tot, bytes;
+  if (!mul_ok(batch, n, &tot) || !mul_ok(tot, 4, &bytes)) return NVFP4_ERR_SHAPE;
+  if (batch == 0) return NVFP4_OK;
+  if (!S || (n > 0 && !x)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(S, 4)) return NVFP4_ERR_ALIGN;
+  return launch_global_scale(x, dtype, batch, n, S, as_stream(stream));
+}
+
+int nvfp4_scale_search_max(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                           const float *S, uint8_t *scales, void *stream) {
+  bool empty = false;
+  int rc = check_tensor(dtype, batch, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!w || !S || !scales) return NVFP4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(S, 4)) return NVFP4_ERR_ALIGN;
+  return launch_quant(w, dtype, batch, rows, cols, S, nullptr, nullptr, scales, nullptr,
+                      as_stream(stream));
+}
+
+int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                           const float *S, uint8_t *scales, float *obj, void *stream) {
+  bool empty = false;
+  int rc = check_tensor(dtype, batch, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!w || !S || !scales) return NVFP4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(S, 4) || !aligned(obj, 4)) return NVFP4_ERR_ALIGN;
+  if (rows * (cols / 16) / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
+  return launch_mse(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
+}
+
+size_t nvfp4_block_hessian_workspace_size(int64_t tokens, int64_t cols, int64_t groups,
+                                          int64_t n_ids) {
+  if (tokens < 0 || cols < 0 || groups < 0 || n_ids < 0) return 0;
+  const size_t dense = hessian_workspace_size(tokens, cols, groups, -1);
+  const size_t grouped = hessian_workspace_size(tokens, cols, groups, n_ids);
+  return dense > grouped ? dense : grouped;
+}
+
+int nvfp4_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t groups,
+                        const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
+                        float *H, int accumulate, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+  if (tokens < 0 || cols < 0 || (cols % 16) != 0 || groups < 0 || n_ids < 0)
+    return NVFP4_ERR_SHAPE;
+  int64_t t1, t2;
+  if (!mul_ok(tokens, cols, &t1) || !mul_ok(t1, 4, &t2)) return NVFP4_ERR_SHAPE;
+  if (groups > kMaxGridY || n_ids > INT32_MAX || tokens > INT32_MAX) return NVFP4_ERR_SHAPE;
+  const bool grouped = group_offsets != nullptr || token_ids != nullptr;
+  if (grouped && (!group_offsets || !token_ids)) return NVFP4_ERR_NULL;
+  if (!grouped && groups != 1) return NVFP4_ERR_ARG;
+  if (cols == 0 || groups == 0) return NVFP4_OK;
+  if (!H || (tokens > 0 && !x)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(H, 4) || !aligned(group_offsets, 4) || !aligned(token_ids, 4))
+    return NVFP4_ERR_ALIGN;
+  const size_t need = nvfp4_block_hessian_workspace_size(tokens, cols, groups, n_ids);
+  if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  return launch_block_hessian(x, dtype, tokens, cols, groups, grouped ? group_offsets : nullptr,
+                              grouped ? token_ids : nullptr, n_ids, H, accumulate, workspace,
+                              as_stream(stream));
+}
+
+int nvfp4_scale_search_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows,
+                                     int64_t cols, const float *S, const float *H, uint8_t *scales,
+                                     double *obj, void *stream) {
+  bool empty = false;
+  int rc = check_tensor(dtype, batch, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!w || !S || !H || !scales) return NVFP4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(S, 4) || !aligned(H, 4) || !aligned(obj, 8))
+    return NVFP4_ERR_ALIGN;
+  if (cols / 16 > kMaxGridY || rows / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
+  return launch_local_hessian(w, dtype, batch, rows, cols, S, H, scales, obj, as_stream(stream));
+}
+
+int nvfp4_quantize(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                   const float *S, const uint8_t *scales_in, uint8_t *codes, uint8_t *scales_out,
+                   void *stream) {
+  bool empty = false;
+  int rc = check_tensor(dtype, batch, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!x || !S || !codes) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(S, 4) || !aligned(codes, 8)) return NVFP4_ERR_ALIGN;
+  return launch_quant(x, dtype, batch, rows, cols, S, scales_in, codes,
+                      scales_in ? nullptr : scales_out, nullptr, as_stream(stream));
+}
+
+int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *S, int64_t batch,
+                     int64_t rows, int64_t cols, void *y, int out_dtype, void *stream) {
+  bool empty = false;
+  int rc = check_tensor(out_dtype, batch, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!codes || !scales || !S || !y) return NVFP4_ERR_NULL;
+  if (!aligned(codes, 8) || !aligned(S, 4) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  return launch_dequant(codes, scales, S, batch, rows, cols, y, out_dtype, as_stream(stream));
+}
+
+int nvfp4_fakequant(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                    const float *S, const uint8_t *scales_in, void *y, uint8_t *codes_out,
+                    uint8_t *scales_out, void *stream) {
+  bool empty = false;
+  int rc = check_tensor(dtype, batch, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!x || !S || !y) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(S, 4) || !aligned(y, 16) || !aligned(codes_out, 8))
+    return NVFP4_ERR_ALIGN;
+  return launch_quant(x, dtype, batch, rows, cols, S, scales_in, codes_out,
+                      scales_in ? nullptr : scales_out, y, as_stream(stream));
+}
+
+size_t nvfp4_route_groups_workspace_size(int64_t tokens, int64_t topk, int64_t experts) {
+  if (tokens < 0 || topk < 0 || experts < 0) return 0;
+  return route_workspace_size(tokens, topk, experts);
+}
+
+int nvfp4_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk, int64_t experts,
+                       int32_t *offsets, int32_t *token_ids, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  if (tokens < 0 || topk < 0 || experts <= 0) return NVFP4_ERR_SHAPE;
+  if (experts > 16384) return NVFP4_ERR_ARG;
+  int64_t pairs;
+  if (!mul_ok(tokens, topk, &pairs) || pairs > INT32_MAX) return NVFP4_ERR_SHAPE;
+  if (!offsets) return NVFP4_ERR_NULL;
+  if (pairs > 0 && (!expert_ids || !token_ids)) return NVFP4_ERR_NULL;
+  if (!aligned(expert_ids, 4) || !aligned(offsets, 4) || !aligned(token_ids, 4))
+    return NVFP4_ERR_ALIGN;
+  const size_t need = route_workspace_size(tokens, topk, experts);
+  if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return NVFP4_ERR_ALIGN;
+  return launch_route_groups(expert_ids, tokens, topk, experts, offsets, token_ids, workspace,
+                             as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,251 @@
+"""Python binding of libnvfp4 (ctypes): argument marshalling only.
+
+Every function takes and returns torch tensors on the GPU; the computation runs in the
+HIP kernels behind the C ABI declared in ``include/nvfp4.h``. torch supplies device memory
+(outputs and workspaces are allocated with torch) and the current stream. There is no
+CPU fallback: if the library has not been built, loading it raises.
+
+Shapes: element tensors are [rows, cols] or [batch, rows, cols] (cols % 16 == 0), bf16 or
+fp32. Tensor scales S are fp32 [batch] on the same device. Block scales are uint8
+[batch, rows, cols/16] (squeezed like the input), packed codes uint8 [..., cols/2].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "nvfp4.h")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "nvfp4_status_string": (ctypes.c_char_p, [_I]),
+    "nvfp4_version": (_I, []),
+    "nvfp4_global_scale": (_I, [_P, _I, _I64, _I64, _P, _P]),
+    "nvfp4_scale_search_max": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P]),
+    "nvfp4_scale_search_mse": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_block_hessian_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
+    "nvfp4_block_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P, _SZ, _P]),
+    "nvfp4_scale_search_local_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
+    "nvfp4_fakequant": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "nvfp4_route_groups_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "nvfp4_route_groups": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
+}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """Load libnvfp4.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -m scale_search_weights_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Names of every entry point declared in include/nvfp4.h."""
+    with open(HEADER) as f:
+        txt = f.read()
+    return sorted(set(re.findall(r"NVFP4_API\s+[\w\s\*]*?\b(nvfp4_\w+)\s*\(", txt)))
+
+
+def status_string(status: int) -> str:
+    return lib().nvfp4_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise NVFP4Error(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _shape3(t: torch.Tensor):
+    if t.dim() == 2:
+        return 1, t.shape[0], t.shape[1]
+    if t.dim() == 3:
+        return t.shape[0], t.shape[1], t.shape[2]
+    raise ValueError("expected a [rows, cols] or [batch, rows, cols] tensor")
+
+
+def _out_shape(t: torch.Tensor, last: int):
+    return tuple(t.shape[:-1]) + (last,)
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def global_scale(x: torch.Tensor) -> torch.Tensor:
+    """S[b] = fp32(amax(|x[b]|) / 2688) per batch entry (2-D input: one scale)."""
+    _need(x, "x")
+    batch = x.shape[0] if x.dim() == 3 else 1
+    n = x.numel() // max(batch, 1)
+    S = torch.empty(batch, dtype=torch.float32, device=x.device)
+    _check(lib().nvfp4_global_scale(_ptr(x), _dt(x), batch, n, _ptr(S), _stream()),
+           "nvfp4_global_scale")
+    return S
+
+
+def scale_search_max(w: torch.Tensor, S: torch.Tensor) -> torch.Tensor:
+    _need(w, "w")
+    b, r, c = _shape3(w)
+    sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
+    _check(lib().nvfp4_scale_search_max(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(sc), _stream()),
+           "nvfp4_scale_search_max")
+    return sc
+
+
+def scale_search_mse(w: torch.Tensor, S: torch.Tensor, return_obj: bool = False):
+    _need(w, "w")
+    b, r, c = _shape3(w)
+    sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
+    obj = torch.empty(_out_shape(w, c // 16), dtype=torch.float32, device=w.device) if return_obj else None
+    _check(lib().nvfp4_scale_search_mse(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(sc), _ptr(obj),
+                                        _stream()), "nvfp4_scale_search_mse")
+    return (sc, obj) if return_obj else sc
+
+
+def block_hessian_workspace_size(tokens: int, cols: int, groups: int = 1, n_ids: int = 0) -> int:
+    return int(lib().nvfp4_block_hessian_workspace_size(tokens, cols, groups, n_ids))
+
+
+def block_hessian(x: torch.Tensor, group_offsets: torch.Tensor | None = None,
+                  token_ids: torch.Tensor | None = None, H: torch.Tensor | None = None,
+                  accumulate: bool = False, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Block-diagonal Gram matrices of x [tokens, cols]: [cols/16, 16, 16] (dense) or
+    [groups, cols/16, 16, 16] (grouped by group_offsets / token_ids)."""
+    _need(x, "x")
+    tokens, cols = x.shape
+    grouped = group_offsets is not None
+    groups = group_offsets.numel() - 1 if grouped else 1
+    n_ids = token_ids.numel() if grouped else 0
+    shape = (groups, cols // 16, 16, 16) if grouped else (cols // 16, 16, 16)
+    if H is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing H")
+        H = torch.empty(shape, dtype=torch.float32, device=x.device)
+    need = block_hessian_workspace_size(tokens, cols, groups, n_ids)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_block_hessian(_ptr(x), _dt(x), tokens, cols, groups, _ptr(group_offsets),
+                                     _ptr(token_ids), n_ids, _ptr(H), int(accumulate),
+                                     _ptr(workspace), workspace.numel(), _stream()),
+           "nvfp4_block_hessian")
+    return H
+
+
+def scale_search_local_hessian(w: torch.Tensor, S: torch.Tensor, H: torch.Tensor,
+                               return_obj: bool = False):
+    _need(w, "w")
+    _need(H, "H")
+    b, r, c = _shape3(w)
+    if H.numel() != b * (c // 16) * 256 or H.dtype != torch.float32:
+        raise ValueError("H must be fp32 [batch, cols/16, 16, 16]")
+    sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
+    obj = torch.empty(_out_shape(w, c // 16), dtype=torch.float64, device=w.device) if return_obj else None
+    _check(lib().nvfp4_scale_search_local_hessian(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(H),
+                                                  _ptr(sc), _ptr(obj), _stream()),
+           "nvfp4_scale_search_local_hessian")
+    return (sc, obj) if return_obj else sc
+
+
+def quantize(x: torch.Tensor, S: torch.Tensor, scales: torch.Tensor | None = None):
+    """Returns (codes, scales): packed E2M1 codes and the block bytes used."""
+    _need(x, "x")
+    b, r, c = _shape3(x)
+    codes = torch.empty(_out_shape(x, c // 2), dtype=torch.uint8, device=x.device)
+    so = None
+    if scales is None:
+        so = torch.empty(_out_shape(x, c // 16), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_quantize(_ptr(x), _dt(x), b, r, c, _ptr(S), _ptr(scales), _ptr(codes),
+                                _ptr(so), _stream()), "nvfp4_quantize")
+    return codes, (scales if so is None else so)
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, S: torch.Tensor,
+               out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    _need(codes, "codes")
+    shape = _out_shape(codes, codes.shape[-1] * 2)
+    y = torch.empty(shape, dtype=out_dtype, device=codes.device)
+    b, r, c = _shape3(y)
+    _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(S), b, r, c, _ptr(y), _dt(y),
+                                  _stream()), "nvfp4_dequantize")
+    return y
+
+
+def fakequant(x: torch.Tensor, S: torch.Tensor, scales: torch.Tensor | None = None,
+              return_codes: bool = False, out: torch.Tensor | None = None):
+    """Quantise -> dequantise in one pass. Returns y (and codes, scales if asked)."""
+    _need(x, "x")
+    b, r, c = _shape3(x)
+    y = torch.empty_like(x) if out is None else out
+    codes = so = None
+    if return_codes:
+        codes = torch.empty(_out_shape(x, c // 2), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            so = torch.empty(_out_shape(x, c // 16), dtype=torch.uint8, device=x.device)
+    _check(lib().nvfp4_fakequant(_ptr(x), _dt(x), b, r, c, _ptr(S), _ptr(scales), _ptr(y),
+                                 _ptr(codes), _ptr(so), _stream()), "nvfp4_fakequant")
+    if return_codes:
+        return y, codes, (scales if so is None else so)
+    return y
+
+
+def route_groups(expert_ids: torch.Tensor, experts: int):
+    """Per-expert token lists from a [tokens, topk] routing table: (offsets, token_ids)."""
+    _need(expert_ids, "expert_ids")
+    tokens, topk = expert_ids.shape
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device=expert_ids.device)
+    tok = torch.empty(tokens * topk, dtype=torch.int32, device=expert_ids.device)
+    need = int(lib().nvfp4_route_groups_workspace_size(tokens, topk, experts))
+    ws = torch.empty(max(need, 4), dtype=torch.uint8, device=expert_ids.device)
+    _check(lib().nvfp4_route_groups(_ptr(expert_ids), tokens, topk, experts, _ptr(offsets),
+                                    _ptr(tok), _ptr(ws), ws.numel(), _stream()),
+           "nvfp4_route_groups")
+    return offsets, tok

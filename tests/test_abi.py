@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad arguments
+on the host before any launch (no GPU needed: no compute call is made)."""
+import ctypes
+
+import pytest
+
+from scale_search_weights_amd import nvfp4
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, EHIP, EARG = range(8)
+FAKE = 0x7F0000000000  # never dereferenced: validation fails or returns before any use
+
+
+@pytest.fixture(scope="module")
+def L():
+    return nvfp4.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = nvfp4.declared_symbols()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.nvfp4_version() == 100
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert nvfp4.status_string(s).startswith("NVFP4_")
+    assert "unknown" in nvfp4.status_string(99)
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def test_shape_dtype_null_align_checks(L):
+    f = L.nvfp4_fakequant
+    # cols not a multiple of 16
+    assert f(P(FAKE), 1, 1, 4, 17, P(FAKE), None, P(FAKE), None, None, None) == ESHAPE
+    assert f(P(FAKE), 1, -1, 4, 16, P(FAKE), None, P(FAKE), None, None, None) == ESHAPE
+    # unknown dtype
+    assert f(P(FAKE), 7, 1, 4, 16, P(FAKE), None, P(FAKE), None, None, None) == EDTYPE
+    # NULL input / output / S
+    assert f(None, 1, 1, 4, 16, P(FAKE), None, P(FAKE), None, None, None) == ENULL
+    assert f(P(FAKE), 1, 1, 4, 16, None, None, P(FAKE), None, None, None) == ENULL
+    assert f(P(FAKE), 1, 1, 4, 16, P(FAKE), None, None, None, None, None) == ENULL
+    # misaligned element pointer and codes pointer
+    assert f(P(FAKE + 2), 1, 1, 4, 16, P(FAKE), None, P(FAKE), None, None, None) == EALIGN
+    assert f(P(FAKE), 1, 1, 4, 16, P(FAKE), None, P(FAKE), P(FAKE + 4), None, None) == EALIGN
+    # size overflow
+    assert f(P(FAKE), 1, 1 << 40, 1 << 20, 1 << 20, P(FAKE), None, P(FAKE), None, None, None) == ESHAPE
+
+
+def test_empty_tensors_return_ok_without_launch(L):
+    assert L.nvfp4_fakequant(None, 1, 1, 0, 16, None, None, None, None, None, None) == OK
+    assert L.nvfp4_fakequant(None, 1, 0, 4, 16, None, None, None, None, None, None) == OK
+    assert L.nvfp4_scale_search_mse(None, 0, 1, 4, 0, None, None, None, None) == OK
+    assert L.nvfp4_scale_search_local_hessian(None, 1, 1, 0, 32, None, None, None, None, None) == OK
+    assert L.nvfp4_global_scale(None, 1, 0, 16, None, None) == OK
+    assert L.nvfp4_quantize(None, 1, 1, 0, 16, None, None, None, None, None) == OK
+    assert L.nvfp4_dequantize(None, None, None, 1, 0, 16, None, 1, None) == OK
+
+
+def test_each_entry_point_validates(L):
+    assert L.nvfp4_global_scale(P(FAKE), 1, 1, 12, P(FAKE), None) == ESHAPE  # n % 8
+    assert L.nvfp4_global_scale(P(FAKE), 9, 1, 16, P(FAKE), None) == EDTYPE
+    assert L.nvfp4_scale_search_max(P(FAKE), 1, 1, 2, 16, P(FAKE), None, None) == ENULL
+    assert L.nvfp4_scale_search_mse(P(FAKE), 1, 1, 2, 8, P(FAKE), P(FAKE), None, None) == ESHAPE
+    assert L.nvfp4_scale_search_mse(P(FAKE), 1, 1, 2, 16, P(FAKE), P(FAKE), P(FAKE + 1), None) == EALIGN
+    assert L.nvfp4_scale_search_local_hessian(P(FAKE), 1, 1, 2, 16, P(FAKE), None, P(FAKE), None,
+                                              None) == ENULL
+    assert L.nvfp4_scale_search_local_hessian(P(FAKE), 1, 1, 2, 16, P(FAKE), P(FAKE), P(FAKE),
+                                              P(FAKE + 4), None) == EALIGN
+    assert L.nvfp4_quantize(P(FAKE), 1, 1, 2, 16, P(FAKE), None, None, None, None) == ENULL
+    assert L.nvfp4_dequantize(P(FAKE), P(FAKE), P(FAKE), 1, 2, 16, P(FAKE), 3, None) == EDTYPE
+
+
+def test_block_hessian_workspace_and_group_checks(L):
+    need = L.nvfp4_block_hessian_workspace_size(4096, 512, 1, 0)
+    assert need >= 512 // 16 * 256 * 4
+    f = L.nvfp4_block_hessian
+    # too small / missing workspace
+    assert f(P(FAKE), 1, 4096, 512, 1, None, None, 0, P(FAKE), 0, P(FAKE), need - 1, None) == EWS
+    assert f(P(FAKE), 1, 4096, 512, 1, None, None, 0, P(FAKE), 0, None, need, None) == EWS
+    # dense form must have exactly one group; grouped form needs both arrays
+    assert f(P(FAKE), 1, 4096, 512, 2, None, None, 0, P(FAKE), 0, P(FAKE), need, None) == EARG
+    assert f(P(FAKE), 1, 4096, 512, 2, P(FAKE), None, 10, P(FAKE), 0, P(FAKE), need, None) == ENULL
+    assert f(P(FAKE), 1, 4096, 500, 1, None, None, 0, P(FAKE), 0, P(FAKE), need, None) == ESHAPE
+    # grouped sizing grows with the number of ids
+    a = L.nvfp4_block_hessian_workspace_size(1000, 512, 8, 100)
+    b = L.nvfp4_block_hessian_workspace_size(1000, 512, 8, 1000000)
+    assert b > a
+
+
+def test_route_groups_checks(L):
+    need = L.nvfp4_route_groups_workspace_size(1000, 8, 128)
+    assert need > 0
+    f = L.nvfp4_route_groups
+    assert f(P(FAKE), 1000, 8, 0, P(FAKE), P(FAKE), P(FAKE), need, None) == ESHAPE
+    assert f(P(FAKE), 1000, 8, 20000, P(FAKE), P(FAKE), P(FAKE), need, None) == EARG
+    assert f(P(FAKE), 1000, 8, 128, P(FAKE), P(FAKE), P(FAKE), need - 1, None) == EWS
+    assert f(P(FAKE), 1000, 8, 128, None, P(FAKE), P(FAKE), need, None) == ENULL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        nvfp4.fakequant(torch.zeros(4, 16), torch.ones(1))
+    with pytest.raises(TypeError):
+        nvfp4._dt(torch.zeros(1, dtype=torch.float16))

@@ -1,0 +1,349 @@
+"""GPU parity: every entry point through the C ABI against the CPU oracle on seeded
+inputs, at sizes the oracle finishes in seconds (several tiles and ragged tails).
+
+Bar: bit-exact for block bytes, packed codes, dequantised values (fp32 bits; bf16 bits of
+the oracle value rounded to nearest-even), MSE objectives, routing lists and the
+Local-Hessian bytes and fp64 objectives; block Hessians within 1e-4 relative Frobenius
+error per block (fp32 accumulation against the oracle's fp64 sums).
+"""
+import numpy as np
+import pytest
+import torch
+
+from scale_search_weights_amd import nvfp4, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def dev_S(*vals):
+    return torch.tensor(np.array(vals, np.float32), device=DEV)
+
+
+def assert_bits(gpu_y: torch.Tensor, dq_ref: np.ndarray, orc):
+    if gpu_y.dtype == torch.bfloat16:
+        got = gpu_y.cpu().view(torch.int16).numpy().view(np.uint16)
+        want = orc.bf16_rne_array(dq_ref)
+    else:
+        got = gpu_y.cpu().numpy().view(np.uint32)
+        want = dq_ref.view(np.uint32)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+def rel_frob(Hg: np.ndarray, Href: np.ndarray) -> float:
+    Hg = Hg.reshape(-1, 256).astype(np.float64)
+    Hr = Href.reshape(-1, 256)
+    num = np.linalg.norm(Hg - Hr, axis=1)
+    den = np.linalg.norm(Hr, axis=1)
+    r = np.where(den > 0, num / np.where(den > 0, den, 1), num)
+    return float(r.max())
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w, x = synth.tiny(0)
+    return w, x
+
+
+# ------------------------------------------------------------------ tensor scale
+
+def test_global_scale(orc, tiny):
+    w, _ = tiny
+    case("global_scale tiny fp32")
+    assert nvfp4.global_scale(w.to(DEV)).item() == orc.tensor_scale(w.numpy())
+    case("global_scale activation bf16 256x4096")
+    a = synth.activation(1, 256, 4096)
+    assert nvfp4.global_scale(a.to(DEV)).item() == orc.tensor_scale(f32(a))
+    case("global_scale zero tensor -> 1")
+    assert nvfp4.global_scale(torch.zeros(8, 32, device=DEV)).item() == 1.0
+    case("global_scale batch of 5 experts")
+    e = synth.moe(2, experts=5, rows=64, cols=128, tokens=16, topk=2)[0]
+    e[3] *= 0
+    S = nvfp4.global_scale(e.to(DEV)).cpu().numpy()
+    for b in range(5):
+        assert S[b] == orc.tensor_scale(f32(e[b])), b
+
+
+# ------------------------------------------------------------------ max scaling / fake-quant
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(64, 256), (333, 1024), (8, 16)])
+def test_fakequant_max_scaling(orc, dtype, shape):
+    case(f"fakequant max {shape} {dtype}")
+    x = synth.activation(3, *shape).to(dtype)
+    xn = f32(x)
+    S = orc.tensor_scale(xn)
+    y, codes, scales = nvfp4.fakequant(x.to(DEV), dev_S(S), return_codes=True)
+    dq, codes_ref, sc_ref = orc.fakequant(xn, S)
+    assert np.array_equal(scales.cpu().numpy(), sc_ref)
+    assert np.array_equal(codes.cpu().numpy(), codes_ref)
+    assert_bits(y, dq, orc)
+    # the separate entry points agree with the fused one
+    assert np.array_equal(nvfp4.scale_search_max(x.to(DEV), dev_S(S)).cpu().numpy(), sc_ref)
+    c2, s2 = nvfp4.quantize(x.to(DEV), dev_S(S))
+    assert np.array_equal(c2.cpu().numpy(), codes_ref) and np.array_equal(s2.cpu().numpy(), sc_ref)
+    y2 = nvfp4.dequantize(c2, s2, dev_S(S), out_dtype=dtype)
+    assert_bits(y2, dq, orc)
+
+
+def test_fakequant_batched_per_entry_scale(orc):
+    case("fakequant batch 3 x 40 x 256 bf16, per-entry S")
+    x = synth.moe(4, experts=3, rows=40, cols=256, tokens=8, topk=1)[0]
+    x[1] *= 1000.0
+    xd = x.to(DEV)
+    S = nvfp4.global_scale(xd)
+    y, codes, sc = nvfp4.fakequant(xd, S, return_codes=True)
+    Sn = S.cpu().numpy()
+    for b in range(3):
+        dq, cr, sr = orc.fakequant(f32(x[b]), Sn[b])
+        assert np.array_equal(sc[b].cpu().numpy(), sr)
+        assert np.array_equal(codes[b].cpu().numpy(), cr)
+        assert_bits(y[b], dq, orc)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_with_given_scales_all_bytes(orc, dtype):
+    case(f"quantize with every byte 1..126, {dtype}")
+    rng = np.random.default_rng(5)
+    rows, cols = 126, 64
+    S = np.float32(3.0e-3)
+    sc = np.repeat(np.arange(1, 127, dtype=np.uint8)[:, None], cols // 16, axis=1)
+    sval = np.array([orc.e4m3_value(b) for b in range(1, 127)], np.float64)[:, None]
+    x = (rng.uniform(-7, 7, (rows, cols)) * sval * float(S)).astype(np.float32)
+    xt = torch.from_numpy(x).to(dtype)
+    xn = f32(xt)
+    codes, _ = nvfp4.quantize(xt.to(DEV), dev_S(S), torch.from_numpy(sc).to(DEV))
+    assert np.array_equal(codes.cpu().numpy(), orc.quantize(xn, S, sc))
+    y = nvfp4.fakequant(xt.to(DEV), dev_S(S), torch.from_numpy(sc).to(DEV))
+    dq, _, _ = orc.fakequant(xn, S, sc)
+    assert_bits(y, dq, orc)
+
+
+def test_exact_ties_and_edges(orc):
+    case("ties on midpoints, zero blocks, -0, saturation, denormal inputs")
+    blocks = []
+    # element ties at unit scale: multiples of 1/16 in [-8, 8]; block max 8 -> byte for 8/6
+    v = synth.on_grid_block_values(7, 64 * 16).reshape(64, 16)
+    blocks.append(v)
+    # all-zero and negative-zero blocks
+    z = np.zeros((2, 16), np.float32)
+    z[1] = -0.0
+    blocks.append(z)
+    # block max exactly on an E4M3 midpoint times 6 (S = 1): ties to the even byte
+    mids = []
+    for b in range(1, 126):
+        m = (orc.e4m3_value(b) + orc.e4m3_value(b + 1)) / 2 * 6.0
+        if np.float32(m) == m:
+            row = np.full(16, np.float32(m) / 3, np.float32)
+            row[0] = np.float32(m)
+            mids.append(row)
+    blocks.append(np.array(mids, np.float32))
+    # denormal fp32 inputs next to normal ones
+    d = np.full((1, 16), 1e-40, np.float32)
+    d[0, 3] = 1.0
+    blocks.append(d)
+    x = np.concatenate(blocks, axis=0)
+    S = np.float32(1.0)
+    xt = torch.from_numpy(x)
+    y, codes, sc = nvfp4.fakequant(xt.to(DEV), dev_S(S), return_codes=True)
+    dq, cr, sr = orc.fakequant(x, S)
+    assert np.array_equal(sc.cpu().numpy(), sr)
+    assert np.array_equal(codes.cpu().numpy(), cr)
+    assert_bits(y, dq, orc)
+    # saturation: values far beyond 6 * 448 * S with a caller-supplied small S
+    big = (np.random.default_rng(8).standard_normal((32, 32)) * 1e6).astype(np.float32)
+    S2 = np.float32(1e-3)
+    y, codes, sc = nvfp4.fakequant(torch.from_numpy(big).to(DEV), dev_S(S2), return_codes=True)
+    dq, cr, sr = orc.fakequant(big, S2)
+    assert np.all(sr == 0x7E)
+    assert np.array_equal(codes.cpu().numpy(), cr)
+    assert_bits(y, dq, orc)
+    # tiny values with the smallest normal tensor scale (subnormal block scales)
+    tiny_x = (np.random.default_rng(9).standard_normal((16, 64)) * 1e-36).astype(np.float32)
+    S3 = orc.tensor_scale(tiny_x)
+    y, codes, sc = nvfp4.fakequant(torch.from_numpy(tiny_x).to(DEV), dev_S(S3), return_codes=True)
+    dq, cr, sr = orc.fakequant(tiny_x, S3)
+    assert np.array_equal(sc.cpu().numpy(), sr)
+    assert np.array_equal(codes.cpu().numpy(), cr)
+    assert_bits(y, dq, orc)
+
+
+def test_worked_example_on_gpu(orc):
+    import json
+    import os
+    case("worked example block: 84 -> scale 14")
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")) as f:
+        g = json.load(f)
+    x = torch.tensor([g["block"]], dtype=torch.float32, device=DEV)
+    y, codes, sc = nvfp4.fakequant(x, dev_S(1.0), return_codes=True)
+    assert orc.e4m3_value(int(sc.item())) == g["scale"]
+    yn = y.cpu().numpy()[0]
+    assert set(np.abs(yn).tolist()) <= set(g["magnitudes"]) and yn[0] == 84.0
+    assert np.all(yn[np.abs(np.array(g["block"])) < g["zero_below"]] == 0)
+    assert nvfp4.scale_search_mse(x, dev_S(1.0)).item() == 0x56
+
+
+# ------------------------------------------------------------------ MSE search
+
+@pytest.mark.parametrize("which", ["tiny_fp32", "mlp_bf16", "mlp_bf16_ragged"])
+def test_mse_search(orc, tiny, which):
+    if which == "tiny_fp32":
+        w = tiny[0]
+    elif which == "mlp_bf16":
+        w = synth.mlp_weight(1, 256, 1024)
+    else:
+        w = synth.mlp_weight(2, 37, 48)
+    case(f"mse {which} {tuple(w.shape)}")
+    wn = f32(w)
+    S = orc.tensor_scale(wn)
+    sc, obj = nvfp4.scale_search_mse(w.to(DEV), dev_S(S), return_obj=True)
+    sr, orf = orc.scales_mse(wn, S, with_obj=True)
+    assert np.array_equal(sc.cpu().numpy(), sr)
+    assert np.array_equal(obj.cpu().numpy().view(np.uint32), orf.view(np.uint32))
+
+
+def test_mse_batched_and_zero_blocks(orc):
+    case("mse batch 4 x 32 x 128 with zero blocks")
+    w = synth.moe(3, experts=4, rows=32, cols=128, tokens=8, topk=1)[0]
+    w[2, 5, 16:32] = 0
+    wd = w.to(DEV)
+    S = nvfp4.global_scale(wd)
+    sc, obj = nvfp4.scale_search_mse(wd, S, return_obj=True)
+    Sn = S.cpu().numpy()
+    for b in range(4):
+        sr, orf = orc.scales_mse(f32(w[b]), Sn[b], with_obj=True)
+        assert np.array_equal(sc[b].cpu().numpy(), sr)
+        assert np.array_equal(obj[b].cpu().numpy(), orf)
+    assert sc[2, 5, 1].item() == 0
+
+
+# ------------------------------------------------------------------ block Hessian
+
+@pytest.mark.parametrize("which", ["tiny_fp32", "proj_bf16", "ragged_bf16", "narrow_bf16"])
+def test_block_hessian_dense(orc, tiny, which):
+    if which == "tiny_fp32":
+        x = tiny[1]
+    elif which == "proj_bf16":
+        x = synth.projection(1, rows=16, cols=512, tokens=4096)[1]
+    elif which == "ragged_bf16":
+        x = synth.projection(2, rows=16, cols=256, tokens=1000)[1]
+    else:
+        x = synth.projection(3, rows=16, cols=48, tokens=777)[1]
+    case(f"hessian dense {which} {tuple(x.shape)}")
+    xd = x.to(DEV)
+    H = nvfp4.block_hessian(xd)
+    Href = orc.block_hessian(f32(x))
+    assert rel_frob(H.cpu().numpy(), Href) <= 1e-4
+    H2 = nvfp4.block_hessian(xd)
+    assert torch.equal(H, H2), "not bitwise reproducible"
+
+
+def test_block_hessian_accumulate(orc):
+    case("hessian accumulate over two batches")
+    x = synth.projection(4, rows=16, cols=256, tokens=3000)[1]
+    a, b = x[:1200].contiguous(), x[1200:].contiguous()
+    H = nvfp4.block_hessian(a.to(DEV))
+    H = nvfp4.block_hessian(b.to(DEV), H=H, accumulate=True)
+    Href = orc.block_hessian(f32(x))
+    assert rel_frob(H.cpu().numpy(), Href) <= 1e-4
+
+
+def test_route_groups_and_grouped_hessian(orc):
+    case("route groups 3000 tokens top-4 over 16 experts + grouped hessian")
+    _, x, ids = synth.moe(5, experts=16, rows=16, cols=256, tokens=3000, topk=4)
+    ids_np = ids.numpy()
+    off, tok = nvfp4.route_groups(ids.to(DEV), 16)
+    off_ref, tok_ref = orc.route_groups(ids_np, 16)
+    assert np.array_equal(off.cpu().numpy(), off_ref)
+    assert np.array_equal(tok.cpu().numpy(), tok_ref)
+    H = nvfp4.block_hessian(x.to(DEV), group_offsets=off, token_ids=tok)
+    Hn = H.cpu().numpy()
+    xn = f32(x)
+    for e in range(16):
+        Href = orc.block_hessian(xn, tok_ref[off_ref[e]:off_ref[e + 1]])
+        assert rel_frob(Hn[e], Href) <= 1e-4, e
+
+
+def test_grouped_hessian_with_empty_group(orc):
+    case("grouped hessian with an empty expert")
+    _, x, _ = synth.moe(6, experts=4, rows=16, cols=64, tokens=700, topk=2)
+    ids = np.array([[0, 2]] * 400 + [[2, 3]] * 300, np.int32)
+    off, tok = nvfp4.route_groups(torch.from_numpy(ids).to(DEV), 4)
+    off_ref, tok_ref = orc.route_groups(ids, 4)
+    assert np.array_equal(off.cpu().numpy(), off_ref)
+    H = nvfp4.block_hessian(x.to(DEV), group_offsets=off, token_ids=tok).cpu().numpy()
+    assert np.all(H[1] == 0)
+    for e in (0, 2, 3):
+        assert rel_frob(H[e], orc.block_hessian(f32(x), tok_ref[off_ref[e]:off_ref[e + 1]])) <= 1e-4
+
+
+# ------------------------------------------------------------------ Local-Hessian search
+
+def _lh_check(orc, w, S, H):
+    sc, obj = nvfp4.scale_search_local_hessian(w.to(DEV), dev_S(S), H, return_obj=True)
+    sr, orf = orc.scales_local_hessian(f32(w), S, H.cpu().numpy(), with_obj=True)
+    g = sc.cpu().numpy()
+    assert np.array_equal(g, sr), f"{np.sum(g != sr)} bytes differ"
+    assert np.array_equal(obj.cpu().numpy(), orf)
+    return g
+
+
+def test_local_hessian_tiny(orc, tiny):
+    w, x = tiny
+    case("local hessian tiny fp32 (H from GPU)")
+    S = orc.tensor_scale(w.numpy())
+    H = nvfp4.block_hessian(x.to(DEV))
+    _lh_check(orc, w, S, H)
+
+
+def test_local_hessian_bf16_projection(orc):
+    case("local hessian bf16 96x512, H from 4096 t4 tokens")
+    w, x = synth.projection(7, rows=96, cols=512, tokens=4096)
+    S = orc.tensor_scale(f32(w))
+    H = nvfp4.block_hessian(x.to(DEV))
+    _lh_check(orc, w, S, H)
+
+
+def test_local_hessian_special_hessians(orc):
+    case("local hessian with H = I (equals MSE up to fp32/fp64 near-ties) and a zero H block")
+    w = synth.mlp_weight(8, 64, 128)
+    wn = f32(w)
+    S = orc.tensor_scale(wn)
+    eye = torch.eye(16, device=DEV).expand(8, 16, 16).contiguous()
+    eye[2] = 0.0
+    g = _lh_check(orc, w, S, eye)
+    mse = orc.scales_mse(wn, S)
+    assert np.array_equal(g[:, 2], mse[:, 2])
+    assert np.mean(g == mse) > 0.99
+    case("local hessian with a rank-1 H (one token)")
+    x1 = torch.randn(1, 128, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    H1 = nvfp4.block_hessian(x1.to(DEV))
+    _lh_check(orc, w, S, H1)
+
+
+def test_local_hessian_batched_experts(orc):
+    case("local hessian batch of 4 experts with per-expert S and H")
+    w, x, ids = synth.moe(9, experts=4, rows=40, cols=128, tokens=600, topk=2)
+    off, tok = nvfp4.route_groups(ids.to(DEV), 4)
+    H = nvfp4.block_hessian(x.to(DEV), group_offsets=off, token_ids=tok)
+    wd = w.to(DEV)
+    S = nvfp4.global_scale(wd)
+    sc, obj = nvfp4.scale_search_local_hessian(wd, S, H, return_obj=True)
+    Sn, Hn = S.cpu().numpy(), H.cpu().numpy()
+    for e in range(4):
+        sr, orf = orc.scales_local_hessian(f32(w[e]), Sn[e], Hn[e], with_obj=True)
+        assert np.array_equal(sc[e].cpu().numpy(), sr)
+        assert np.array_equal(obj[e].cpu().numpy(), orf)
+    # final quantisation with the chosen bytes
+    codes, _ = nvfp4.quantize(wd, S, sc)
+    for e in range(4):
+        assert np.array_equal(codes[e].cpu().numpy(), orc.quantize(f32(w[e]), Sn[e], sc[e].cpu().numpy()))
