@@ -1,0 +1,295 @@
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step is one pass of the whole path over resident synthetic inputs:
+  1. activation fake-quant, bf16 8192x4096, max scaling (quantise -> pack -> dequantise,
+     codes and block bytes written too), with the calibrated tensor scale held fixed;
+  2. MSE scale search on a bf16 12288x4096 MLP weight (tensor scale, 3.1M blocks x 126
+     candidates) and its final quantisation;
+  3. block Hessian of 131072 calibration tokens x 4096 (bf16) and the Local-Hessian search
+     on a bf16 4096x4096 projection weight, then its final quantisation;
+  4. MoE: routing of 65536 tokens (top-8, Zipf 1.1) into per-expert token lists, per-expert
+     block Hessians, tensor scales and Local-Hessian search for 128 experts of 512x2048,
+     then their final quantisation.
+Headline value: fake-quant GB/s of stage 1 (algorithmic bytes / kernel time). The JSON
+line also carries Local-Hessian blocks/s, every stage's time and roofline, and the CPU
+oracle timed on a bounded sample of the same workloads.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_MFMA_TFLOPS = 157.3       # dense fp32 matrix
+FP64_VECTOR_TFLOPS = 78.6      # fp64 vector (FMA = 2 flops)
+VALU_LANE_TOPS = 256 * 64 * 2.4e9 / 1e12   # non-packed lane-ops/s: 256 CU x 64 lanes x 2.4 GHz = 39.3
+MSE_OPS_PER_EVAL = 5           # compare/select x3, subtract, fma per element x candidate
+FQ_BYTES_PER_ELEM = 2 + 2 + 0.5 + 1 / 16   # read bf16, write bf16 + packed code + 1/16 byte
+
+
+def _sha_of(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, source_file: str):
+    """HBM traffic per launch from committed rocprofv3 PMC runs, if the kernel source is
+    unchanged since they were taken; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            tab = json.load(f)
+        ent = tab[kernel_key]
+        if ent.get("source_sha") != _sha_of([os.path.join(ROOT, source_file)]):
+            return None
+        return ent["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for PMC byte-counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from scale_search_weights_amd import nvfp4, synth
+
+    L = nvfp4.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(st.cuda_stream)
+
+    def P(t):
+        return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {nvfp4.status_string(rc)}")
+
+    BF16 = nvfp4.DTYPE_BF16
+    t_setup = time.time()
+    # ---------------------------------------------------------------- inputs (resident)
+    a2 = synth.activation(0).to(dev)                       # [8192, 4096]
+    r2, c2 = a2.shape
+    S2 = nvfp4.global_scale(a2)                            # calibrated, held fixed
+    y2 = torch.empty_like(a2)
+    codes2 = torch.empty(r2, c2 // 2, dtype=torch.uint8, device=dev)
+    sc2 = torch.empty(r2, c2 // 16, dtype=torch.uint8, device=dev)
+
+    w3 = synth.mlp_weight(0).to(dev)                       # [12288, 4096]
+    r3, c3 = w3.shape
+    S3 = torch.empty(1, dtype=torch.float32, device=dev)
+    sc3 = torch.empty(r3, c3 // 16, dtype=torch.uint8, device=dev)
+    codes3 = torch.empty(r3, c3 // 2, dtype=torch.uint8, device=dev)
+
+    w4c, x4c = synth.projection(0)
+    w4, x4 = w4c.to(dev), x4c.to(dev)                      # [4096, 4096], [131072, 4096]
+    del w4c, x4c
+    r4, c4 = w4.shape
+    t4 = x4.shape[0]
+    H4 = torch.empty(c4 // 16, 16, 16, dtype=torch.float32, device=dev)
+    ws4_n = L.nvfp4_block_hessian_workspace_size(t4, c4, 1, 0)
+    ws4 = torch.empty(ws4_n, dtype=torch.uint8, device=dev)
+    S4 = torch.empty(1, dtype=torch.float32, device=dev)
+    sc4 = torch.empty(r4, c4 // 16, dtype=torch.uint8, device=dev)
+    codes4 = torch.empty(r4, c4 // 2, dtype=torch.uint8, device=dev)
+
+    w5c, x5c, ids5c = synth.moe(0)
+    w5, x5, ids5 = w5c.to(dev), x5c.to(dev), ids5c.to(dev)
+    del w5c, x5c
+    E, r5, c5 = w5.shape
+    t5, topk = ids5.shape
+    off5 = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    tok5 = torch.empty(t5 * topk, dtype=torch.int32, device=dev)
+    wsr_n = L.nvfp4_route_groups_workspace_size(t5, topk, E)
+    wsr = torch.empty(max(wsr_n, 4), dtype=torch.uint8, device=dev)
+    H5 = torch.empty(E, c5 // 16, 16, 16, dtype=torch.float32, device=dev)
+    ws5_n = L.nvfp4_block_hessian_workspace_size(t5, c5, E, t5 * topk)
+    ws5 = torch.empty(ws5_n, dtype=torch.uint8, device=dev)
+    S5 = torch.empty(E, dtype=torch.float32, device=dev)
+    sc5 = torch.empty(E, r5, c5 // 16, dtype=torch.uint8, device=dev)
+    codes5 = torch.empty(E, r5, c5 // 2, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    # ---------------------------------------------------------------- one step
+    stages = {}
+
+    def stage(name, fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        stages.setdefault(name, []).append((e0, e1))
+
+    def step():
+        stage("fakequant_act", lambda: ok(L.nvfp4_fakequant(
+            P(a2), BF16, 1, r2, c2, P(S2), None, P(y2), P(codes2), P(sc2), sptr), "fakequant"))
+        stage("scale_mlp", lambda: ok(L.nvfp4_global_scale(P(w3), BF16, 1, r3 * c3, P(S3), sptr), "scale"))
+        stage("mse_mlp", lambda: ok(L.nvfp4_scale_search_mse(
+            P(w3), BF16, 1, r3, c3, P(S3), P(sc3), None, sptr), "mse"))
+        stage("quantize_mlp", lambda: ok(L.nvfp4_quantize(
+            P(w3), BF16, 1, r3, c3, P(S3), P(sc3), P(codes3), None, sptr), "quantize"))
+        stage("hessian_proj", lambda: ok(L.nvfp4_block_hessian(
+            P(x4), BF16, t4, c4, 1, None, None, 0, P(H4), 0, P(ws4), ws4_n, sptr), "hessian"))
+        stage("scale_proj", lambda: ok(L.nvfp4_global_scale(P(w4), BF16, 1, r4 * c4, P(S4), sptr), "scale"))
+        stage("lh_proj", lambda: ok(L.nvfp4_scale_search_local_hessian(
+            P(w4), BF16, 1, r4, c4, P(S4), P(H4), P(sc4), None, sptr), "lh"))
+        stage("quantize_proj", lambda: ok(L.nvfp4_quantize(
+            P(w4), BF16, 1, r4, c4, P(S4), P(sc4), P(codes4), None, sptr), "quantize"))
+        stage("route_moe", lambda: ok(L.nvfp4_route_groups(
+            P(ids5), t5, topk, E, P(off5), P(tok5), P(wsr), wsr_n, sptr), "route"))
+        stage("hessian_moe", lambda: ok(L.nvfp4_block_hessian(
+            P(x5), BF16, t5, c5, E, P(off5), P(tok5), t5 * topk, P(H5), 0, P(ws5), ws5_n, sptr),
+            "hessian"))
+        stage("scale_moe", lambda: ok(L.nvfp4_global_scale(P(w5), BF16, E, r5 * c5, P(S5), sptr), "scale"))
+        stage("lh_moe", lambda: ok(L.nvfp4_scale_search_local_hessian(
+            P(w5), BF16, E, r5, c5, P(S5), P(H5), P(sc5), None, sptr), "lh"))
+        stage("quantize_moe", lambda: ok(L.nvfp4_quantize(
+            P(w5), BF16, E, r5, c5, P(S5), P(sc5), P(codes5), None, sptr), "quantize"))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stages.clear()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in stages.items()}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- figures
+    fq_bytes = r2 * c2 * FQ_BYTES_PER_ELEM
+    fq_gbs = fq_bytes / (ms["fakequant_act"] * 1e-3) / 1e9
+    n_lh4 = r4 * (c4 // 16)
+    n_lh5 = E * r5 * (c5 // 16)
+    lh4_time = ms["hessian_proj"] + ms["lh_proj"]
+    lh4_blocks_s = n_lh4 / (lh4_time * 1e-3)
+    lh5_time = ms["route_moe"] + ms["hessian_moe"] + ms["lh_moe"]
+    lh5_blocks_s = n_lh5 / (lh5_time * 1e-3)
+    mse_evals = r3 * (c3 // 16) * 126 * 16
+    h4_bytes = t4 * c4 * 2
+    h5_bytes = t5 * topk * c5 * 2
+
+    def roof(bound, achieved, peak, unit, traffic=None):
+        return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic}
+
+    fq_traffic = load_traffic("fakequant_act", "scale_search_weights_amd/csrc/nvfp4_quant.hip")
+    rooflines = {
+        "fakequant_act": roof("hbm", fq_gbs, HBM_PEAK_GBS, "GB/s", fq_traffic),
+        "mse_mlp": roof("alu", mse_evals * MSE_OPS_PER_EVAL / (ms["mse_mlp"] * 1e-3) / 1e12,
+                        round(VALU_LANE_TOPS, 2), "TOP/s"),
+        "hessian_proj": roof("hbm", h4_bytes / (ms["hessian_proj"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "lh_proj": roof("alu", n_lh4 * 126 * 512 / (ms["lh_proj"] * 1e-3) / 1e12, FP64_VECTOR_TFLOPS,
+                        "TFLOP/s"),
+        "hessian_moe": roof("hbm", h5_bytes / (ms["hessian_moe"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "lh_moe": roof("alu", n_lh5 * 126 * 512 / (ms["lh_moe"] * 1e-3) / 1e12, FP64_VECTOR_TFLOPS,
+                       "TFLOP/s"),
+    }
+
+    out = {
+        "metric": "NVFP4 fake-quant GB/s + Local-Hessian blocks/s, % of MI355X roofline",
+        "value": round(fq_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators; no datasets or checkpoints)",
+        "config": {
+            "workload": "activation fake-quant bf16 8192x4096, max scaling (headline); per step "
+                        "also MSE on bf16 12288x4096, block Hessian of 131072x4096 + Local-Hessian "
+                        "on 4096x4096, MoE 128 experts 512x2048 with 65536 tokens top-8",
+            "fakequant_bytes_per_step": int(fq_bytes),
+        },
+        "local_hessian_blocks_per_s": {
+            "proj_4096x4096_incl_hessian": round(lh4_blocks_s, 1),
+            "moe_128x512x2048_incl_routing_hessian": round(lh5_blocks_s, 1),
+        },
+        "roofline": rooflines["fakequant_act"],
+        "rooflines": rooflines,
+        "stage_ms": {k: round(v, 4) for k, v in ms.items()},
+        "setup_s": round(t_setup, 1),
+    }
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        nthr = oracle.num_threads()
+        xa = a2[:1024].float().cpu().numpy()
+        s2 = float(S2.item())
+        t = time.perf_counter()
+        oracle.fakequant(xa, s2)
+        dt_fq = time.perf_counter() - t
+        wl = w4[:16].float().cpu().numpy()
+        Hn = H4.cpu().numpy()
+        s4 = float(S4.item())
+        t = time.perf_counter()
+        oracle.scales_local_hessian(wl, s4, Hn)
+        dt_lh = time.perf_counter() - t
+        wm = w3[:32].float().cpu().numpy()
+        s3 = float(S3.item())
+        t = time.perf_counter()
+        oracle.scales_mse(wm, s3)
+        dt_mse = time.perf_counter() - t
+        out["cpu_baseline"] = {
+            "value": round(xa.size * FQ_BYTES_PER_ELEM / dt_fq / 1e9, 4),
+            "unit": "GB/s",
+            "cores": nthr,
+            "kind": "oracle",
+            "sample": "fake-quant of 1024 of the 8192 activation rows (4.2M values); "
+                      "Local-Hessian on 16 rows (4096 blocks) of the 4096x4096 weight; "
+                      "MSE on 32 rows (8192 blocks) of the 12288x4096 weight",
+            "local_hessian_blocks_per_s": round(16 * (c4 // 16) / dt_lh, 1),
+            "mse_blocks_per_s": round(32 * (c3 // 16) / dt_mse, 1),
+            "seconds": round(dt_fq + dt_lh + dt_mse, 2),
+        }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
