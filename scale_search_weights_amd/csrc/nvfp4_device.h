@@ -91,11 +91,160 @@ __device__ __forceinline__ int max_scale_byte(float amax, float S) {
   return b == 0 ? 1 : b;
 }
 
+// ---------------------------------------------------------------- hardware-convert fast path
+//
+// gfx950's FP4 convert rounds an fp32 value half-to-even onto the E2M1 grid and saturates at
+// +-6; its FP8 convert rounds half-to-even onto E4M3FN (inputs clamped to 448 first). They
+// decide on the fp32 *input*, whereas the decision must be taken on the exact quotient
+// x / (s S). So each value is converted twice, after multiplying by two reciprocals that
+// bracket 1/(s S) (relative gap 2^-22 each side of it, above every rounding in the
+// products): if both conversions agree, the exact quotient rounds the same way (rounding is
+// monotone and a quotient on a midpoint would split the pair). If they differ (a value
+// within ~2^-22 of a midpoint) the caller falls back to the exact threshold path.
+
+typedef float nv_v2f __attribute__((ext_vector_type(2)));
+
+// lo < 1/d < hi for an exact double d > 0 (both as fp32). Two Newton steps on v_rcp_f64.
+__device__ __forceinline__ void recip_bracket(double d, float &lo, float &hi) {
+  double r = __builtin_amdgcn_rcp(d);
+  r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+  r = __builtin_fma(r, __builtin_fma(-d, r, 1.0), r);
+  lo = (float)(r * (1.0 - 0x1p-22));
+  hi = (float)(r * (1.0 + 0x1p-22));
+}
+
+// Max-scaling byte from bracketing multipliers lo < 1/(6S) < hi. The two FP8 conversions
+// give the same byte, or two adjacent bytes when amax / (6S) lies within the bracket of the
+// midpoint between them; then one exact comparison (products <= 31 bits, exact in double)
+// decides, ties to the even byte.
+__device__ __forceinline__ int max_scale_byte_fast(float amax, float qlo_mul, float qhi_mul,
+                                                   float S) {
+  if (amax == 0.0f) return 0;
+  const float qlo = fminf(amax * qlo_mul, 448.0f), qhi = fminf(amax * qhi_mul, 448.0f);
+  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(qlo, qhi, 0, false);
+  int b = pk & 0xFF;
+  const int b1 = (pk >> 8) & 0xFF;
+  if (b != b1) {
+    if (b1 == b + 1) {
+      const double mid = 0.5 * (e4m3_value_d(b) + e4m3_value_d(b1)) * (6.0 * (double)S);
+      const double a = amax;
+      b = (a > mid || (a == mid && (b & 1))) ? b1 : b;
+    } else {
+      b = max_scale_byte(amax, S);
+    }
+  }
+  return b == 0 ? 1 : b;
+}
+
+// Midpoint between E2M1 grid indices j and j+1.
+__device__ __forceinline__ double e2m1_mid(int j) {
+  double m = 0.25;
+  m = j == 1 ? 0.75 : m;
+  m = j == 2 ? 1.25 : m;
+  m = j == 3 ? 1.75 : m;
+  m = j == 4 ? 2.5 : m;
+  m = j == 5 ? 3.5 : m;
+  m = j == 6 ? 5.0 : m;
+  return m;
+}
+
+// Resolve the nibbles where the codes from the low and high brackets differ: the exact
+// code is one of the two adjacent magnitudes, decided by one exact comparison with the
+// midpoint between them (ties to the even index). a: codes from lo, b: codes from hi.
+__device__ __forceinline__ unsigned fp4_resolve8(const float *v, unsigned a, unsigned b,
+                                                 double sS) {
+  unsigned d = a ^ b;
+  while (d) {
+    const int i = __builtin_ctz(d) >> 2;
+    const unsigned sh = 4u * (unsigned)i;
+    const int j = (int)((a >> sh) & 7u);
+    float vi = v[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) vi = (i == k) ? v[k] : vi;
+    const double X = fabs((double)vi), T = e2m1_mid(j) * sS;  // T exact (<= 31 bits)
+    const bool up = (X > T) || (X == T && (j & 1));
+    const unsigned mag = (unsigned)(up ? j + 1 : j);
+    const unsigned neg = (__float_as_uint(vi) >> 31) & (mag ? 1u : 0u);
+    a = (a & ~(0xFu << sh)) | ((mag | (neg << 3)) << sh);
+    d &= ~(0xFu << sh);
+  }
+  return a;
+}
+
+// Signed E2M1 codes of 8 values (element i in nibble i) after scaling by lo (into a) and
+// by hi (into b); equal nibbles are the exact codes.
+__device__ __forceinline__ void fp4_codes8(const float *v, float lo, float hi, unsigned &a,
+                                           unsigned &b) {
+  a = 0u;
+  b = 0u;
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[0] * lo, v[1] * lo, 1.0f, 0);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[2] * lo, v[3] * lo, 1.0f, 1);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[4] * lo, v[5] * lo, 1.0f, 2);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[6] * lo, v[7] * lo, 1.0f, 3);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, v[0] * hi, v[1] * hi, 1.0f, 0);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, v[2] * hi, v[3] * hi, 1.0f, 1);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, v[4] * hi, v[5] * hi, 1.0f, 2);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, v[6] * hi, v[7] * hi, 1.0f, 3);
+}
+
+// Exact signed codes of 8 values for block scale s (sS = s * S exact in double).
+__device__ __forceinline__ unsigned fp4_exact_codes8(const float *v, float lo, float hi,
+                                                     double sS) {
+  unsigned a, b;
+  fp4_codes8(v, lo, hi, a, b);
+  if (a != b) a = fp4_resolve8(v, a, b, sS);
+  return a;
+}
+
+// Clear the sign bit of every zero-magnitude nibble (the convert keeps the sign of -0).
+__device__ __forceinline__ unsigned fp4_clear_neg_zero(unsigned c) {
+  const unsigned m = c & 0x77777777u;
+  const unsigned nz = (m + 0x77777777u) & 0x88888888u;  // bit 3 set iff magnitude != 0
+  return m | (c & nz);
+}
+
+// Signed grid values G of 8 packed codes.
+__device__ __forceinline__ void fp4_decode8(unsigned c, float g[8]) {
+  nv_v2f t;
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+  g[0] = t.x; g[1] = t.y;
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+  g[2] = t.x; g[3] = t.y;
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+  g[4] = t.x; g[5] = t.y;
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+  g[6] = t.x; g[7] = t.y;
+}
+
+// Exact codes of 8 values from a threshold table (the fallback path).
+__device__ __forceinline__ unsigned exact_codes8(const float *v, const ScaleTable &tb) {
+  unsigned out = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float X = fabsf(v[i]);
+    unsigned k = 0u;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) k += (X > tb.t[j]) ? 1u : 0u;
+    const unsigned neg = (__float_as_uint(v[i]) >> 31) & (k ? 1u : 0u);
+    out |= (k | (neg << 3)) << (4 * i);
+  }
+  return out;
+}
+
 // RNE of fp32 to bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+typedef __bf16 nv_v2bf __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16 (round half to even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  const nv_v2f f = {a, b};
+  const nv_v2bf h = __builtin_convertvector(f, nv_v2bf);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -92,14 +92,71 @@ __device__ __forceinline__ void mse_search(const float X[16], const float (*tab)
 }
 
 // ------------------------------------------------------------------ MSE
+//
+// Exact candidate pruning (the result is the exhaustive search's, bit for bit):
+//  * c_z = the smallest byte at which every value of the block rounds to 0 (amax <= s S/4).
+//    All bytes >= c_z produce the same codes (0), the same errors (-x) and the same fp32
+//    objective, so with first-index ties only c_z itself can win among them.
+//  * c_b = the largest byte whose top grid value D7 = fp32(6 s S) is <= amax. For every
+//    byte c <= c_b the block max is coded 7 and its error e = fp32(D7(c) - amax) grows as c
+//    falls, and the fp32 fma chain never decreases, so obj(c) >= fp32(e*e) =: LB(c), a
+//    lower bound that is non-increasing in c. Bytes below c_b are visited downwards until
+//    LB exceeds the best objective; then no smaller byte can win.
+// Each lane owns one block and walks its own window [max(c_b,1), c_hi], then downwards;
+// per-candidate constants (s, the two bracketing reciprocals of s S) come from an LDS table.
+
+struct Cand {
+  float s, rlo, rhi, pad;
+};
+
+__device__ __forceinline__ void build_cands(Cand *cand, float S) {
+  for (int c = threadIdx.x; c < 127; c += blockDim.x) {
+    Cand e;
+    e.s = c ? e4m3_value(c) : 0.0f;
+    e.rlo = e.rhi = 0.0f;
+    if (c) recip_bracket((double)e.s * (double)S, e.rlo, e.rhi);
+    e.pad = 0.0f;
+    cand[c] = e;
+  }
+}
+
+// fp32 objective of candidate byte c for |x| (codes unsigned): sum of fma(e, e, acc) in order.
+// fast_ok: all products x * r stay in the normal fp32 range, so the bracketed hardware
+// conversions apply; otherwise the exact threshold table decides every code.
+__device__ __forceinline__ float mse_candidate(const float X[16], int c, const Cand &e, float S,
+                                               bool fast_ok) {
+  unsigned c0, c1;
+  if (fast_ok) {
+    const double sS = (double)e.s * (double)S;
+    c0 = fp4_exact_codes8(X, e.rlo, e.rhi, sS);
+    c1 = fp4_exact_codes8(X + 8, e.rlo, e.rhi, sS);
+  } else {
+    ScaleTable tb;
+    make_table(c, S, tb);
+    c0 = exact_codes8(X, tb);
+    c1 = exact_codes8(X + 8, tb);
+  }
+  float g[16];
+  fp4_decode8(c0, g);
+  fp4_decode8(c1, g + 8);
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float d = (g[i] * e.s) * S;  // fp32(G s S): G s is exact
+    const float err = d - X[i];
+    acc = __builtin_fmaf(err, err, acc);
+  }
+  return acc;
+}
 
 template <int DT>
 __global__ void __launch_bounds__(256)
     k_mse(const void *__restrict__ w, const float *__restrict__ S_arr, uint8_t *__restrict__ scales,
           float *__restrict__ obj, int64_t blocks_per_batch) {
-  __shared__ float tab[126][kTab];
+  __shared__ Cand cand[127];
   const int64_t batch = blockIdx.y;
-  build_tables(tab, S_arr[batch]);
+  const float S = S_arr[batch];
+  build_cands(cand, S);
   __syncthreads();
   const int64_t local = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (local >= blocks_per_batch) return;
@@ -114,7 +171,48 @@ __global__ void __launch_bounds__(256)
   }
   int best_c = 0;
   float best = 0.0f;
-  if (amax != 0.0f) mse_search(X, tab, best_c, best);
+  if (amax != 0.0f) {
+    const double a = amax, Sd = S;
+    // c_z: smallest byte with amax <= s S / 4 (exact); 127 if none
+    int cz;
+    {
+      const float q = fminf(amax * cand[1].rhi * 0x1p-7f, 448.0f);  // ~ 4 amax / S (guess)
+      cz = __builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xFF;
+      cz = cz < 1 ? 1 : (cz > 126 ? 126 : cz);
+      while (cz > 1 && 0.25 * e4m3_value_d(cz - 1) * Sd >= a) --cz;
+      while (cz <= 126 && 0.25 * e4m3_value_d(cz) * Sd < a) ++cz;
+    }
+    // c_b: largest byte with fp32(6 s S) <= amax; 0 if none
+    int cb;
+    {
+      const float q = fminf(amax * cand[1].rlo * 0x1p-9f * (1.0f / 6.0f), 448.0f);
+      cb = __builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xFF;
+      cb = cb > 126 ? 126 : cb;
+      while (cb < 126 && (6.0f * cand[cb + 1].s) * S <= amax) ++cb;
+      while (cb >= 1 && (6.0f * cand[cb].s) * S > amax) --cb;
+    }
+    const int c_hi = cz <= 126 ? cz : 126;
+    const int c_lo = cb >= 1 ? cb : 1;
+    // the largest products (byte 1) stay finite and the smallest reciprocal (byte 126) normal
+    const bool fast_ok = amax * cand[1].rhi < 0x1p126f && cand[126].rlo >= 0x1p-126f;
+    best = INFINITY;
+    for (int c = c_lo; c <= c_hi; ++c) {
+      const float o = mse_candidate(X, c, cand[c], S, fast_ok);
+      if (o < best) {
+        best = o;
+        best_c = c;
+      }
+    }
+    for (int c = c_lo - 1; c >= 1; --c) {
+      const float e7 = (6.0f * cand[c].s) * S - amax;
+      if (e7 * e7 > best) break;  // LB(c) > best, and LB only grows below
+      const float o = mse_candidate(X, c, cand[c], S, fast_ok);
+      if (o <= best) {  // ties: the smaller byte wins
+        best = o;
+        best_c = c;
+      }
+    }
+  }
   scales[blk] = (uint8_t)best_c;
   if (obj) obj[blk] = best;
 }

@@ -6,6 +6,9 @@ the oracle value rounded to nearest-even), MSE objectives, routing lists and the
 Local-Hessian bytes and fp64 objectives; block Hessians within 1e-4 relative Frobenius
 error per block (fp32 accumulation against the oracle's fp64 sums).
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -177,9 +180,45 @@ def test_exact_ties_and_edges(orc):
     assert_bits(y, dq, orc)
 
 
+@pytest.mark.parametrize("S", [1.0, 0.8123457, 3.0517578e-05])
+def test_values_on_and_beside_every_midpoint(orc, S):
+    """Given bytes, values exactly on every E2M1 midpoint / grid point (times s S, rounded to
+    fp32) and one and two ulps either side: exercises the exact fallback of the fast path."""
+    case(f"midpoint neighbourhoods, S={S}")
+    S = np.float32(S)
+    rng = np.random.default_rng(11)
+    bytes_ = [0x01, 0x07, 0x08, 0x30, 0x38, 0x3B, 0x56, 0x6F, 0x7E]
+    pts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 6.5]
+    rows, scs = [], []
+    for b in bytes_:
+        sS = orc.e4m3_value(b) * float(S)
+        vals = []
+        for p in pts:
+            c = np.float32(p * sS)
+            for k in (-2, -1, 0, 1, 2):
+                v = c
+                for _ in range(abs(k)):
+                    v = np.nextafter(v, np.float32(np.inf if k > 0 else 0))
+                vals.append(v)
+        vals = np.array(vals, np.float32)
+        vals *= np.where(rng.random(vals.size) < 0.5, -1, 1).astype(np.float32)
+        pad = (-vals.size) % 16
+        vals = np.concatenate([vals, np.zeros(pad, np.float32)]).reshape(-1, 16)
+        rows.append(vals)
+        scs.append(np.full((vals.shape[0], 1), b, np.uint8))
+    x = np.concatenate(rows)
+    sc = np.concatenate(scs)
+    xd = torch.from_numpy(x).to(DEV)
+    y = nvfp4.fakequant(xd, dev_S(S), torch.from_numpy(sc).to(DEV))
+    codes, _ = nvfp4.quantize(xd, dev_S(S), torch.from_numpy(sc).to(DEV))
+    dq, cr, _ = orc.fakequant(x, S, sc)
+    assert np.array_equal(codes.cpu().numpy(), cr)
+    assert_bits(y, dq, orc)
+    y2 = nvfp4.dequantize(codes, torch.from_numpy(sc).to(DEV), dev_S(S))
+    assert_bits(y2, dq, orc)
+
+
 def test_worked_example_on_gpu(orc):
-    import json
-    import os
     case("worked example block: 84 -> scale 14")
     with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")) as f:
         g = json.load(f)
@@ -208,6 +247,29 @@ def test_mse_search(orc, tiny, which):
     sc, obj = nvfp4.scale_search_mse(w.to(DEV), dev_S(S), return_obj=True)
     sr, orf = orc.scales_mse(wn, S, with_obj=True)
     assert np.array_equal(sc.cpu().numpy(), sr)
+    assert np.array_equal(obj.cpu().numpy().view(np.uint32), orf.view(np.uint32))
+
+
+@pytest.mark.parametrize("S", [None, 1e-9, 1e-3, 1.0, 50.0])
+def test_mse_pruning_edges(orc, S):
+    """Blocks that put the window edges in odd places: everything saturating (tiny S),
+    everything rounding to zero for most bytes (huge S), single non-zero values, constant
+    blocks, on-grid blocks and exact ties."""
+    case(f"mse pruning edges S={S}")
+    rng = np.random.default_rng(21)
+    blocks = [rng.standard_normal((64, 16)).astype(np.float32) * np.float32(0.02)]
+    one = np.zeros((16, 16), np.float32)
+    one[np.arange(16), np.arange(16)] = rng.uniform(0.001, 1.0, 16).astype(np.float32)
+    blocks.append(one)
+    blocks.append(np.repeat(rng.uniform(-1, 1, (16, 1)).astype(np.float32), 16, axis=1))
+    blocks.append(synth.on_grid_block_values(3, 32 * 16).reshape(32, 16) * np.float32(0.125))
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")) as f:
+        blocks.append(np.array([json.load(f)["block"]], np.float32))
+    x = np.concatenate(blocks).reshape(-1, 16)
+    Sv = orc.tensor_scale(x) if S is None else np.float32(S)
+    sc, obj = nvfp4.scale_search_mse(torch.from_numpy(x).to(DEV), dev_S(Sv), return_obj=True)
+    sr, orf = orc.scales_mse(x, Sv, with_obj=True)
+    assert np.array_equal(sc.cpu().numpy(), sr), np.argwhere(sc.cpu().numpy() != sr)[:5]
     assert np.array_equal(obj.cpu().numpy().view(np.uint32), orf.view(np.uint32))
 
 
