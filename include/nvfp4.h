@@ -129,7 +129,7 @@ NVFP4_API int nvfp4_block_hessian(const void *x, int dtype, int64_t tokens, int6
  * smallest d H_b d^T wins, with d_i = fp32(dq_i(c) - w_i) and H_b the block's 16x16
  * matrix shared by all rows (the block-diagonal approximation). The objective is
  * evaluated as y_i = sum_j H_ij d_j, obj = sum_i d_i y_i in double precision, ascending
- * indices, separate multiply and add. A block with an all-zero H_b takes the MSE choice
+ * indices, one fused multiply-add per term. A block with an all-zero H_b takes the MSE choice
  * (objective reported as 0); an all-zero block gets 0x00.
  * w: [batch][rows][cols]; S: [batch]; H: [batch][cols/16][16][16] fp32;
  * scales: [batch][rows][cols/16]; obj (nullable): same shape, double.

@@ -40,7 +40,8 @@
  *  - nibble order: element 2j in the low nibble of byte j;
  *  - MSE objective: fp32, e_i = fp32(dq_i - x_i), acc = fmaf(e_i, e_i, acc) for i = 0..15;
  *  - Local-Hessian objective: d_i = fp32(dq_i - w_i); y_i = sum_j H_ij d_j and
- *    obj = sum_i d_i y_i, both in double, ascending index, separate multiply and add;
+ *    obj = sum_i d_i y_i, both in double, ascending index, each term added with a fused
+ *    multiply-add (one rounding per term);
  *  - argmins take the first (smallest byte) minimum; a block whose H_b is all zero
  *    takes the MSE choice.
  */
@@ -281,8 +282,8 @@ double oracle_block_lh_objective(const float *w, int byte, float S, const float 
     double obj = 0.0;
     for (int i = 0; i < 16; ++i) {
         double y = 0.0;
-        for (int j = 0; j < 16; ++j) y = y + (double)Hb[i * 16 + j] * d[j];
-        obj = obj + d[i] * y;
+        for (int j = 0; j < 16; ++j) y = fma((double)Hb[i * 16 + j], d[j], y);
+        obj = fma(d[i], y, obj);
     }
     return obj;
 }

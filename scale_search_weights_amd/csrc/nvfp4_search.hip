@@ -15,29 +15,6 @@
 
 namespace nvfp4 {
 
-constexpr int kTab = 16;  // floats per candidate entry: t[0..6], d[1..7], 2 pad
-
-__device__ __forceinline__ void build_tables(float (*tab)[kTab], float S) {
-  for (int c = threadIdx.x; c < 126; c += blockDim.x) {
-    ScaleTable tb;
-    make_table(c + 1, S, tb);
-#pragma unroll
-    for (int j = 0; j < 7; ++j) tab[c][j] = tb.t[j];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) tab[c][6 + j] = tb.d[j];
-    tab[c][14] = 0.0f;
-    tab[c][15] = 0.0f;
-  }
-}
-
-// magnitude of the dequantised value of |x| under a candidate's table
-__device__ __forceinline__ float rtn_mag(float X, const float *e) {
-  float d = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 7; ++j) d = (X > e[j]) ? e[7 + j] : d;
-  return d;
-}
-
 template <int DT>
 __device__ __forceinline__ void load16(const void *__restrict__ x, int64_t blk, float v[16]) {
   if (DT == NVFP4_DTYPE_BF16) {
@@ -58,35 +35,6 @@ __device__ __forceinline__ void load16(const void *__restrict__ x, int64_t blk, 
       v[4 * k + 1] = a.y;
       v[4 * k + 2] = a.z;
       v[4 * k + 3] = a.w;
-    }
-  }
-}
-
-// MSE objective of one candidate: fp32, e_i = fp32(dq_i - x_i), acc = fma(e_i, e_i, acc).
-// With |x| and the magnitude: dq - x = sign(x) (d - |x|) rounds symmetrically, and for a
-// zero code (d = 0) it is -x; the square is the same either way.
-__device__ __forceinline__ float mse_obj(const float X[16], const float *e) {
-  float acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float err = rtn_mag(X[i], e) - X[i];
-    acc = __builtin_fmaf(err, err, acc);
-  }
-  return acc;
-}
-
-__device__ __forceinline__ void mse_search(const float X[16], const float (*tab)[kTab],
-                                           int &best_c, float &best) {
-  best = INFINITY;
-  best_c = 0;
-  for (int c = 0; c < 126; ++c) {
-    float e[kTab];
-#pragma unroll
-    for (int j = 0; j < 14; ++j) e[j] = tab[c][j];
-    const float acc = mse_obj(X, e);
-    if (acc < best) {
-      best = acc;
-      best_c = c + 1;
     }
   }
 }
@@ -149,6 +97,57 @@ __device__ __forceinline__ float mse_candidate(const float X[16], int c, const C
   return acc;
 }
 
+// c_z: the smallest byte with amax <= s S / 4 (every value rounds to 0), 127 if none;
+// c_b: the largest byte with fp32(6 s S) <= amax (the block max saturates), 0 if none.
+// Both start from an FP8-convert guess and are settled by exact comparisons.
+__device__ __forceinline__ void window_bounds(float amax, const Cand *cand, float S, int &cz,
+                                              int &cb) {
+  const double a = amax, Sd = S;
+  const float qz = fminf(amax * cand[1].rhi * 0x1p-7f, 448.0f);  // ~ 4 amax / S
+  cz = __builtin_amdgcn_cvt_pk_fp8_f32(qz, qz, 0, false) & 0xFF;
+  cz = cz < 1 ? 1 : (cz > 126 ? 126 : cz);
+  while (cz > 1 && 0.25 * e4m3_value_d(cz - 1) * Sd >= a) --cz;
+  while (cz <= 126 && 0.25 * e4m3_value_d(cz) * Sd < a) ++cz;
+  const float qb = fminf(amax * cand[1].rlo * 0x1p-9f * (1.0f / 6.0f), 448.0f);  // ~ amax/(6S)
+  cb = __builtin_amdgcn_cvt_pk_fp8_f32(qb, qb, 0, false) & 0xFF;
+  cb = cb > 126 ? 126 : cb;
+  while (cb < 126 && (6.0f * cand[cb + 1].s) * S <= amax) ++cb;
+  while (cb >= 1 && (6.0f * cand[cb].s) * S > amax) --cb;
+}
+
+// products x * r stay in the normal fp32 range for every candidate
+__device__ __forceinline__ bool fast_path_ok(float amax, const Cand *cand) {
+  return amax * cand[1].rhi < 0x1p126f && cand[126].rlo >= 0x1p-126f;
+}
+
+// Pruned MSE search over |x| (see above); amax > 0.
+__device__ __forceinline__ void mse_pruned(const float X[16], float amax, const Cand *cand,
+                                           float S, int &best_c, float &best) {
+  int cz, cb;
+  window_bounds(amax, cand, S, cz, cb);
+  const int c_hi = cz <= 126 ? cz : 126;
+  const int c_lo = cb >= 1 ? cb : 1;
+  const bool fast_ok = fast_path_ok(amax, cand);
+  best = INFINITY;
+  best_c = 0;
+  for (int c = c_lo; c <= c_hi; ++c) {
+    const float o = mse_candidate(X, c, cand[c], S, fast_ok);
+    if (o < best) {
+      best = o;
+      best_c = c;
+    }
+  }
+  for (int c = c_lo - 1; c >= 1; --c) {
+    const float e7 = (6.0f * cand[c].s) * S - amax;
+    if (e7 * e7 > best) break;  // LB(c) > best, and LB only grows below
+    const float o = mse_candidate(X, c, cand[c], S, fast_ok);
+    if (o <= best) {  // ties: the smaller byte wins
+      best = o;
+      best_c = c;
+    }
+  }
+}
+
 template <int DT>
 __global__ void __launch_bounds__(256)
     k_mse(const void *__restrict__ w, const float *__restrict__ S_arr, uint8_t *__restrict__ scales,
@@ -171,48 +170,7 @@ __global__ void __launch_bounds__(256)
   }
   int best_c = 0;
   float best = 0.0f;
-  if (amax != 0.0f) {
-    const double a = amax, Sd = S;
-    // c_z: smallest byte with amax <= s S / 4 (exact); 127 if none
-    int cz;
-    {
-      const float q = fminf(amax * cand[1].rhi * 0x1p-7f, 448.0f);  // ~ 4 amax / S (guess)
-      cz = __builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xFF;
-      cz = cz < 1 ? 1 : (cz > 126 ? 126 : cz);
-      while (cz > 1 && 0.25 * e4m3_value_d(cz - 1) * Sd >= a) --cz;
-      while (cz <= 126 && 0.25 * e4m3_value_d(cz) * Sd < a) ++cz;
-    }
-    // c_b: largest byte with fp32(6 s S) <= amax; 0 if none
-    int cb;
-    {
-      const float q = fminf(amax * cand[1].rlo * 0x1p-9f * (1.0f / 6.0f), 448.0f);
-      cb = __builtin_amdgcn_cvt_pk_fp8_f32(q, q, 0, false) & 0xFF;
-      cb = cb > 126 ? 126 : cb;
-      while (cb < 126 && (6.0f * cand[cb + 1].s) * S <= amax) ++cb;
-      while (cb >= 1 && (6.0f * cand[cb].s) * S > amax) --cb;
-    }
-    const int c_hi = cz <= 126 ? cz : 126;
-    const int c_lo = cb >= 1 ? cb : 1;
-    // the largest products (byte 1) stay finite and the smallest reciprocal (byte 126) normal
-    const bool fast_ok = amax * cand[1].rhi < 0x1p126f && cand[126].rlo >= 0x1p-126f;
-    best = INFINITY;
-    for (int c = c_lo; c <= c_hi; ++c) {
-      const float o = mse_candidate(X, c, cand[c], S, fast_ok);
-      if (o < best) {
-        best = o;
-        best_c = c;
-      }
-    }
-    for (int c = c_lo - 1; c >= 1; --c) {
-      const float e7 = (6.0f * cand[c].s) * S - amax;
-      if (e7 * e7 > best) break;  // LB(c) > best, and LB only grows below
-      const float o = mse_candidate(X, c, cand[c], S, fast_ok);
-      if (o <= best) {  // ties: the smaller byte wins
-        best = o;
-        best_c = c;
-      }
-    }
-  }
+  if (amax != 0.0f) mse_pruned(X, amax, cand, S, best_c, best);
   scales[blk] = (uint8_t)best_c;
   if (obj) obj[blk] = best;
 }
@@ -229,21 +187,84 @@ int launch_mse(const void *w, int dtype, int64_t batch, int64_t rows, int64_t co
 }
 
 // ------------------------------------------------------------------ Local-Hessian
-
+//
 // Grid: x = chunks of 256 rows, y = block column b, z = batch entry. All rows of block
 // column b share H_b (the block-diagonal approximation), held in LDS as doubles.
+//
+// The objective of a candidate is evaluated exactly as the definition fixes it (fp64,
+// ascending indices, one fma per term), so bytes and objectives match bit for bit. Only
+// candidates that can win are evaluated:
+//  * bytes >= c_z (every value rounds to 0) share one objective: only c_z is evaluated;
+//  * below c_b the block max saturates; with g_i = H_ii - sum_{j!=i} (|H_ij| + |H_ji|)/2,
+//    d H d^T >= sum_i g_i d_i^2 for any d, so when every g_i > 0 the block max's own error
+//    e7 gives obj(c) >= g_m e7(c)^2, non-increasing in c. Bytes below c_b are visited
+//    downwards until that bound, with a margin covering the fp64 rounding of the objective
+//    (gamma_33 times kappa = max_i (H_ii + r_i) / g_i), exceeds the best objective.
+
+__device__ __forceinline__ double lh_candidate(const float v[16], int c, const Cand &e, float S,
+                                               bool fast_ok, const double *hb) {
+  unsigned c0, c1;
+  if (fast_ok) {
+    const double sS = (double)e.s * (double)S;
+    c0 = fp4_exact_codes8(v, e.rlo, e.rhi, sS);
+    c1 = fp4_exact_codes8(v + 8, e.rlo, e.rhi, sS);
+  } else {
+    ScaleTable tb;
+    make_table(c, S, tb);
+    c0 = exact_codes8(v, tb);
+    c1 = exact_codes8(v + 8, tb);
+  }
+  float g[16];
+  fp4_decode8(fp4_clear_neg_zero(c0), g);
+  fp4_decode8(fp4_clear_neg_zero(c1), g + 8);
+  double dl[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dl[i] = (double)((g[i] * e.s) * S - v[i]);  // fp32(dq - w)
+  // i stays a rolled, wave-uniform loop so H rows stream from LDS rather than occupying
+  // 512 VGPRs; dl[i] becomes a uniform register index
+  double o = 0.0;
+#pragma unroll 1
+  for (int i = 0; i < 16; ++i) {
+    double y = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) y = __builtin_fma(hb[i * 16 + j], dl[j], y);
+    o = __builtin_fma(dl[i], y, o);
+  }
+  return o;
+}
+
 template <int DT>
 __global__ void __launch_bounds__(256)
-    k_lh_exact(const void *__restrict__ w, const float *__restrict__ S_arr,
-               const float *__restrict__ H, uint8_t *__restrict__ scales, double *__restrict__ obj,
-               int64_t rows, int64_t nb) {
-  __shared__ float tab[126][kTab];
+    k_lh(const void *__restrict__ w, const float *__restrict__ S_arr, const float *__restrict__ H,
+         uint8_t *__restrict__ scales, double *__restrict__ obj, int64_t rows, int64_t nb) {
+  __shared__ Cand cand[127];
   __shared__ double hb[256];
+  __shared__ double gw[16];
+  __shared__ double kap[16];
   const int64_t batch = blockIdx.z, b = blockIdx.y;
-  build_tables(tab, S_arr[batch]);
+  const float S = S_arr[batch];
+  build_cands(cand, S);
   const float hv = H[(batch * nb + b) * 256 + threadIdx.x];
   hb[threadIdx.x] = (double)hv;
   const int h_nonzero = __syncthreads_or(hv != 0.0f);
+  if (threadIdx.x < 16) {
+    const int i = threadIdx.x;
+    double off = 0.0;
+    for (int j = 0; j < 16; ++j)
+      if (j != i) off += 0.5 * (fabs(hb[i * 16 + j]) + fabs(hb[j * 16 + i]));
+    const double d = hb[i * 17];
+    const double g = d - off - 1e-12 * (fabs(d) + off);  // margin for the rounding of these sums
+    gw[i] = g;
+    kap[i] = g > 0.0 ? (fabs(d) + off) / g : INFINITY;
+  }
+  __syncthreads();
+  double kappa = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) kappa = fmax(kappa, kap[i]);
+  // prune only with a well-defined bound; margin on the comparison with fp64 objectives
+  const bool prune = kappa < 1e9;
+  const double margin = 1.0 + 8e-15 * kappa + 1e-13;
+
   const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (row >= rows) return;
   const int64_t blk = (batch * rows + row) * nb + b;
@@ -255,38 +276,41 @@ __global__ void __launch_bounds__(256)
     X[i] = fabsf(v[i]);
     amax = fmaxf(amax, X[i]);
   }
+  int m = 0;  // first index of the block max
+#pragma unroll
+  for (int i = 15; i >= 0; --i) m = (X[i] == amax) ? i : m;
   int best_c = 0;
   double best_o = 0.0;
   if (amax != 0.0f) {
     if (!h_nonzero) {
       float bm;
-      mse_search(X, tab, best_c, bm);
+      mse_pruned(X, amax, cand, S, best_c, bm);
     } else {
+      int cz, cb;
+      window_bounds(amax, cand, S, cz, cb);
+      const int c_hi = cz <= 126 ? cz : 126;
+      const int c_lo = cb >= 1 ? cb : 1;
+      const bool fast_ok = fast_path_ok(amax, cand);
+      double gm = gw[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) gm = (m == i) ? gw[i] : gm;
       best_o = INFINITY;
-      for (int c = 0; c < 126; ++c) {
-        float e[kTab];
-#pragma unroll
-        for (int j = 0; j < 14; ++j) e[j] = tab[c][j];
-        double dl[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float d = rtn_mag(X[i], e);
-          const float dq = (v[i] < 0.0f && d > 0.0f) ? -d : d;
-          dl[i] = (double)(dq - v[i]);
-        }
-        // i stays a rolled (wave-uniform) loop so H_b rows stream from LDS instead of
-        // being hoisted into registers; dl[i] is a uniform register index
-        double o = 0.0;
-#pragma unroll 1
-        for (int i = 0; i < 16; ++i) {
-          double y = 0.0;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) y = __dadd_rn(y, __dmul_rn(hb[i * 16 + j], dl[j]));
-          o = __dadd_rn(o, __dmul_rn(dl[i], y));
-        }
+      for (int c = c_lo; c <= c_hi; ++c) {
+        const double o = lh_candidate(v, c, cand[c], S, fast_ok, hb);
         if (o < best_o) {
           best_o = o;
-          best_c = c + 1;
+          best_c = c;
+        }
+      }
+      for (int c = c_lo - 1; c >= 1; --c) {
+        if (prune) {
+          const double e7 = (double)((6.0f * cand[c].s) * S - amax);
+          if (gm * e7 * e7 > best_o * margin) break;
+        }
+        const double o = lh_candidate(v, c, cand[c], S, fast_ok, hb);
+        if (o <= best_o) {  // ties: the smaller byte wins
+          best_o = o;
+          best_c = c;
         }
       }
     }
@@ -301,9 +325,9 @@ int launch_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows, 
   const int64_t nb = cols / 16;
   const dim3 g((unsigned)((rows + 255) / 256), (unsigned)nb, (unsigned)batch), b(256);
   if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_lh_exact<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
+    hipLaunchKernelGGL(k_lh<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
   else
-    hipLaunchKernelGGL(k_lh_exact<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
+    hipLaunchKernelGGL(k_lh<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
