@@ -196,6 +196,35 @@ __device__ __forceinline__ unsigned fp4_exact_codes8(const float *v, float lo, f
   return a;
 }
 
+// ---- cross-lane exchange through the VALU (v_permlane16_swap / v_permlane32_swap)
+// A "row" is 16 consecutive lanes; rows pair up as {0,1} and {2,3}, halves as {0-31, 32-63}.
+// swap16(a, b) returns (r0, r1): in an even row r0 = its own a, r1 = a of the odd row; in an
+// odd row r0 = b of the even row, r1 = its own b (swap32 likewise with the two halves).
+struct LanePair {
+  float r0, r1;
+};
+__device__ __forceinline__ LanePair swap16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair swap32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// x of the lane 16 (resp. 32) positions away: odd rows take r0, even rows r1
+__device__ __forceinline__ float xor16(float x) {
+  const LanePair r = swap16(x, x);
+  return (threadIdx.x & 16) ? r.r0 : r.r1;
+}
+__device__ __forceinline__ float xor32(float x) {
+  const LanePair r = swap32(x, x);
+  return (threadIdx.x & 32) ? r.r0 : r.r1;
+}
+__device__ __forceinline__ int xor16(int x) { return __float_as_int(xor16(__int_as_float(x))); }
+__device__ __forceinline__ int xor32(int x) { return __float_as_int(xor32(__int_as_float(x))); }
+
 // Clear the sign bit of every zero-magnitude nibble (the convert keeps the sign of -0).
 __device__ __forceinline__ unsigned fp4_clear_neg_zero(unsigned c) {
   const unsigned m = c & 0x77777777u;

@@ -188,59 +188,182 @@ int launch_mse(const void *w, int dtype, int64_t batch, int64_t rows, int64_t co
 
 // ------------------------------------------------------------------ Local-Hessian
 //
-// Grid: x = chunks of 256 rows, y = block column b, z = batch entry. All rows of block
+// Grid: x = chunks of 64 rows, y = block column b, z = batch entry. All rows of block
 // column b share H_b (the block-diagonal approximation), held in LDS as doubles.
 //
-// The objective of a candidate is evaluated exactly as the definition fixes it (fp64,
-// ascending indices, one fma per term), so bytes and objectives match bit for bit. Only
-// candidates that can win are evaluated:
-//  * bytes >= c_z (every value rounds to 0) share one objective: only c_z is evaluated;
+// The chosen byte and its objective equal those of the definition evaluated exactly as it
+// is written (fp64, ascending indices, one fma per term), bit for bit. Only candidates that
+// can win are visited:
+//  * bytes >= c_z (every value rounds to 0) share one objective: only c_z is visited;
 //  * below c_b the block max saturates; with g_i = H_ii - sum_{j!=i} (|H_ij| + |H_ji|)/2,
 //    d H d^T >= sum_i g_i d_i^2 for any d, so when every g_i > 0 the block max's own error
 //    e7 gives obj(c) >= g_m e7(c)^2, non-increasing in c. Bytes below c_b are visited
 //    downwards until that bound, with a margin covering the fp64 rounding of the objective
 //    (gamma_33 times kappa = max_i (H_ii + r_i) / g_i), exceeds the best objective.
+//
+// A wave handles 16 (row, block) pairs of one block column: lane l owns pair p = l & 15 and the
+// four elements 4q..4q+3, q = l >> 4. For a candidate each lane forms its four fp32 weight
+// errors d and four v_mfma_f32_16x16x4_f32 compute Y = H_b d for all 16 pairs: in step t the
+// K slot of lane group q is element 4q + t, so A = H[p][4q+t] and B = d_p[4q+t] are the
+// lane's own values, and the 16x16 result leaves Y_p[4q..4q+3] in the lane that holds
+// d_p[4q..4q+3]. A four-term dot and two cross-lane adds give the fp32 objective.
+// Screening: |fp32 obj - exact obj| <= 1e-5 (sum_i |d_i| a_i)^2 + 2^-110 with
+// a_i^2 >= max_j max(|H_ij|, |H_ji|) (so sum_ij |d_i||H_ij||d_j| <= (sum |d_i| a_i)^2; the
+// constant is ~8x the worst-case fp32 rounding of the 16-term products, the four-term dot
+// and the two adds; the absolute term covers flushed denormals). Per pair the kernel keeps
+// theta = min(obj + err) and the two smallest (obj - err): every candidate that can still be
+// the exact argmin has obj - err <= theta. If at most two do, they are re-evaluated in the
+// exact fp64 order (split over the pair's four lanes) and the smaller wins; if three or
+// more do, or values are too small or large for the fast path, the pair is rescanned
+// exactly. The downward pruning compares with theta.
 
-__device__ __forceinline__ double lh_candidate(const float v[16], int c, const Cand &e, float S,
-                                               bool fast_ok, const double *hb) {
-  unsigned c0, c1;
+// the four fp32 weight errors of this lane's elements under candidate c
+__device__ __forceinline__ void lh_delta4(const float v[4], int c, const Cand &e, float S,
+                                          bool fast_ok, float d[4]) {
+  unsigned code;
   if (fast_ok) {
-    const double sS = (double)e.s * (double)S;
-    c0 = fp4_exact_codes8(v, e.rlo, e.rhi, sS);
-    c1 = fp4_exact_codes8(v + 8, e.rlo, e.rhi, sS);
+    unsigned a = 0u, b = 0u;
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[0] * e.rlo, v[1] * e.rlo, 1.0f, 0);
+    a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, v[2] * e.rlo, v[3] * e.rlo, 1.0f, 1);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, v[0] * e.rhi, v[1] * e.rhi, 1.0f, 0);
+    b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, v[2] * e.rhi, v[3] * e.rhi, 1.0f, 1);
+    a &= 0xFFFFu;
+    b &= 0xFFFFu;
+    if (a != b) {
+      float v8[8] = {v[0], v[1], v[2], v[3], 0.0f, 0.0f, 0.0f, 0.0f};
+      a = fp4_resolve8(v8, a, b, (double)e.s * (double)S);
+    }
+    code = a;
   } else {
     ScaleTable tb;
     make_table(c, S, tb);
-    c0 = exact_codes8(v, tb);
-    c1 = exact_codes8(v + 8, tb);
+    float v8[8] = {v[0], v[1], v[2], v[3], 0.0f, 0.0f, 0.0f, 0.0f};
+    code = exact_codes8(v8, tb) & 0xFFFFu;
   }
-  float g[16];
-  fp4_decode8(fp4_clear_neg_zero(c0), g);
-  fp4_decode8(fp4_clear_neg_zero(c1), g + 8);
-  double dl[16];
+  // (a -0 code needs no clearing here: -0 - v and +0 - v are the same error)
+  nv_v2f g01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
+  nv_v2f g23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1);
+  d[0] = (g01.x * e.s) * S - v[0];
+  d[1] = (g01.y * e.s) * S - v[1];
+  d[2] = (g23.x * e.s) * S - v[2];
+  d[3] = (g23.y * e.s) * S - v[3];
+}
+
+// x of rows 0, 1, 2, 3 (same lane within the row), in every lane
+__device__ __forceinline__ void rows4(float x, float out[4]) {
+  const LanePair a = swap16(x, x);       // rows (0 | 2, 1 | 3)
+  const LanePair e = swap32(a.r0, a.r0);  // rows (0, 2)
+  const LanePair o = swap32(a.r1, a.r1);  // rows (1, 3)
+  out[0] = e.r0;
+  out[1] = o.r0;
+  out[2] = e.r1;
+  out[3] = o.r1;
+}
+
+// exact fp64 objective (the definition's order) of the pair, from the four lanes' errors;
+// every lane of the pair returns the same value. Row q holds errors 4q..4q+3 in d[0..3].
+__device__ __forceinline__ double lh_exact_split(const float d[4], int q, const double *hb) {
+  float D[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dl[i] = (double)((g[i] * e.s) * S - v[i]);  // fp32(dq - w)
-  // i stays a rolled, wave-uniform loop so H rows stream from LDS rather than occupying
-  // 512 VGPRs; dl[i] becomes a uniform register index
-  double o = 0.0;
+  for (int r = 0; r < 4; ++r) {
+    float t[4];
+    rows4(d[r], t);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) D[4 * g + r] = t[g];
+  }
+  // y_i for this row's four indices i = 4q + r; the source row g stays a rolled, wave-uniform
+  // loop so H streams from LDS instead of being hoisted into registers
+  double y[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 1
-  for (int i = 0; i < 16; ++i) {
-    double y = 0.0;
+  for (int g = 0; g < 4; ++g) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) y = __builtin_fma(hb[i * 16 + j], dl[j], y);
-    o = __builtin_fma(dl[i], y, o);
+    for (int jj = 0; jj < 4; ++jj) {
+      const double dj = (double)D[4 * g + jj];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = __builtin_fma(hb[(4 * q + r) * 16 + 4 * g + jj], dj, y[r]);
+    }
   }
+  double Y[16];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float lo[4], hi[4];
+    rows4(__int_as_float(__double2loint(y[r])), lo);
+    rows4(__int_as_float(__double2hiint(y[r])), hi);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      Y[4 * g + r] = __hiloint2double(__float_as_int(hi[g]), __float_as_int(lo[g]));
+  }
+  double o = 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) o = __builtin_fma((double)D[k], Y[k], o);
   return o;
+}
+
+// Screening state of one lane: the smallest upper bound and the three smallest lower bounds
+// (with the bytes of the first two) over the candidates this lane has scored.
+struct Screen {
+  float theta, L1, L2, L3;
+  int c1, c2;
+};
+
+__device__ __forceinline__ void screen_add(Screen &z, float L, float U, int c) {
+  z.theta = fminf(z.theta, U);
+  if (L < z.L1) {
+    z.L3 = z.L2; z.L2 = z.L1; z.c2 = z.c1; z.L1 = L; z.c1 = c;
+  } else if (L < z.L2) {
+    z.L3 = z.L2; z.L2 = L; z.c2 = c;
+  } else if (L < z.L3) {
+    z.L3 = L;
+  }
+}
+
+// merge with the lane 16 (OFF = 16) or 32 (OFF = 32) positions away (both lanes end with
+// the union's state)
+template <int OFF>
+__device__ __forceinline__ void screen_merge(Screen &z) {
+  auto other = [](auto x) { return OFF == 16 ? xor16(x) : xor32(x); };
+  Screen o;
+  o.theta = other(z.theta);
+  o.L1 = other(z.L1);
+  o.L2 = other(z.L2);
+  o.L3 = other(z.L3);
+  o.c1 = other(z.c1);
+  o.c2 = other(z.c2);
+  // order the two lists' entries deterministically (by L, then byte) so both lanes agree
+  auto less = [](float La, int ca, float Lb, int cb) { return La < Lb || (La == Lb && ca < cb); };
+  Screen r;
+  r.theta = fminf(z.theta, o.theta);
+  float A[3] = {z.L1, z.L2, z.L3}, B[3] = {o.L1, o.L2, o.L3};
+  int Ac[3] = {z.c1, z.c2, 0}, Bc[3] = {o.c1, o.c2, 0};
+  float M[3];
+  int Mc[3];
+  int ia = 0, ib = 0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    float La = ia == 0 ? A[0] : (ia == 1 ? A[1] : A[2]);
+    int ca = ia == 0 ? Ac[0] : (ia == 1 ? Ac[1] : Ac[2]);
+    float Lb = ib == 0 ? B[0] : (ib == 1 ? B[1] : B[2]);
+    int cb = ib == 0 ? Bc[0] : (ib == 1 ? Bc[1] : Bc[2]);
+    const bool ta = less(La, ca, Lb, cb);
+    M[k] = ta ? La : Lb;
+    Mc[k] = ta ? ca : cb;
+    ia += ta ? 1 : 0;
+    ib += ta ? 0 : 1;
+  }
+  r.L1 = M[0]; r.c1 = Mc[0]; r.L2 = M[1]; r.c2 = Mc[1]; r.L3 = M[2];
+  z = r;
 }
 
 template <int DT>
 __global__ void __launch_bounds__(256)
-    k_lh(const void *__restrict__ w, const float *__restrict__ S_arr, const float *__restrict__ H,
-         uint8_t *__restrict__ scales, double *__restrict__ obj, int64_t rows, int64_t nb) {
+    k_lh_mfma(const void *__restrict__ w, const float *__restrict__ S_arr,
+              const float *__restrict__ H, uint8_t *__restrict__ scales, double *__restrict__ obj,
+              int64_t rows, int64_t nb) {
   __shared__ Cand cand[127];
   __shared__ double hb[256];
   __shared__ double gw[16];
   __shared__ double kap[16];
+  __shared__ float aw[16];
   const int64_t batch = blockIdx.z, b = blockIdx.y;
   const float S = S_arr[batch];
   build_cands(cand, S);
@@ -249,85 +372,251 @@ __global__ void __launch_bounds__(256)
   const int h_nonzero = __syncthreads_or(hv != 0.0f);
   if (threadIdx.x < 16) {
     const int i = threadIdx.x;
-    double off = 0.0;
-    for (int j = 0; j < 16; ++j)
+    double off = 0.0, mx = 0.0;
+    for (int j = 0; j < 16; ++j) {
+      mx = fmax(mx, fmax(fabs(hb[i * 16 + j]), fabs(hb[j * 16 + i])));
       if (j != i) off += 0.5 * (fabs(hb[i * 16 + j]) + fabs(hb[j * 16 + i]));
-    const double d = hb[i * 17];
-    const double g = d - off - 1e-12 * (fabs(d) + off);  // margin for the rounding of these sums
+    }
+    const double dg = hb[i * 17];
+    const double g = dg - off - 1e-12 * (fabs(dg) + off);
     gw[i] = g;
-    kap[i] = g > 0.0 ? (fabs(d) + off) / g : INFINITY;
+    kap[i] = g > 0.0 ? (fabs(dg) + off) / g : INFINITY;
+    aw[i] = (float)(sqrt(mx) * (1.0 + 0x1p-20));  // a_i^2 >= max |H| along row and column i
   }
   __syncthreads();
   double kappa = 0.0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) kappa = fmax(kappa, kap[i]);
-  // prune only with a well-defined bound; margin on the comparison with fp64 objectives
   const bool prune = kappa < 1e9;
   const double margin = 1.0 + 8e-15 * kappa + 1e-13;
 
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= rows) return;
-  const int64_t blk = (batch * rows + row) * nb + b;
-  float v[16], X[16];
-  load16<DT>(w, blk, v);
-  float amax = 0.0f;
+  if (!h_nonzero) {  // every candidate has objective 0: the MSE choice, one lane per row
+    if (threadIdx.x < 64) {
+      const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
+      if (row < rows) {
+        const int64_t blk = (batch * rows + row) * nb + b;
+        float v[16], X[16];
+        load16<DT>(w, blk, v);
+        float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    X[i] = fabsf(v[i]);
-    amax = fmaxf(amax, X[i]);
+        for (int i = 0; i < 16; ++i) {
+          X[i] = fabsf(v[i]);
+          amax = fmaxf(amax, X[i]);
+        }
+        int bc = 0;
+        float bm = 0.0f;
+        if (amax != 0.0f) mse_pruned(X, amax, cand, S, bc, bm);
+        scales[blk] = (uint8_t)bc;
+        if (obj) obj[blk] = 0.0;
+      }
+    }
+    return;
   }
-  int m = 0;  // first index of the block max
+
+  const int lane = threadIdx.x & 63, p = lane & 15, q = lane >> 4;
+  const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + p;
+  const bool valid = row < rows;
+  const int64_t blk = (batch * rows + (valid ? row : 0)) * nb + b;
+  float ha[4], ab[4], v[4];
 #pragma unroll
-  for (int i = 15; i >= 0; --i) m = (X[i] == amax) ? i : m;
+  for (int t = 0; t < 4; ++t) {
+    ha[t] = (float)hb[p * 16 + 4 * q + t];
+    ab[t] = aw[4 * q + t];
+  }
+  if (DT == NVFP4_DTYPE_BF16) {
+    uint2 u = make_uint2(0u, 0u);
+    if (valid) u = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(w) + blk * 16)[q];
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+  } else {
+    float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid) u = reinterpret_cast<const float4 *>(static_cast<const float *>(w) + blk * 16)[q];
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+  float lmax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  LanePair t = swap16(lmax, lmax);
+  lmax = fmaxf(t.r0, t.r1);
+  t = swap32(lmax, lmax);
+  const float amax = fmaxf(t.r0, t.r1);
+  int li = 16;
+#pragma unroll
+  for (int r = 3; r >= 0; --r) li = (fabsf(v[r]) == amax) ? 4 * q + r : li;
+  li = min(li, xor16(li));
+  const int m = min(li, xor32(li));  // first index of the block max
+
+  const bool live = valid && amax != 0.0f;
+  int cz = 127, cb = 0;
+  if (live) window_bounds(amax, cand, S, cz, cb);
+  const int c_hi = cz <= 126 ? cz : 126;
+  const int c_lo = cb >= 1 ? cb : 1;
+  const bool fast_ok = fast_path_ok(amax, cand) && amax >= 0x1p-60f;
+  const double gm = gw[m < 16 ? m : 0];
+
+  // ---- screen on MFMA, four candidates per step (independent MFMA chains); after the
+  // transposing reduction lane group q holds the objective of the step's candidate q
+  bool screen = live && fast_ok;
+  Screen z = {INFINITY, INFINITY, INFINITY, INFINITY, 0, 0};
+  auto step4 = [&](const int cs[4], const bool acts[4]) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    float P[4], B[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (acts[k]) lh_delta4(v, cs[k], cand[cs[k]], S, true, d);
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[t], d[t], acc, 0, 0, 0);
+      float op = d[0] * acc[0];
+      float bp = fabsf(d[0]) * ab[0];
+#pragma unroll
+      for (int r = 1; r < 4; ++r) {
+        op = __builtin_fmaf(d[r], acc[r], op);
+        bp = __builtin_fmaf(fabsf(d[r]), ab[r], bp);
+      }
+      P[k] = op;
+      B[k] = bp;
+    }
+    // halves: the lower half sums candidates 0 and 1 over both halves, the upper 2 and 3;
+    // then rows: even rows keep the even candidate of their half, odd rows the odd one
+    LanePair t = swap32(P[0], P[2]);
+    const float A0 = t.r0 + t.r1;
+    t = swap32(P[1], P[3]);
+    const float A1 = t.r0 + t.r1;
+    t = swap32(B[0], B[2]);
+    const float C0 = t.r0 + t.r1;
+    t = swap32(B[1], B[3]);
+    const float C1 = t.r0 + t.r1;
+    t = swap16(A0, A1);
+    const float o = t.r0 + t.r1;
+    t = swap16(C0, C1);
+    const float bb = t.r0 + t.r1;
+    const int cq = q == 0 ? cs[0] : (q == 1 ? cs[1] : (q == 2 ? cs[2] : cs[3]));
+    const bool aq = q == 0 ? acts[0] : (q == 1 ? acts[1] : (q == 2 ? acts[2] : acts[3]));
+    const float er = 1e-5f * bb * bb + 0x1p-110f;
+    if (aq) screen_add(z, o - er, o + er, cq);
+  };
+  for (int j = 0;; j += 4) {
+    int cs[4];
+    bool acts[4];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c_lo + j + k;
+      acts[k] = screen && c <= c_hi;
+      cs[k] = acts[k] ? c : 1;
+      any = any || acts[k];
+    }
+    if (!__any(any)) break;
+    step4(cs, acts);
+  }
+  // downward: the bound uses the pair's theta so far (merged over its four lanes)
+  bool down = screen;
+  for (int c0 = c_lo - 1;; c0 -= 4) {
+    LanePair t = swap16(z.theta, z.theta);
+    float th = fminf(t.r0, t.r1);
+    t = swap32(th, th);
+    th = fminf(t.r0, t.r1);
+    int cs[4];
+    bool acts[4];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 - k;
+      bool a = down && c >= 1;
+      if (a && prune) {
+        const double e7 = (double)((6.0f * cand[c].s) * S - amax);
+        if (gm * e7 * e7 > (double)th * margin) a = false;
+      }
+      down = a;  // the bound is monotone: once pruned, every smaller byte is too
+      acts[k] = a;
+      cs[k] = a ? c : 1;
+      any = any || a;
+    }
+    if (!__any(any)) break;
+    step4(cs, acts);
+  }
+  screen_merge<16>(z);
+  screen_merge<32>(z);
+  const float theta = z.theta, L2 = z.L2, L3 = z.L3;
+  const int c1 = z.c1, c2 = z.c2;
+
+  // ---- exact decision
+  const bool overflow = screen && L3 <= theta;
+  const bool slow = live && (!fast_ok || overflow);
   int best_c = 0;
   double best_o = 0.0;
-  if (amax != 0.0f) {
-    if (!h_nonzero) {
-      float bm;
-      mse_pruned(X, amax, cand, S, best_c, bm);
-    } else {
-      int cz, cb;
-      window_bounds(amax, cand, S, cz, cb);
-      const int c_hi = cz <= 126 ? cz : 126;
-      const int c_lo = cb >= 1 ? cb : 1;
-      const bool fast_ok = fast_path_ok(amax, cand);
-      double gm = gw[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) gm = (m == i) ? gw[i] : gm;
-      best_o = INFINITY;
-      for (int c = c_lo; c <= c_hi; ++c) {
-        const double o = lh_candidate(v, c, cand[c], S, fast_ok, hb);
-        if (o < best_o) {
-          best_o = o;
-          best_c = c;
-        }
-      }
-      for (int c = c_lo - 1; c >= 1; --c) {
-        if (prune) {
-          const double e7 = (double)((6.0f * cand[c].s) * S - amax);
-          if (gm * e7 * e7 > best_o * margin) break;
-        }
-        const double o = lh_candidate(v, c, cand[c], S, fast_ok, hb);
-        if (o <= best_o) {  // ties: the smaller byte wins
-          best_o = o;
-          best_c = c;
-        }
+  // (all cross-lane steps below run with the whole wave active; the four lanes of a pair
+  // always agree on every per-pair flag)
+  const bool sel = screen && !overflow;
+  const bool two = sel && L2 <= theta;
+  const bool need = sel && (two || obj != nullptr);
+  if (sel) best_c = c1;
+  if (__any(need)) {
+    float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (need) lh_delta4(v, c1, cand[c1], S, true, d);
+    const double oa = lh_exact_split(d, q, hb);
+    if (need) best_o = oa;
+    if (__any(two)) {
+      float d2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (two) lh_delta4(v, c2, cand[c2], S, true, d2);
+      const double ob = lh_exact_split(d2, q, hb);
+      if (two && (ob < best_o || (ob == best_o && c2 < c1))) {
+        best_o = ob;
+        best_c = c2;
       }
     }
   }
-  scales[blk] = (uint8_t)best_c;
-  if (obj) obj[blk] = best_o;
+  if (__any(slow)) {  // exact scan of every candidate that can win
+    double bo = INFINITY;
+    int bcx = 0;
+    for (int j = 0;; ++j) {
+      const int c = c_lo + j;
+      const bool act = slow && c <= c_hi;
+      if (!__any(act)) break;
+      float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (act) lh_delta4(v, c, cand[c], S, fast_ok, d);
+      const double o = lh_exact_split(d, q, hb);
+      if (act && o < bo) {
+        bo = o;
+        bcx = c;
+      }
+    }
+    bool dn = slow;
+    for (int c = c_lo - 1;; --c) {
+      bool act = dn && c >= 1;
+      if (act && prune) {
+        const double e7 = (double)((6.0f * cand[c].s) * S - amax);
+        if (gm * e7 * e7 > bo * margin) act = false;
+      }
+      dn = act;
+      if (!__any(act)) break;
+      float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (act) lh_delta4(v, c, cand[c], S, fast_ok, d);
+      const double o = lh_exact_split(d, q, hb);
+      if (act && o <= bo) {
+        bo = o;
+        bcx = c;
+      }
+    }
+    if (slow) {
+      best_c = bcx;
+      best_o = bo;
+    }
+  }
+  if (valid && q == 0) {
+    scales[blk] = (uint8_t)best_c;
+    if (obj) obj[blk] = best_c ? best_o : 0.0;
+  }
 }
 
 int launch_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
                          const float *S, const float *H, uint8_t *scales, double *obj,
                          hipStream_t st) {
   const int64_t nb = cols / 16;
-  const dim3 g((unsigned)((rows + 255) / 256), (unsigned)nb, (unsigned)batch), b(256);
+  const dim3 g((unsigned)((rows + 63) / 64), (unsigned)nb, (unsigned)batch), b(256);
   if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_lh<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
+    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
   else
-    hipLaunchKernelGGL(k_lh<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
+    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
