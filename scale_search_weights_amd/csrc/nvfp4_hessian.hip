@@ -3,11 +3,13 @@
 // diagonal blocks are kept) and the per-expert token lists that feed the grouped form.
 //
 // H is bandwidth-bound (16 flop per byte of bf16 X against a bf16-MFMA ridge near 300), so
-// the kernel is organised to stream X once at full width:
-//  * a workgroup owns 64 channels (four 16-channel blocks, one per wave) and a chunk of
-//    tokens; each step stages a [32 tokens x 64 channels] tile in LDS with one coalesced
-//    16-byte load per lane (a 128-byte row segment per 8 lanes);
-//  * each wave reads its block's 16 channels x 32 tokens out of LDS as the MFMA operand
+// the bf16 kernel is organised to stream X once at full width:
+//  * a workgroup owns 64 W channels (W 16-channel blocks per wave; W = 4 for a dense X, so
+//    every token row is read in 512-byte pieces, 1 for the gathered rows of the grouped
+//    form) and a chunk of tokens; each step stages a [32 tokens x 64 W channels] tile in
+//    LDS with W coalesced 16-byte loads per lane, and the next step's loads (for the
+//    grouped form also its row ids) are issued before this step's MFMAs;
+//  * each wave reads a block's 16 channels x 32 tokens out of LDS as the MFMA operand
 //    (lane = channel, eight tokens per lane; the row pitch is padded so the four lane
 //    groups hit disjoint banks) and issues one v_mfma_f32_16x16x32_bf16 with the same
 //    register as both A and B: A = X_b^T and B = X_b hold identical fragments, so any
@@ -28,14 +30,22 @@ constexpr int HC = 64;        // channels per workgroup
 constexpr int PITCH16 = 66;   // bf16 LDS row pitch in elements (132 B)
 constexpr int PITCH32 = 68;   // fp32 LDS row pitch in elements (272 B)
 
-static inline int64_t hess_chunk(int64_t n) { return n >= 65536 ? 2048 : 512; }
+constexpr int HW_DENSE = 4;      // bf16 dense: blocks per wave (512-byte row segments)
+constexpr int HW_GROUPED = 1;    // bf16 grouped: blocks per wave
+constexpr int64_t TC_DENSE = 4096;  // tokens per workgroup (dense, large n)
+
+// tokens (dense) or list positions (grouped) per workgroup
+static inline int64_t hess_chunk(int64_t n, bool grouped) {
+  if (n < 65536) return 512;
+  return grouped ? 2048 : TC_DENSE;
+}
 
 static inline int64_t hess_items_max(int64_t tokens, int64_t groups, int64_t n_ids, bool grouped) {
   if (!grouped) {
-    const int64_t tc = hess_chunk(tokens);
+    const int64_t tc = hess_chunk(tokens, false);
     return (tokens + tc - 1) / tc;
   }
-  const int64_t tc = hess_chunk(n_ids);
+  const int64_t tc = hess_chunk(n_ids, true);
   return n_ids / tc + groups;
 }
 
@@ -112,54 +122,88 @@ __device__ __forceinline__ bool hess_range(int64_t it, int64_t tokens, int64_t g
   return p0 < p1;
 }
 
-template <bool GROUPED>
+template <bool GROUPED, int W>
 __global__ void __launch_bounds__(256)
     k_hess_bf16(const uint16_t *__restrict__ x, int64_t tokens, int64_t cols, int64_t groups,
                 const int32_t *__restrict__ offsets, const int32_t *__restrict__ ids, int64_t n_ids,
                 const int32_t *__restrict__ item_off, int64_t tc, float *__restrict__ partial,
                 int64_t nb) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[HT * PITCH16];
+  constexpr int C = HC * W;          // channels per workgroup: W blocks per wave
+  constexpr int PITCH = C + 2;       // u16; the 8-row stride of the MFMA reads shifts banks by 8
+  constexpr int SEGS = C / 8;        // 16-byte segments per token row
+  constexpr int ROWS = 256 / SEGS;   // token rows per load instruction
+  constexpr int NLD = HT / ROWS;     // 16-byte loads per lane per step (= W)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[HT * PITCH];
   const int64_t it = blockIdx.y;
   int64_t p0, p1;
   if (!hess_range<GROUPED>(it, tokens, groups, offsets, n_ids, item_off, tc, p0, p1)) return;
-  const int64_t ch0 = (int64_t)blockIdx.x * HC;
-  const int r = threadIdx.x >> 3, q = threadIdx.x & 7;
+  const int64_t ch0 = (int64_t)blockIdx.x * C;
+  const int r = threadIdx.x / SEGS, q = threadIdx.x % SEGS;
   const int64_t ch = ch0 + q * 8;
+  const bool ch_ok = ch < cols;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int fch = wave * 16 + (lane & 15), fk = (lane >> 4) * 8;
+  const int fk = (lane >> 4) * 8;
 
-  auto load = [&](int64_t pos) -> uint4 {
-    const int64_t pp = pos + r;
-    if (pp < p1 && ch < cols) {
-      const int64_t tok = GROUPED ? (int64_t)ids[pp] : pp;
-      if (tok >= 0 && tok < tokens) return *reinterpret_cast<const uint4 *>(x + tok * cols + ch);
-    }
-    return make_uint4(0u, 0u, 0u, 0u);
+  auto token_at = [&](int64_t pp) -> int64_t {
+    if (pp >= p1) return -1;
+    const int64_t tok = GROUPED ? (int64_t)ids[pp] : pp;
+    return (tok >= 0 && tok < tokens) ? tok : -1;
+  };
+  auto tokens_of = [&](int64_t pos, int64_t tok[NLD]) {
+#pragma unroll
+    for (int s = 0; s < NLD; ++s) tok[s] = token_at(pos + r + ROWS * s);
+  };
+  auto load = [&](const int64_t tok[NLD], uint4 out[NLD]) {
+#pragma unroll
+    for (int s = 0; s < NLD; ++s)
+      out[s] = (tok[s] >= 0 && ch_ok) ? *reinterpret_cast<const uint4 *>(x + tok[s] * cols + ch)
+                                      : make_uint4(0u, 0u, 0u, 0u);
   };
 
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 cur = load(p0);
-  for (int64_t pos = p0; pos < p1; pos += HT) {
-    unsigned *dst = reinterpret_cast<unsigned *>(tile + r * PITCH16 + q * 8);
-    dst[0] = cur.x;
-    dst[1] = cur.y;
-    dst[2] = cur.z;
-    dst[3] = cur.w;
-    __syncthreads();
-    if (pos + HT < p1) cur = load(pos + HT);
-    v8u16 f;
+  // software pipeline: this step's rows are in cur, the next step's token rows are known,
+  // and the next step's loads are issued before this step's MFMAs
+  v4f acc[W];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = tile[(fk + j) * PITCH16 + fch];
-    const v8bf a = __builtin_bit_cast(v8bf, f);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc, 0, 0, 0);
+  for (int w = 0; w < W; ++w) acc[w] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t tk[NLD];
+  uint4 cur[NLD];
+  tokens_of(p0, tk);
+  load(tk, cur);
+  tokens_of(p0 + HT, tk);
+  for (int64_t pos = p0; pos < p1; pos += HT) {
+#pragma unroll
+    for (int s = 0; s < NLD; ++s) {
+      unsigned *dst = reinterpret_cast<unsigned *>(tile + (r + ROWS * s) * PITCH + q * 8);
+      dst[0] = cur[s].x;
+      dst[1] = cur[s].y;
+      dst[2] = cur[s].z;
+      dst[3] = cur[s].w;
+    }
+    __syncthreads();
+    if (pos + HT < p1) {
+      load(tk, cur);
+      tokens_of(pos + 2 * HT, tk);
+    }
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const int fch = (wave * W + w) * 16 + (lane & 15);
+      v8u16 f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = tile[(fk + j) * PITCH + fch];
+      const v8bf a = __builtin_bit_cast(v8bf, f);
+      acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, acc[w], 0, 0, 0);
+    }
     __syncthreads();
   }
-  const int64_t b = ch0 / 16 + wave;
-  if (b < nb) {
-    float *P = partial + (it * nb + b) * 256;
-    const int col = lane & 15, row0 = (lane >> 4) * 4;
+  const int col = lane & 15, row0 = (lane >> 4) * 4;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) P[(row0 + rr) * 16 + col] = acc[rr];
+  for (int w = 0; w < W; ++w) {
+    const int64_t b = ch0 / 16 + wave * W + w;
+    if (b < nb) {
+      float *P = partial + (it * nb + b) * 256;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) P[(row0 + rr) * 16 + col] = acc[w][rr];
+    }
   }
 }
 
@@ -224,8 +268,19 @@ __global__ void __launch_bounds__(256)
   const int64_t b = blockIdx.x, g = blockIdx.y, e = threadIdx.x;
   const int64_t i0 = item_off ? item_off[g] : 0;
   const int64_t i1 = item_off ? item_off[g + 1] : n_items_dense;
+  // loads in batches of eight (independent, in flight together); the sum stays ascending
+  const float *src = partial + b * 256 + e;
+  const int64_t stride = nb * 256;
   float s = 0.0f;
-  for (int64_t it = i0; it < i1; ++it) s += partial[(it * nb + b) * 256 + e];
+  int64_t it = i0;
+  for (; it + 8 <= i1; it += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[(it + k) * stride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+  for (; it < i1; ++it) s += src[it * stride];
   float *out = H + (g * nb + b) * 256 + e;
   *out = accumulate ? *out + s : s;
 }
@@ -236,7 +291,7 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
   const bool grouped = group_offsets != nullptr;
   const int64_t nb = cols / 16;
   const int64_t items = hess_items_max(tokens, groups, grouped ? n_ids : -1, grouped);
-  const int64_t tc = hess_chunk(grouped ? n_ids : tokens);
+  const int64_t tc = hess_chunk(grouped ? n_ids : tokens, grouped);
   int32_t *item_off = nullptr;
   char *ws = static_cast<char *>(workspace);
   if (grouped) item_off = reinterpret_cast<int32_t *>(ws);
@@ -246,13 +301,15 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
                        items, item_off);
   if (items > 0) {
     const dim3 g((unsigned)((cols + HC - 1) / HC), (unsigned)items), b(256);
+    const int64_t cw = HC * (grouped ? HW_GROUPED : HW_DENSE);
+    const dim3 gb((unsigned)((cols + cw - 1) / cw), (unsigned)items);
     if (dtype == NVFP4_DTYPE_BF16) {
       const uint16_t *xb = static_cast<const uint16_t *>(x);
       if (grouped)
-        hipLaunchKernelGGL(k_hess_bf16<true>, g, b, 0, st, xb, tokens, cols, groups,
+        hipLaunchKernelGGL((k_hess_bf16<true, HW_GROUPED>), gb, b, 0, st, xb, tokens, cols, groups,
                            group_offsets, token_ids, n_ids, item_off, tc, partial, nb);
       else
-        hipLaunchKernelGGL(k_hess_bf16<false>, g, b, 0, st, xb, tokens, cols, groups, nullptr,
+        hipLaunchKernelGGL((k_hess_bf16<false, HW_DENSE>), gb, b, 0, st, xb, tokens, cols, groups, nullptr,
                            nullptr, n_ids, nullptr, tc, partial, nb);
     } else {
       const float *xf = static_cast<const float *>(x);
