@@ -25,6 +25,8 @@ FLAGS = [
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     # no packed fp32 ops in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (no accumulator-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

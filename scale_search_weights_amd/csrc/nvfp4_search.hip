@@ -358,7 +358,7 @@ template <int DT>
 __global__ void __launch_bounds__(256)
     k_lh_mfma(const void *__restrict__ w, const float *__restrict__ S_arr,
               const float *__restrict__ H, uint8_t *__restrict__ scales, double *__restrict__ obj,
-              int64_t rows, int64_t nb) {
+              int64_t rows, int64_t nb, int64_t tiles_per_wg) {
   __shared__ Cand cand[127];
   __shared__ double hb[256];
   __shared__ double gw[16];
@@ -389,11 +389,19 @@ __global__ void __launch_bounds__(256)
   for (int i = 0; i < 16; ++i) kappa = fmax(kappa, kap[i]);
   const bool prune = kappa < 1e9;
   const double margin = 1.0 + 8e-15 * kappa + 1e-13;
+  // screening error relative to the objective itself when H_b is well conditioned:
+  // sum_ij |d_i||H_ij||d_j| <= kappa sum_i g_i d_i^2 <= kappa d H d^T
+  const bool rel = prune && kappa <= 1e4;
+  const float rho = (float)(1.2e-5 * kappa);
+  // this workgroup's tiles of 64 rows
+  const int64_t n_tiles = (rows + 63) / 64;
+  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_wg;
+  const int64_t tile1 = min(tile0 + tiles_per_wg, n_tiles);
 
   if (!h_nonzero) {  // every candidate has objective 0: the MSE choice, one lane per row
-    if (threadIdx.x < 64) {
-      const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
-      if (row < rows) {
+    const int64_t row_end = min(tile1 * 64, rows);
+    for (int64_t row = tile0 * 64 + threadIdx.x; row < row_end; row += blockDim.x) {
+      {
         const int64_t blk = (batch * rows + row) * nb + b;
         float v[16], X[16];
         load16<DT>(w, blk, v);
@@ -414,15 +422,17 @@ __global__ void __launch_bounds__(256)
   }
 
   const int lane = threadIdx.x & 63, p = lane & 15, q = lane >> 4;
-  const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + p;
-  const bool valid = row < rows;
-  const int64_t blk = (batch * rows + (valid ? row : 0)) * nb + b;
-  float ha[4], ab[4], v[4];
+  float ha[4], ab[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     ha[t] = (float)hb[p * 16 + 4 * q + t];
     ab[t] = aw[4 * q + t];
   }
+  for (int64_t tile = tile0; tile < tile1; ++tile) {
+  const int64_t row = tile * 64 + (threadIdx.x >> 6) * 16 + p;
+  const bool valid = row < rows;
+  const int64_t blk = (batch * rows + (valid ? row : 0)) * nb + b;
+  float v[4];
   if (DT == NVFP4_DTYPE_BF16) {
     uint2 u = make_uint2(0u, 0u);
     if (valid) u = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(w) + blk * 16)[q];
@@ -466,14 +476,16 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[t], d[t], acc, 0, 0, 0);
       float op = d[0] * acc[0];
-      float bp = fabsf(d[0]) * ab[0];
 #pragma unroll
-      for (int r = 1; r < 4; ++r) {
-        op = __builtin_fmaf(d[r], acc[r], op);
-        bp = __builtin_fmaf(fabsf(d[r]), ab[r], bp);
-      }
+      for (int r = 1; r < 4; ++r) op = __builtin_fmaf(d[r], acc[r], op);
       P[k] = op;
-      B[k] = bp;
+      B[k] = 0.0f;
+      if (!rel) {
+        float bp = fabsf(d[0]) * ab[0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r) bp = __builtin_fmaf(fabsf(d[r]), ab[r], bp);
+        B[k] = bp;
+      }
     }
     // halves: the lower half sums candidates 0 and 1 over both halves, the upper 2 and 3;
     // then rows: even rows keep the even candidate of their half, odd rows the odd one
@@ -481,17 +493,22 @@ __global__ void __launch_bounds__(256)
     const float A0 = t.r0 + t.r1;
     t = swap32(P[1], P[3]);
     const float A1 = t.r0 + t.r1;
-    t = swap32(B[0], B[2]);
-    const float C0 = t.r0 + t.r1;
-    t = swap32(B[1], B[3]);
-    const float C1 = t.r0 + t.r1;
     t = swap16(A0, A1);
     const float o = t.r0 + t.r1;
-    t = swap16(C0, C1);
-    const float bb = t.r0 + t.r1;
+    float er;
+    if (rel) {
+      er = rho * fabsf(o) + 0x1p-109f;
+    } else {
+      t = swap32(B[0], B[2]);
+      const float C0 = t.r0 + t.r1;
+      t = swap32(B[1], B[3]);
+      const float C1 = t.r0 + t.r1;
+      t = swap16(C0, C1);
+      const float bb = t.r0 + t.r1;
+      er = 1e-5f * bb * bb + 0x1p-110f;
+    }
     const int cq = q == 0 ? cs[0] : (q == 1 ? cs[1] : (q == 2 ? cs[2] : cs[3]));
     const bool aq = q == 0 ? acts[0] : (q == 1 ? acts[1] : (q == 2 ? acts[2] : acts[3]));
-    const float er = 1e-5f * bb * bb + 0x1p-110f;
     if (aq) screen_add(z, o - er, o + er, cq);
   };
   for (int j = 0;; j += 4) {
@@ -606,17 +623,28 @@ __global__ void __launch_bounds__(256)
     scales[blk] = (uint8_t)best_c;
     if (obj) obj[blk] = best_c ? best_o : 0.0;
   }
+  }  // tiles
 }
+
+constexpr int64_t LH_TILES = 8;
 
 int launch_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
                          const float *S, const float *H, uint8_t *scales, double *obj,
                          hipStream_t st) {
   const int64_t nb = cols / 16;
-  const dim3 g((unsigned)((rows + 63) / 64), (unsigned)nb, (unsigned)batch), b(256);
+  // up to LH_TILES tiles of 64 rows per workgroup (the H_b analysis and candidate table are
+  // shared by them), fewer when that would leave the grid under ~8192 workgroups
+  const int64_t n_tiles = (rows + 63) / 64;
+  const int64_t cols_batch = nb * batch;
+  int64_t tpw = LH_TILES;
+  while (tpw > 1 && cols_batch * ((n_tiles + tpw - 1) / tpw) < 8192) tpw >>= 1;
+  const dim3 g((unsigned)((n_tiles + tpw - 1) / tpw), (unsigned)nb, (unsigned)batch), b(256);
   if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
+    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, H, scales, obj, rows, nb,
+                       tpw);
   else
-    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, H, scales, obj, rows, nb);
+    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, H, scales, obj, rows, nb,
+                       tpw);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
