@@ -207,15 +207,17 @@ int launch_mse(const void *w, int dtype, int64_t batch, int64_t rows, int64_t co
 // K slot of lane group q is element 4q + t, so A = H[p][4q+t] and B = d_p[4q+t] are the
 // lane's own values, and the 16x16 result leaves Y_p[4q..4q+3] in the lane that holds
 // d_p[4q..4q+3]. A four-term dot and two cross-lane adds give the fp32 objective.
-// Screening: |fp32 obj - exact obj| <= 1e-5 (sum_i |d_i| a_i)^2 + 2^-110 with
-// a_i^2 >= max_j max(|H_ij|, |H_ji|) (so sum_ij |d_i||H_ij||d_j| <= (sum |d_i| a_i)^2; the
-// constant is ~8x the worst-case fp32 rounding of the 16-term products, the four-term dot
-// and the two adds; the absolute term covers flushed denormals). Per pair the kernel keeps
-// theta = min(obj + err) and the two smallest (obj - err): every candidate that can still be
-// the exact argmin has obj - err <= theta. If at most two do, they are re-evaluated in the
-// exact fp64 order (split over the pair's four lanes) and the smaller wins; if three or
-// more do, or values are too small or large for the fast path, the pair is rescanned
-// exactly. The downward pruning compares with theta.
+// Screening: |fp32 obj - exact obj| <= 1e-5 A + t, A = sum_ij |d_i||H_ij||d_j|. The constant
+// is ~8x the worst-case fp32 rounding of the 16-term products, the four-term dot and the two
+// adds; t = 2^-138 (1 + amax) covers roundings in the denormal range (the fp32 MFMA keeps
+// denormals). A <= (sum |d_i| a_i)^2 with a_i^2 >= max_j max(|H_ij|, |H_ji|); when every
+// g_i > 0 (below), also A <= kappa d H d^T, so for kappa <= 1e4 the bound is relative to the
+// objective. Per pair the kernel keeps theta = min(obj + err) and the three smallest
+// (obj - err): every candidate that can still be the exact argmin has obj - err <= theta.
+// If at most two do, they are re-evaluated in the exact fp64 order (split over the pair's
+// four lanes) and the smaller wins; if three or more do, or values are too small or large
+// for the fast path or for fp32, the pair is rescanned exactly. The downward pruning
+// compares with theta.
 
 // the four fp32 weight errors of this lane's elements under candidate c
 __device__ __forceinline__ void lh_delta4(const float v[4], int c, const Cand &e, float S,
@@ -392,6 +394,9 @@ __global__ void __launch_bounds__(256)
   // screening error relative to the objective itself when H_b is well conditioned:
   // sum_ij |d_i||H_ij||d_j| <= kappa sum_i g_i d_i^2 <= kappa d H d^T
   const bool rel = prune && kappa <= 1e4;
+  float hmax = 0.0f;  // max |H_ij| (up to the 2^-20 margin of a_i)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) hmax = fmaxf(hmax, aw[i] * aw[i]);
   const float rho = (float)(1.2e-5 * kappa);
   // this workgroup's tiles of 64 rows
   const int64_t n_tiles = (rows + 63) / 64;
@@ -463,7 +468,13 @@ __global__ void __launch_bounds__(256)
 
   // ---- screen on MFMA, four candidates per step (independent MFMA chains); after the
   // transposing reduction lane group q holds the objective of the step's candidate q
-  bool screen = live && fast_ok;
+  // Absolute part of the screening error: the fp32 MFMA keeps denormals (gradual underflow),
+  // so each rounding below 2^-126 errs by at most 2^-150, scaled by |d_i| <= 4.5 amax.
+  const float tiny = 0x1p-138f * (1.0f + amax);
+  // fp32 stays finite: sum_ij |d_i||H_ij||d_j| <= hmax (sum_i |d_i|)^2 <= hmax (72 amax)^2
+  const float da = 72.0f * amax;
+  const bool screen_ok = fast_ok && hmax * da * da < 0x1p100f;
+  bool screen = live && screen_ok;
   Screen z = {INFINITY, INFINITY, INFINITY, INFINITY, 0, 0};
   auto step4 = [&](const int cs[4], const bool acts[4]) {
     typedef float v4f __attribute__((ext_vector_type(4)));
@@ -497,7 +508,7 @@ __global__ void __launch_bounds__(256)
     const float o = t.r0 + t.r1;
     float er;
     if (rel) {
-      er = rho * fabsf(o) + 0x1p-109f;
+      er = rho * fabsf(o) + 2.0f * tiny;
     } else {
       t = swap32(B[0], B[2]);
       const float C0 = t.r0 + t.r1;
@@ -505,7 +516,7 @@ __global__ void __launch_bounds__(256)
       const float C1 = t.r0 + t.r1;
       t = swap16(C0, C1);
       const float bb = t.r0 + t.r1;
-      er = 1e-5f * bb * bb + 0x1p-110f;
+      er = 1e-5f * bb * bb + tiny;
     }
     const int cq = q == 0 ? cs[0] : (q == 1 ? cs[1] : (q == 2 ? cs[2] : cs[3]));
     const bool aq = q == 0 ? acts[0] : (q == 1 ? acts[1] : (q == 2 ? acts[2] : acts[3]));
@@ -558,7 +569,7 @@ __global__ void __launch_bounds__(256)
 
   // ---- exact decision
   const bool overflow = screen && L3 <= theta;
-  const bool slow = live && (!fast_ok || overflow);
+  const bool slow = live && (!screen_ok || overflow);
   int best_c = 0;
   double best_o = 0.0;
   // (all cross-lane steps below run with the whole wave active; the four lanes of a pair

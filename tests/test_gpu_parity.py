@@ -392,6 +392,33 @@ def test_local_hessian_special_hessians(orc):
     _lh_check(orc, w, S, H1)
 
 
+def _dominant_h(delta: float) -> torch.Tensor:
+    """(16 + delta) I - 11^T: PSD, g_i = delta, kappa ~ 30 / delta."""
+    return (16.0 + delta) * torch.eye(16) - torch.ones(16, 16)
+
+
+def test_local_hessian_magnitude_regimes(orc):
+    w0, x = synth.projection(11, rows=64, cols=256, tokens=2048)
+    H0 = nvfp4.block_hessian(x.to(DEV))
+    nb = H0.shape[0]
+    regimes = [
+        ("large weights (x1e4)", 1e4, H0),
+        ("tiny weights (x1e-15)", 1e-15, H0),
+        ("H in the fp32 denormal range (x1e-44)", 1.0, H0 * 1e-44),
+        ("huge H (x1e30): fp32 screen would overflow", 1.0, H0 * 1e30),
+        ("large weights and large H (x1e3, x1e20)", 1e3, H0 * 1e20),
+        ("diagonally dominant H, kappa ~3e4 (absolute screen bound)", 1.0,
+         _dominant_h(1e-3).to(DEV).expand(nb, 16, 16).contiguous()),
+        ("nearly singular H, kappa ~3e9 (no pruning)", 1.0,
+         _dominant_h(1e-8).to(DEV).expand(nb, 16, 16).contiguous()),
+    ]
+    for name, ws, H in regimes:
+        case(f"local hessian, {name}")
+        w = (w0.float() * ws).to(torch.bfloat16)
+        S = orc.tensor_scale(f32(w))
+        _lh_check(orc, w, S, H)
+
+
 def test_local_hessian_batched_experts(orc):
     case("local hessian batch of 4 experts with per-expert S and H")
     w, x, ids = synth.moe(9, experts=4, rows=40, cols=128, tokens=600, topk=2)
