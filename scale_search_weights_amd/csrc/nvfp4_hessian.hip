@@ -328,118 +328,152 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
 
 // ------------------------------------------------------------------ routing groups
 //
-// A stable counting sort of (token, expert) pairs by expert. Tokens are cut into chunks;
-// per chunk, an LDS bitmap per expert marks the chunk's tokens routed there, so a pair's
-// rank among the expert's tokens in the chunk is a popcount of the bits below it.
+// A stable counting sort of the (token, slot) pairs of the routing table by expert: pair
+// i = t * topk + k keeps its flattened order within its expert, so each expert lists its
+// tokens in ascending order (a token routed twice to one expert appears twice). Pairs are
+// cut into chunks of 32 W; per chunk, an LDS bitmap per expert marks the chunk's pairs routed
+// there, and a pair's rank among them is a popcount of the bits below it.
+//  1. k_route_count: per (chunk, expert) counts, from LDS counters;
+//  2. k_route_scan: one workgroup turns them into per-expert offsets and per-(chunk,
+//     expert) bases (experts in blocks of up to 1024, chunks split into segments);
+//  3. k_route_scatter: every pair writes its token at base + rank.
 
 static inline int route_words(int64_t experts) {
   int64_t w = 16384 / (experts > 0 ? experts : 1);
-  return (int)(w > 32 ? 32 : (w < 1 ? 1 : w));
+  return (int)(w > 64 ? 64 : (w < 1 ? 1 : w));
+}
+
+static inline int64_t route_chunks(int64_t pairs, int64_t experts) {
+  const int64_t cp = 32 * (int64_t)route_words(experts);
+  return (pairs + cp - 1) / cp;
 }
 
 size_t route_workspace_size(int64_t tokens, int64_t topk, int64_t experts) {
-  (void)topk;
-  const int64_t ct = 32 * (int64_t)route_words(experts);
-  const int64_t chunks = (tokens + ct - 1) / ct;
+  const int64_t chunks = route_chunks(tokens * topk, experts);
   return sizeof(int32_t) * (size_t)(chunks > 0 ? chunks : 1) * (size_t)(experts > 0 ? experts : 1);
 }
 
-__device__ __forceinline__ void route_bitmap(const int32_t *__restrict__ ids, int64_t tokens,
-                                             int topk, int E, int W, unsigned *bm, int64_t t0) {
-  for (int i = threadIdx.x; i < E * W; i += blockDim.x) bm[i] = 0u;
-  __syncthreads();
-  const int64_t nt = min((int64_t)32 * W, tokens - t0);
-  for (int64_t i = threadIdx.x; i < nt * topk; i += blockDim.x) {
-    const int e = ids[t0 * topk + i];
-    if (e >= 0 && e < E) {
-      const int rel = (int)(i / topk);
-      atomicOr(&bm[e * W + (rel >> 5)], 1u << (rel & 31));
-    }
-  }
-  __syncthreads();
-}
-
 __global__ void __launch_bounds__(256)
-    k_route_count(const int32_t *__restrict__ ids, int64_t tokens, int topk, int E, int W,
+    k_route_count(const int32_t *__restrict__ ids, int64_t pairs, int E, int64_t cp,
                   int32_t *__restrict__ counts) {
-  extern __shared__ unsigned bm[];
-  const int64_t chunk = blockIdx.x;
-  route_bitmap(ids, tokens, topk, E, W, bm, chunk * 32 * W);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int w = 0; w < W; ++w) c += __popc(bm[e * W + w]);
-    counts[chunk * E + e] = c;
+  extern __shared__ unsigned cnt[];
+  const int64_t chunk = blockIdx.x, i0 = chunk * cp;
+  const int64_t n = min(cp, pairs - i0);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0u;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = ids[i0 + i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1u);
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) counts[chunk * E + e] = (int32_t)cnt[e];
 }
 
-// One workgroup: per-expert totals, exclusive scan over experts, then per-(chunk, expert)
-// base offsets written over the counts.
+// One workgroup of 1024 threads. For a block of EB experts, thread (e, s) owns expert e and
+// segment s of the chunks; counts are replaced by the base of each (chunk, expert) in
+// token_ids and offsets[e] gets the start of expert e.
 __global__ void __launch_bounds__(1024)
     k_route_scan(int32_t *__restrict__ counts, int64_t chunks, int E, int32_t *__restrict__ offsets) {
   __shared__ int32_t part[1024];
+  __shared__ int32_t tot[1024];
   __shared__ int32_t carry;
-  if (threadIdx.x == 0) carry = 0;
+  const int t = threadIdx.x;
+  const int EB = E < 1024 ? E : 1024;
+  const int SEG = 1024 / EB;
+  const int64_t L = (chunks + SEG - 1) / SEG;
+  if (t == 0) carry = 0;
   __syncthreads();
-  for (int e0 = 0; e0 < E; e0 += 1024) {
-    const int e = e0 + threadIdx.x;
-    int32_t tot = 0;
-    if (e < E)
-      for (int64_t c = 0; c < chunks; ++c) tot += counts[c * E + e];
-    part[threadIdx.x] = tot;
+  for (int e0 = 0; e0 < E; e0 += EB) {
+    const int el = t % EB, sg = t / EB, e = e0 + el;
+    const bool on = sg < SEG && e < E;
+    const int64_t c0 = sg * L, c1 = min(chunks, c0 + L);
+    int32_t sum = 0;
+    if (on) {
+      int64_t c = c0;
+      for (; c + 8 <= c1; c += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = counts[(c + k) * E + e];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum += v[k];
+      }
+      for (; c < c1; ++c) sum += counts[c * E + e];
+    }
+    part[t] = sum;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-      const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    // per-expert totals and the exclusive prefix of this thread's segment
+    int32_t pre = 0, all = 0;
+    if (on) {
+      for (int k = 0; k < SEG; ++k) {
+        const int32_t v = part[k * EB + el];
+        if (k < sg) pre += v;
+        all += v;
+      }
+    }
+    if (sg == 0) tot[el] = on ? all : 0;
+    __syncthreads();
+    // inclusive scan of the block's expert totals (Hillis-Steele over EB entries)
+    for (int off = 1; off < EB; off <<= 1) {
+      const int32_t v = (t < EB && t >= off) ? tot[t - off] : 0;
       __syncthreads();
-      part[threadIdx.x] += v;
+      if (t < EB) tot[t] += v;
       __syncthreads();
     }
-    const int32_t base = carry + part[threadIdx.x] - tot;
-    if (e < E) {
-      offsets[e] = base;
-      int32_t run = base;
-      for (int64_t c = 0; c < chunks; ++c) {
-        const int32_t n = counts[c * E + e];
+    if (on) {
+      const int32_t ebase = carry + (el > 0 ? tot[el - 1] : 0);
+      if (sg == 0) offsets[e] = ebase;
+      int32_t run = ebase + pre;
+      for (int64_t c = c0; c < c1; ++c) {
+        const int32_t v = counts[c * E + e];
         counts[c * E + e] = run;
-        run += n;
+        run += v;
       }
     }
     __syncthreads();
-    if (threadIdx.x == 1023) carry += part[1023];
+    if (t == 0) carry += tot[EB - 1];
     __syncthreads();
   }
-  if (threadIdx.x == 0) offsets[E] = carry;
+  if (t == 0) offsets[E] = carry;
 }
 
 __global__ void __launch_bounds__(256)
-    k_route_scatter(const int32_t *__restrict__ ids, int64_t tokens, int topk, int E, int W,
+    k_route_scatter(const int32_t *__restrict__ ids, int64_t pairs, int topk, int E, int W,
                     const int32_t *__restrict__ base, int32_t *__restrict__ token_ids) {
   extern __shared__ unsigned bm[];
-  const int64_t chunk = blockIdx.x, t0 = chunk * 32 * W;
-  route_bitmap(ids, tokens, topk, E, W, bm, t0);
-  const int64_t nt = min((int64_t)32 * W, tokens - t0);
-  for (int64_t i = threadIdx.x; i < nt * topk; i += blockDim.x) {
-    const int e = ids[t0 * topk + i];
+  const int64_t chunk = blockIdx.x, cp = 32 * (int64_t)W, i0 = chunk * cp;
+  const int n = (int)min(cp, pairs - i0);
+  for (int i = threadIdx.x; i < E * W; i += blockDim.x) bm[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = ids[i0 + i];
+    if (e >= 0 && e < E) atomicOr(&bm[e * W + (i >> 5)], 1u << (i & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = ids[i0 + i];
     if (e < 0 || e >= E) continue;
-    const int rel = (int)(i / topk), wd = rel >> 5, bit = rel & 31;
-    int rank = __popc(bm[e * W + wd] & ((1u << bit) - 1u));
-    for (int w = 0; w < wd; ++w) rank += __popc(bm[e * W + w]);
-    token_ids[base[chunk * E + e] + rank] = (int32_t)(t0 + rel);
+    const int wd = i >> 5;
+    const unsigned *row = bm + e * W;
+    int rank = __popc(row[wd] & ((1u << (i & 31)) - 1u));
+    for (int w = 0; w < wd; ++w) rank += __popc(row[w]);
+    token_ids[base[chunk * E + e] + rank] = (int32_t)((i0 + i) / topk);
   }
 }
 
 int launch_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk, int64_t experts,
                         int32_t *offsets, int32_t *token_ids, void *workspace, hipStream_t st) {
   const int E = (int)experts, W = route_words(experts);
-  const int64_t ct = 32 * (int64_t)W, chunks = (tokens + ct - 1) / ct;
+  const int64_t pairs = tokens * topk, cp = 32 * (int64_t)W;
+  const int64_t chunks = route_chunks(pairs, experts);
   int32_t *counts = static_cast<int32_t *>(workspace);
-  const size_t lds = sizeof(unsigned) * (size_t)E * (size_t)W;
   if (chunks > 0)
-    hipLaunchKernelGGL(k_route_count, dim3((unsigned)chunks), dim3(256), lds, st, expert_ids,
-                       tokens, (int)topk, E, W, counts);
+    hipLaunchKernelGGL(k_route_count, dim3((unsigned)chunks), dim3(256), sizeof(unsigned) * E, st,
+                       expert_ids, pairs, E, cp, counts);
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, counts, chunks, E, offsets);
   if (chunks > 0)
-    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)chunks), dim3(256), lds, st, expert_ids,
-                       tokens, (int)topk, E, W, counts, token_ids);
+    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)chunks), dim3(256),
+                       sizeof(unsigned) * (size_t)E * (size_t)W, st, expert_ids, pairs, (int)topk,
+                       E, W, counts, token_ids);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -335,6 +335,26 @@ def test_route_groups_and_grouped_hessian(orc):
         assert rel_frob(Hn[e], Href) <= 1e-4, e
 
 
+@pytest.mark.parametrize("tokens,topk,experts,lo,hi", [
+    (5000, 3, 7, -2, 9),        # repeats within a token and out-of-range ids
+    (4000, 8, 3000, 0, 3000),   # several expert blocks in the scan
+    (700, 2, 16384, -1, 16385), # the largest expert count
+    (1234, 5, 1, 0, 1),         # one expert: every pair, in order
+    (0, 4, 5, 0, 5),            # no tokens
+])
+def test_route_groups_repeats_and_invalid_ids(orc, tokens, topk, experts, lo, hi):
+    case(f"route groups tokens={tokens} topk={topk} experts={experts} ids in [{lo},{hi})")
+    rng = np.random.default_rng(tokens + experts)
+    ids = rng.integers(lo, hi, size=(tokens, topk)).astype(np.int32)
+    off, tok = nvfp4.route_groups(torch.from_numpy(ids).to(DEV), experts)
+    # expected: the stable sort of the valid pairs; invalid ids go to an extra last expert
+    dump = np.where((ids >= 0) & (ids < experts), ids, experts).astype(np.int32)
+    off_ref, tok_ref = orc.route_groups(dump, experts + 1)
+    n = int(off_ref[experts])
+    assert np.array_equal(off.cpu().numpy(), off_ref[:experts + 1])
+    assert np.array_equal(tok.cpu().numpy()[:n], tok_ref[:n])
+
+
 def test_grouped_hessian_with_empty_group(orc):
     case("grouped hessian with an empty expert")
     _, x, _ = synth.moe(6, experts=4, rows=16, cols=64, tokens=700, topk=2)
