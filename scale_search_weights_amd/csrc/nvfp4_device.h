@@ -136,6 +136,22 @@ __device__ __forceinline__ int max_scale_byte_fast(float amax, float qlo_mul, fl
   return b == 0 ? 1 : b;
 }
 
+// Per-tensor table of the 127 scale bytes: entry c >= 1 holds s = E4M3(c) and the bracket
+// lo < 1/(s S) < hi; entry 0 holds s = 0 and the bracket of 1/(6 S) used by the max byte.
+struct Cand {
+  float s, rlo, rhi, pad;
+};
+
+__device__ __forceinline__ void build_cands(Cand *cand, float S) {
+  for (int c = threadIdx.x; c < 127; c += blockDim.x) {
+    Cand e;
+    e.s = c ? e4m3_value(c) : 0.0f;
+    recip_bracket(c ? (double)e.s * (double)S : 6.0 * (double)S, e.rlo, e.rhi);
+    e.pad = 0.0f;
+    cand[c] = e;
+  }
+}
+
 // Midpoint between E2M1 grid indices j and j+1.
 __device__ __forceinline__ double e2m1_mid(int j) {
   double m = 0.25;

@@ -184,6 +184,41 @@ __device__ __forceinline__ void st_out(uint8_t *p, uint8_t v) { NVFP4_ST(p, v); 
 // bf16), the block max is exchanged between the lane pair, and each lane writes its own
 // 4 code bytes and 16 output bytes, so every wave load and store is contiguous and twice
 // as many waves are in flight as with one lane per block (measured faster on MI355X).
+// Eight consecutive elements as loaded: bf16 uses a (16 bytes), fp32 uses a and b.
+struct Raw8 {
+  uint4 a, b;
+};
+
+template <int DT>
+__device__ __forceinline__ Raw8 load_raw8(const void *__restrict__ x, int64_t hb) {
+  Raw8 r;
+  if (DT == NVFP4_DTYPE_BF16) {
+    r.a = reinterpret_cast<const uint4 *>(x)[hb];
+    r.b = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(x) + 2 * hb;
+    r.a = p[0];
+    r.b = p[1];
+  }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_raw8(const Raw8 &r, float v[8]) {
+  if (DT == NVFP4_DTYPE_BF16) {
+    const unsigned w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = bf16_lo(w[k]);
+      v[2 * k + 1] = bf16_hi(w[k]);
+    }
+  } else {
+    const unsigned w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(w[k]);
+  }
+}
+
 template <int DT, int OUT_DT, int FLAGS>
 __global__ void __launch_bounds__(256)
     k_quant(const void *__restrict__ x, const float *__restrict__ S_arr,
@@ -192,6 +227,12 @@ __global__ void __launch_bounds__(256)
              int64_t total_blocks) {
   const bool one_batch = blocks_per_batch == total_blocks;
   const float S0 = S_arr[0];  // uniform: a scalar load
+  // one tensor: the per-byte constants come from a table built once per workgroup
+  __shared__ Cand tab[127];
+  if (one_batch) {
+    build_cands(tab, S0);
+    __syncthreads();
+  }
   const int64_t total_half = 2 * total_blocks;
   for (int64_t hb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; hb < total_half;
        hb += (int64_t)gridDim.x * blockDim.x) {
@@ -199,38 +240,39 @@ __global__ void __launch_bounds__(256)
     const int h = (int)(hb & 1);
     const float S = one_batch ? S0 : S_arr[blk / blocks_per_batch];
     float v[8];
-    if (DT == NVFP4_DTYPE_BF16) {
-      const uint4 a = reinterpret_cast<const uint4 *>(x)[hb];
-      const unsigned w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = bf16_lo(w[k]);
-        v[2 * k + 1] = bf16_hi(w[k]);
-      }
-    } else {
-      const float4 *p = reinterpret_cast<const float4 *>(x) + 2 * hb;
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
+    unpack_raw8<DT>(load_raw8<DT>(x, hb), v);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    // the two lanes of a block are lanes 2k and 2k+1 (both active): DPP quad_perm [1,0,3,2]
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
+                                                                   0xF, 0xF, false)));
     int byte;
     if (FLAGS & F_SCALES_IN) {
       byte = scales_in[blk];
     } else {
       float qlo, qhi;
-      recip_bracket(6.0 * (double)S, qlo, qhi);
+      if (one_batch) {
+        qlo = tab[0].rlo;
+        qhi = tab[0].rhi;
+      } else {
+        recip_bracket(6.0 * (double)S, qlo, qhi);
+      }
       byte = max_scale_byte_fast(amax, qlo, qhi, S);
     }
     unsigned c = 0u;
     float s = 0.0f;
     if (byte) {
-      s = e4m3_value(byte);
       float rlo, rhi;
-      recip_bracket((double)s * (double)S, rlo, rhi);
+      if (one_batch) {
+        const Cand e = tab[byte];
+        s = e.s;
+        rlo = e.rlo;
+        rhi = e.rhi;
+      } else {
+        s = e4m3_value(byte);
+        recip_bracket((double)s * (double)S, rlo, rhi);
+      }
       const double sS = (double)s * (double)S;
       if (rlo >= 0x1p-126f && amax * rhi < 0x1p126f) {
         c = fp4_exact_codes8(v, rlo, rhi, sS);

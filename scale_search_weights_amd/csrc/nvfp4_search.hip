@@ -53,21 +53,6 @@ __device__ __forceinline__ void load16(const void *__restrict__ x, int64_t blk, 
 // Each lane owns one block and walks its own window [max(c_b,1), c_hi], then downwards;
 // per-candidate constants (s, the two bracketing reciprocals of s S) come from an LDS table.
 
-struct Cand {
-  float s, rlo, rhi, pad;
-};
-
-__device__ __forceinline__ void build_cands(Cand *cand, float S) {
-  for (int c = threadIdx.x; c < 127; c += blockDim.x) {
-    Cand e;
-    e.s = c ? e4m3_value(c) : 0.0f;
-    e.rlo = e.rhi = 0.0f;
-    if (c) recip_bracket((double)e.s * (double)S, e.rlo, e.rhi);
-    e.pad = 0.0f;
-    cand[c] = e;
-  }
-}
-
 // fp32 objective of candidate byte c for |x| (codes unsigned): sum of fma(e, e, acc) in order.
 // fast_ok: all products x * r stay in the normal fp32 range, so the bracketed hardware
 // conversions apply; otherwise the exact threshold table decides every code.
