@@ -351,7 +351,13 @@ __global__ void __launch_bounds__(256)
   __shared__ double gw[16];
   __shared__ double kap[16];
   __shared__ float aw[16];
-  const int64_t batch = blockIdx.z, b = blockIdx.y;
+  // Workgroups go to the eight XCDs round-robin by linear id; renumber them so that each XCD
+  // takes one contiguous range (neighbouring block columns share 128-byte lines of W and of
+  // the scale bytes, and each XCD has its own L2).
+  const int64_t gx = gridDim.x, gy = gridDim.y, n_wg = gx * gy * gridDim.z;
+  int64_t wid = blockIdx.x + gx * (blockIdx.y + gy * (int64_t)blockIdx.z);
+  if ((n_wg & 7) == 0) wid = (wid & 7) * (n_wg >> 3) + (wid >> 3);
+  const int64_t wx = wid % gx, batch = wid / (gx * gy), b = (wid / gx) % gy;
   const float S = S_arr[batch];
   build_cands(cand, S);
   const float hv = H[(batch * nb + b) * 256 + threadIdx.x];
@@ -385,7 +391,7 @@ __global__ void __launch_bounds__(256)
   const float rho = (float)(1.2e-5 * kappa);
   // this workgroup's tiles of 64 rows
   const int64_t n_tiles = (rows + 63) / 64;
-  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_wg;
+  const int64_t tile0 = wx * tiles_per_wg;
   const int64_t tile1 = min(tile0 + tiles_per_wg, n_tiles);
 
   if (!h_nonzero) {  // every candidate has objective 0: the MSE choice, one lane per row
