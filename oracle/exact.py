@@ -39,9 +39,15 @@ E4M3_VALUES = [e4m3(b) for b in range(127)]  # bytes 0x00..0x7E
 
 def max_byte(amax: Fr, S: Fr) -> int:
     """E4M3 byte nearest to amax / (6 S), saturating at 448 and at least 1 if amax > 0."""
+    return byte_for_divisor(amax, S, 6)
+
+
+def byte_for_divisor(amax: Fr, S: Fr, k: int) -> int:
+    """E4M3 byte nearest to amax / (k S) (ties to the even byte), saturating at 448 and at
+    least 1 if amax > 0."""
     if amax == 0:
         return 0
-    q = Fr(amax) / (6 * Fr(S))
+    q = Fr(amax) / (k * Fr(S))
     if q >= 448:
         return 126
     b = nearest_index(E4M3_VALUES, q)

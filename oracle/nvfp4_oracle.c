@@ -25,8 +25,8 @@
  *  [LH]   "How much dumber does 4-bit make a model? The answer is in the scale shared by
  *         every 16 weights" (2kiu.com/news/4970560), a write-up of NVIDIA Model
  *         Optimizer's "Improving NVFP4 Accuracy with Local-Hessian Weight Scales":
- *         "NVFP4 structure", the max / MSE paragraph (all 126 positive non-zero FP8
- *         scales), "Change the objective" (E(s) = ||dX||^2 = tr(d XX^T d^T); block-
+ *         "NVFP4 structure", the max / Four-Over-Six / MSE paragraph (two candidate
+ *         scales; all 126 positive non-zero FP8 scales), "Change the objective" (E(s) = ||dX||^2 = tr(d XX^T d^T); block-
  *         diagonal 16x16 H_b, 126 candidates per block).
  *
  * Readings where the pages are silent (each is listed in the design notes):
@@ -43,7 +43,8 @@
  *    obj = sum_i d_i y_i, both in double, ascending index, each term added with a fused
  *    multiply-add (one rounding per term);
  *  - argmins take the first (smallest byte) minimum; a block whose H_b is all zero
- *    takes the MSE choice.
+ *    takes the MSE choice;
+ *  - Four Over Six's two candidates are the bytes nearest amax_b / (6 S) and amax_b / (4 S).
  */
 #include <float.h>
 #include <math.h>
@@ -117,17 +118,25 @@ float oracle_tensor_scale(const float *x, int64_t n)
 /* Max-scaling block byte: E4M3 round-half-even of amax / (6 S) ([QAD] sec. 2.3 and 4.2,
  * [BT] "Why blocks", [LH] max scaling). Exact: v_b * 6S and midpoints * 6S have at most
  * 31 significant bits. */
-int oracle_max_byte(float amax, float S)
+/* E4M3 byte nearest to amax / (k S), ties to the even byte, saturating at 0x7E, at least
+ * 0x01 (k = 6 for max scaling, 4 for the second Four Over Six candidate; value * k * S has
+ * at most 31 significant bits, so the comparisons are exact in double). */
+int oracle_byte_for_divisor(float amax, float S, double k)
 {
     if (amax == 0.0f) return 0;
-    double a = amax, sixS = 6.0 * (double)S;
-    int b = 0; /* largest byte whose value * 6S <= amax */
-    while (b < 126 && oracle_e4m3_value(b + 1) * sixS <= a) ++b;
+    double a = amax, kS = k * (double)S;
+    int b = 0; /* largest byte whose value * kS <= amax */
+    while (b < 126 && oracle_e4m3_value(b + 1) * kS <= a) ++b;
     if (b < 126) {
-        double mid = 0.5 * (oracle_e4m3_value(b) + oracle_e4m3_value(b + 1)) * sixS;
+        double mid = 0.5 * (oracle_e4m3_value(b) + oracle_e4m3_value(b + 1)) * kS;
         if (a > mid || (a == mid && (b & 1))) ++b; /* ties to the even byte */
     }
     return b == 0 ? 1 : b;
+}
+
+int oracle_max_byte(float amax, float S)
+{
+    return oracle_byte_for_divisor(amax, S, 6.0);
 }
 
 /* E2M1 code of x under block byte `byte` and tensor scale S: round half to even on the
@@ -252,6 +261,41 @@ void oracle_scales_mse(const float *w, int64_t rows, int64_t cols, float S,
  * blocks are kept). X is row-major [tokens, cols] (one token per row). If token_ids is
  * non-NULL only those rows are summed, in the order given. Accumulates in double over
  * ascending position into H [cols/16][16][16] (which is overwritten). */
+/* Four Over Six ([LH], the paragraph on max / Four-Over-Six / MSE selection: one of two
+ * candidate scales per block). Reading (the page names only "two candidates"): the bytes
+ * nearest amax_b / (6 S) and amax_b / (4 S), i.e. the block max on the E2M1 magnitudes 6
+ * and 4; the one with the smaller MSE objective (as in oracle_scales_mse) wins, ties to
+ * the smaller byte. An all-zero block gets 0x00 and objective 0. */
+void oracle_scales_four_over_six(const float *w, int64_t rows, int64_t cols, float S,
+                                 uint8_t *scales, float *obj)
+{
+    int64_t nb = cols / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *x = w + r * cols + b * 16;
+            float amax = block_amax(x);
+            int best_b = 0;
+            float best = 0.0f;
+            if (amax != 0.0f) {
+                int c6 = oracle_byte_for_divisor(amax, S, 6.0);
+                int c4 = oracle_byte_for_divisor(amax, S, 4.0);
+                float e6 = oracle_block_sq_error(x, c6, S);
+                float e4 = oracle_block_sq_error(x, c4, S);
+                /* c4 >= c6; on equal objectives the smaller byte wins */
+                if (e4 < e6) {
+                    best_b = c4;
+                    best = e4;
+                } else {
+                    best_b = c6;
+                    best = e6;
+                }
+            }
+            scales[r * nb + b] = (uint8_t)best_b;
+            if (obj) obj[r * nb + b] = best;
+        }
+}
+
 void oracle_block_hessian(const float *X, int64_t tokens, int64_t cols,
                           const int32_t *token_ids, int64_t n_ids, double *H)
 {

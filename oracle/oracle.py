@@ -67,6 +67,10 @@ def lib():
         L.oracle_block_sq_error.argtypes = [P, ctypes.c_int, f32]
         L.oracle_scales_mse.restype = None
         L.oracle_scales_mse.argtypes = [P, i64, i64, f32, P, P]
+        L.oracle_byte_for_divisor.restype = ctypes.c_int
+        L.oracle_byte_for_divisor.argtypes = [f32, f32, ctypes.c_double]
+        L.oracle_scales_four_over_six.restype = None
+        L.oracle_scales_four_over_six.argtypes = [P, i64, i64, f32, P, P]
         L.oracle_block_hessian.restype = None
         L.oracle_block_hessian.argtypes = [P, i64, i64, P, i64, P]
         L.oracle_block_lh_objective.restype = ctypes.c_double
@@ -176,6 +180,19 @@ def scales_mse(w, S, with_obj: bool = False):
     out = np.empty((rows, cols // 16), dtype=np.uint8)
     obj = np.empty((rows, cols // 16), dtype=np.float32)
     lib().oracle_scales_mse(_p(a), rows, cols, float(np.float32(S)), _p(out), _p(obj))
+    return (out, obj) if with_obj else out
+
+
+def byte_for_divisor(amax: float, S: float, k: float) -> int:
+    return int(lib().oracle_byte_for_divisor(float(np.float32(amax)), float(np.float32(S)), float(k)))
+
+
+def scales_four_over_six(w, S, with_obj: bool = False):
+    a = _f32(w)
+    rows, cols = a.shape
+    out = np.empty((rows, cols // 16), dtype=np.uint8)
+    obj = np.empty((rows, cols // 16), dtype=np.float32)
+    lib().oracle_scales_four_over_six(_p(a), rows, cols, float(np.float32(S)), _p(out), _p(obj))
     return (out, obj) if with_obj else out
 
 
