@@ -113,6 +113,7 @@ def main():
     r3, c3 = w3.shape
     S3 = torch.empty(1, dtype=torch.float32, device=dev)
     sc3 = torch.empty(r3, c3 // 16, dtype=torch.uint8, device=dev)
+    sc3b = torch.empty(r3, c3 // 16, dtype=torch.uint8, device=dev)   # Four Over Six bytes
     codes3 = torch.empty(r3, c3 // 2, dtype=torch.uint8, device=dev)
 
     w4c, x4c = synth.projection(0)
@@ -165,6 +166,8 @@ def main():
         stage("scale_mlp", lambda: ok(L.nvfp4_global_scale(P(w3), BF16, 1, r3 * c3, P(S3), sptr), "scale"))
         stage("mse_mlp", lambda: ok(L.nvfp4_scale_search_mse(
             P(w3), BF16, 1, r3, c3, P(S3), P(sc3), None, sptr), "mse"))
+        stage("four_over_six_mlp", lambda: ok(L.nvfp4_scale_search_four_over_six(
+            P(w3), BF16, 1, r3, c3, P(S3), P(sc3b), None, sptr), "four over six"))
         stage("quantize_mlp", lambda: ok(L.nvfp4_quantize(
             P(w3), BF16, 1, r3, c3, P(S3), P(sc3), P(codes3), None, sptr), "quantize"))
         stage("hessian_proj", lambda: ok(L.nvfp4_block_hessian(
@@ -227,6 +230,7 @@ def main():
     lh5_time = ms["route_moe"] + ms["hessian_moe"] + ms["lh_moe"]
     lh5_blocks_s = n_lh5 / (lh5_time * 1e-3)
     mse_evals = r3 * (c3 // 16) * 126 * 16
+    fos_bytes = r3 * c3 * 2 + r3 * (c3 // 16)
     h4_bytes = t4 * c4 * 2
     h5_bytes = t5 * topk * c5 * 2
 
@@ -243,6 +247,8 @@ def main():
         "fakequant_act": roof("hbm", fq_gbs, HBM_PEAK_GBS, "GB/s", fq_traffic),
         "mse_mlp": roof("alu", mse_evals * MSE_OPS_PER_EVAL / (ms["mse_mlp"] * 1e-3) / 1e12,
                         round(VALU_LANE_TOPS, 2), "TOP/s"),
+        "four_over_six_mlp": roof("hbm", fos_bytes / (ms["four_over_six_mlp"] * 1e-3) / 1e9,
+                                  HBM_PEAK_GBS, "GB/s"),
         "hessian_proj": roof("hbm", h4_bytes / (ms["hessian_proj"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "lh_proj": roof("mfma", n_lh4 * 126 * 512 / (ms["lh_proj"] * 1e-3) / 1e12, FP32_MFMA_TFLOPS,
                         "TFLOP/s"),
@@ -266,8 +272,9 @@ def main():
         "data": "synthetic (seeded generators; no datasets or checkpoints)",
         "config": {
             "workload": "activation fake-quant bf16 8192x4096, max scaling (headline); per step "
-                        "also MSE on bf16 12288x4096, block Hessian of 131072x4096 + Local-Hessian "
-                        "on 4096x4096, MoE 128 experts 512x2048 with 65536 tokens top-8",
+                        "also MSE and Four Over Six on bf16 12288x4096, block Hessian of "
+                        "131072x4096 + Local-Hessian on 4096x4096, MoE 128 experts 512x2048 with "
+                        "65536 tokens top-8",
             "fakequant_bytes_per_launch": int(fq_bytes),
             "fakequant_launches_per_step": FQ_SETS,
         },
@@ -304,6 +311,9 @@ def main():
         t = time.perf_counter()
         oracle.scales_mse(wm, s3)
         dt_mse = time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.scales_four_over_six(wm, s3)
+        dt_fos = time.perf_counter() - t
         n_exp = 16
         We = w5[:n_exp].float().cpu().numpy()
         He = H5[:n_exp].cpu().numpy()
@@ -319,12 +329,14 @@ def main():
             "kind": "oracle",
             "sample": f"fake-quant of the whole 8192x4096 activation; Local-Hessian on "
                       f"{rows_lh} rows ({rows_lh * (c4 // 16)} blocks) of the 4096x4096 weight; "
-                      f"MSE on {rows_mse} rows ({rows_mse * (c3 // 16)} blocks) of the "
-                      f"12288x4096 weight; Local-Hessian on {n_exp} of the 128 experts",
+                      f"MSE and Four Over Six on {rows_mse} rows ({rows_mse * (c3 // 16)} "
+                      f"blocks) of the 12288x4096 weight; Local-Hessian on {n_exp} of the 128 "
+                      f"experts",
             "local_hessian_blocks_per_s": round(rows_lh * (c4 // 16) / dt_lh, 1),
             "mse_blocks_per_s": round(rows_mse * (c3 // 16) / dt_mse, 1),
+            "four_over_six_blocks_per_s": round(rows_mse * (c3 // 16) / dt_fos, 1),
             "local_hessian_moe_blocks_per_s": round(n_exp * r5 * (c5 // 16) / dt_lh5, 1),
-            "seconds": round(dt_fq + dt_lh + dt_mse + dt_lh5, 2),
+            "seconds": round(dt_fq + dt_lh + dt_mse + dt_fos + dt_lh5, 2),
         }
         out["gpu_over_cpu"] = {
             "fakequant": round(out["value"] / out["cpu_baseline"]["value"], 1),

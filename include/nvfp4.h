@@ -104,6 +104,19 @@ NVFP4_API int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, in
                            void *stream);
 
 /*
+ * Four Over Six scale selection ([LH] paragraph on max / Four-Over-Six / MSE selection:
+ * one of two candidate scales per block). Reading: the candidates are the E4M3 bytes
+ * nearest amax_b / (6 S[b]) (max scaling) and amax_b / (4 S[b]) (the block max on the E2M1
+ * magnitude 4), each saturating at 448 and at least 0x01; the one with the smaller MSE
+ * objective (as for nvfp4_scale_search_mse) wins, ties to the smaller byte. An all-zero
+ * block gets 0x00 and objective 0. Shapes, alignment and errors as for
+ * nvfp4_scale_search_mse; obj (nullable) receives the winning objective.
+ */
+NVFP4_API int nvfp4_scale_search_four_over_six(const void *w, int dtype, int64_t batch,
+                           int64_t rows, int64_t cols, const float *S, uint8_t *scales,
+                           float *obj, void *stream);
+
+/*
  * Block-diagonal calibration Gram matrix ([LH] "Change the objective": the output error
  * ||dX||^2 = tr(d XX^T d^T) is weighted by XX^T; only its 16x16 diagonal blocks are kept):
  *   H[g][b][i][j] (+)= sum over the tokens t of group g of x[t][16b+i] * x[t][16b+j].

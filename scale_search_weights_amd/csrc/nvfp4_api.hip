@@ -87,6 +87,18 @@ int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, int64_t rows
   return launch_mse(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
 }
 
+int nvfp4_scale_search_four_over_six(const void *w, int dtype, int64_t batch, int64_t rows,
+                                     int64_t cols, const float *S, uint8_t *scales, float *obj,
+                                     void *stream) {
+  bool empty = false;
+  int rc = check_tensor(dtype, batch, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!w || !S || !scales) return NVFP4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(S, 4) || !aligned(obj, 4)) return NVFP4_ERR_ALIGN;
+  if (rows * (cols / 16) / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
+  return launch_four_over_six(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
+}
+
 size_t nvfp4_block_hessian_workspace_size(int64_t tokens, int64_t cols, int64_t groups,
                                           int64_t n_ids) {
   if (tokens < 0 || cols < 0 || groups < 0 || n_ids < 0) return 0;

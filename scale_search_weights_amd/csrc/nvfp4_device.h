@@ -65,13 +65,15 @@ __device__ __forceinline__ void make_table(int byte, float S, ScaleTable &tb) {
   tb.d[7] = (float)(6.0 * sS);
 }
 
-// Max-scaling byte: E4M3 value nearest to amax / (6 S), ties to the even byte, saturating
-// at 448 (0x7E), at least 0x01 for amax > 0; 0x00 for amax == 0.
-__device__ __forceinline__ int max_scale_byte(float amax, float S) {
+// Max-scaling byte: E4M3 value nearest to amax / (k S), ties to the even byte, saturating
+// at 448 (0x7E), at least 0x01 for amax > 0; 0x00 for amax == 0. k = 6 maps the block max
+// onto the largest E2M1 magnitude; Four Over Six also tries k = 4. Products value * k * S
+// have at most 31 significant bits, so every comparison below is exact in double.
+__device__ __forceinline__ int max_scale_byte(float amax, float S, float k = 6.0f) {
   if (amax == 0.0f) return 0;
-  const double a = amax, sixS = 6.0 * (double)S;  // exact
+  const double a = amax, sixS = (double)k * (double)S;  // exact
   // first guess from an fp32 quotient, then exact correction
-  const float q = amax / (6.0f * S);
+  const float q = amax / (k * S);
   int b;
   if (!(q < 448.0f)) {
     b = 126;
@@ -113,12 +115,12 @@ __device__ __forceinline__ void recip_bracket(double d, float &lo, float &hi) {
   hi = (float)(r * (1.0 + 0x1p-22));
 }
 
-// Max-scaling byte from bracketing multipliers lo < 1/(6S) < hi. The two FP8 conversions
-// give the same byte, or two adjacent bytes when amax / (6S) lies within the bracket of the
+// Max-scaling byte from bracketing multipliers lo < 1/(kS) < hi. The two FP8 conversions
+// give the same byte, or two adjacent bytes when amax / (kS) lies within the bracket of the
 // midpoint between them; then one exact comparison (products <= 31 bits, exact in double)
 // decides, ties to the even byte.
 __device__ __forceinline__ int max_scale_byte_fast(float amax, float qlo_mul, float qhi_mul,
-                                                   float S) {
+                                                   float S, float k = 6.0f) {
   if (amax == 0.0f) return 0;
   const float qlo = fminf(amax * qlo_mul, 448.0f), qhi = fminf(amax * qhi_mul, 448.0f);
   const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(qlo, qhi, 0, false);
@@ -126,14 +128,22 @@ __device__ __forceinline__ int max_scale_byte_fast(float amax, float qlo_mul, fl
   const int b1 = (pk >> 8) & 0xFF;
   if (b != b1) {
     if (b1 == b + 1) {
-      const double mid = 0.5 * (e4m3_value_d(b) + e4m3_value_d(b1)) * (6.0 * (double)S);
+      const double mid = 0.5 * (e4m3_value_d(b) + e4m3_value_d(b1)) * ((double)k * (double)S);
       const double a = amax;
       b = (a > mid || (a == mid && (b & 1))) ? b1 : b;
     } else {
-      b = max_scale_byte(amax, S);
+      b = max_scale_byte(amax, S, k);
     }
   }
   return b == 0 ? 1 : b;
+}
+
+// Workgroup barrier that orders LDS only (address-space-qualified fences): global loads
+// issued before it stay in flight across it, so a table can be built while they land.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Per-tensor table of the 127 scale bytes: entry c >= 1 holds s = E4M3(c) and the bracket

@@ -227,20 +227,23 @@ __global__ void __launch_bounds__(256)
              int64_t total_blocks) {
   const bool one_batch = blocks_per_batch == total_blocks;
   const float S0 = S_arr[0];  // uniform: a scalar load
+  const int64_t total_half = 2 * total_blocks;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t hb0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // the first load (clamped to a valid index) is in flight while the table is built
+  const Raw8 first = load_raw8<DT>(x, hb0 < total_half ? hb0 : total_half - 1);
   // one tensor: the per-byte constants come from a table built once per workgroup
   __shared__ Cand tab[127];
   if (one_batch) {
     build_cands(tab, S0);
-    __syncthreads();
+    lds_barrier();
   }
-  const int64_t total_half = 2 * total_blocks;
-  for (int64_t hb = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; hb < total_half;
-       hb += (int64_t)gridDim.x * blockDim.x) {
+  auto block = [&](int64_t hb, const Raw8 &raw) {
     const int64_t blk = hb >> 1;
     const int h = (int)(hb & 1);
     const float S = one_batch ? S0 : S_arr[blk / blocks_per_batch];
     float v[8];
-    unpack_raw8<DT>(load_raw8<DT>(x, hb), v);
+    unpack_raw8<DT>(raw, v);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -301,7 +304,9 @@ __global__ void __launch_bounds__(256)
         st_out(p + 1, make_float4(dq[4], dq[5], dq[6], dq[7]));
       }
     }
-  }
+  };
+  if (hb0 < total_half) block(hb0, first);
+  for (int64_t hb = hb0 + stride; hb < total_half; hb += stride) block(hb, load_raw8<DT>(x, hb));
 }
 
 static unsigned grid_for(int64_t total_blocks) {

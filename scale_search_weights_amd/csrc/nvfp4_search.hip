@@ -140,13 +140,14 @@ __global__ void __launch_bounds__(256)
   __shared__ Cand cand[127];
   const int64_t batch = blockIdx.y;
   const float S = S_arr[batch];
-  build_cands(cand, S);
-  __syncthreads();
   const int64_t local = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (local >= blocks_per_batch) return;
-  const int64_t blk = batch * blocks_per_batch + local;
+  const bool active = local < blocks_per_batch;
+  const int64_t blk = batch * blocks_per_batch + (active ? local : 0);
   float v[16], X[16];
-  load16<DT>(w, blk, v);
+  load16<DT>(w, blk, v);  // in flight while the table is built
+  build_cands(cand, S);
+  lds_barrier();
+  if (!active) return;
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -168,6 +169,63 @@ int launch_mse(const void *w, int dtype, int64_t batch, int64_t rows, int64_t co
     hipLaunchKernelGGL(k_mse<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, scales, obj, bpb);
   else
     hipLaunchKernelGGL(k_mse<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, scales, obj, bpb);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ Four Over Six
+//
+// Local-Hessian write-up, paragraph on max / Four-Over-Six / MSE selection: one of two
+// candidate scales per block. Reading: the bytes nearest amax/(6S) and amax/(4S) (block max
+// on the E2M1 magnitudes 6 and 4); the smaller MSE objective (the same fp32 chain as the MSE
+// search) wins, ties to the smaller byte. One lane per block, as for MSE.
+
+template <int DT>
+__global__ void __launch_bounds__(256)
+    k_four_over_six(const void *__restrict__ w, const float *__restrict__ S_arr,
+                    uint8_t *__restrict__ scales, float *__restrict__ obj,
+                    int64_t blocks_per_batch) {
+  __shared__ Cand cand[127];
+  const int64_t batch = blockIdx.y;
+  const float S = S_arr[batch];
+  const int64_t local = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = local < blocks_per_batch;
+  const int64_t blk = batch * blocks_per_batch + (active ? local : 0);
+  float v[16], X[16];
+  load16<DT>(w, blk, v);  // in flight while the table is built
+  build_cands(cand, S);
+  lds_barrier();
+  if (!active) return;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    X[i] = fabsf(v[i]);
+    amax = fmaxf(amax, X[i]);
+  }
+  int best_c = 0;
+  float best = 0.0f;
+  if (amax != 0.0f) {
+    // cand[0] brackets 1/(6S); 1/(4S) = 1.5/(6S) keeps the bracket (one rounding < 2^-24)
+    const int c6 = max_scale_byte_fast(amax, cand[0].rlo, cand[0].rhi, S, 6.0f);
+    const int c4 = max_scale_byte_fast(amax, 1.5f * cand[0].rlo, 1.5f * cand[0].rhi, S, 4.0f);
+    const bool fast_ok = fast_path_ok(amax, cand);
+    const float o6 = mse_candidate(X, c6, cand[c6], S, fast_ok);
+    const float o4 = mse_candidate(X, c4, cand[c4], S, fast_ok);
+    const bool take4 = o4 < o6;  // c4 >= c6: on equal objectives the smaller byte wins
+    best_c = take4 ? c4 : c6;
+    best = take4 ? o4 : o6;
+  }
+  scales[blk] = (uint8_t)best_c;
+  if (obj) obj[blk] = best;
+}
+
+int launch_four_over_six(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                         const float *S, uint8_t *scales, float *obj, hipStream_t st) {
+  const int64_t bpb = rows * (cols / 16);
+  const dim3 g((unsigned)((bpb + 255) / 256), (unsigned)batch), b(256);
+  if (dtype == NVFP4_DTYPE_BF16)
+    hipLaunchKernelGGL(k_four_over_six<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, scales, obj, bpb);
+  else
+    hipLaunchKernelGGL(k_four_over_six<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, scales, obj, bpb);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

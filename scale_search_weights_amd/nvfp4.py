@@ -37,6 +37,7 @@ _SIGS = {
     "nvfp4_global_scale": (_I, [_P, _I, _I64, _I64, _P, _P]),
     "nvfp4_scale_search_max": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P]),
     "nvfp4_scale_search_mse": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_scale_search_four_over_six": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_block_hessian_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
     "nvfp4_block_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_scale_search_local_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -148,6 +149,17 @@ def scale_search_mse(w: torch.Tensor, S: torch.Tensor, return_obj: bool = False)
     obj = torch.empty(_out_shape(w, c // 16), dtype=torch.float32, device=w.device) if return_obj else None
     _check(lib().nvfp4_scale_search_mse(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(sc), _ptr(obj),
                                         _stream()), "nvfp4_scale_search_mse")
+    return (sc, obj) if return_obj else sc
+
+
+def scale_search_four_over_six(w: torch.Tensor, S: torch.Tensor, return_obj: bool = False):
+    _need(w, "w")
+    b, r, c = _shape3(w)
+    sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
+    obj = torch.empty(_out_shape(w, c // 16), dtype=torch.float32, device=w.device) if return_obj else None
+    _check(lib().nvfp4_scale_search_four_over_six(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(sc),
+                                                  _ptr(obj), _stream()),
+           "nvfp4_scale_search_four_over_six")
     return (sc, obj) if return_obj else sc
 
 

@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = nvfp4.declared_symbols()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert L.nvfp4_version() == 100
@@ -55,6 +55,7 @@ def test_empty_tensors_return_ok_without_launch(L):
     assert L.nvfp4_fakequant(None, 1, 1, 0, 16, None, None, None, None, None, None) == OK
     assert L.nvfp4_fakequant(None, 1, 0, 4, 16, None, None, None, None, None, None) == OK
     assert L.nvfp4_scale_search_mse(None, 0, 1, 4, 0, None, None, None, None) == OK
+    assert L.nvfp4_scale_search_four_over_six(None, 1, 0, 4, 16, None, None, None, None) == OK
     assert L.nvfp4_scale_search_local_hessian(None, 1, 1, 0, 32, None, None, None, None, None) == OK
     assert L.nvfp4_global_scale(None, 1, 0, 16, None, None) == OK
     assert L.nvfp4_quantize(None, 1, 1, 0, 16, None, None, None, None, None) == OK
@@ -67,6 +68,12 @@ def test_each_entry_point_validates(L):
     assert L.nvfp4_scale_search_max(P(FAKE), 1, 1, 2, 16, P(FAKE), None, None) == ENULL
     assert L.nvfp4_scale_search_mse(P(FAKE), 1, 1, 2, 8, P(FAKE), P(FAKE), None, None) == ESHAPE
     assert L.nvfp4_scale_search_mse(P(FAKE), 1, 1, 2, 16, P(FAKE), P(FAKE), P(FAKE + 1), None) == EALIGN
+    f46 = L.nvfp4_scale_search_four_over_six
+    assert f46(P(FAKE), 1, 1, 2, 24, P(FAKE), P(FAKE), None, None) == ESHAPE
+    assert f46(P(FAKE), 4, 1, 2, 16, P(FAKE), P(FAKE), None, None) == EDTYPE
+    assert f46(P(FAKE), 1, 1, 2, 16, None, P(FAKE), None, None) == ENULL
+    assert f46(P(FAKE + 8), 1, 1, 2, 16, P(FAKE), P(FAKE), None, None) == EALIGN
+    assert f46(P(FAKE), 1, 1, 2, 16, P(FAKE), P(FAKE), P(FAKE + 2), None) == EALIGN
     assert L.nvfp4_scale_search_local_hessian(P(FAKE), 1, 1, 2, 16, P(FAKE), None, P(FAKE), None,
                                               None) == ENULL
     assert L.nvfp4_scale_search_local_hessian(P(FAKE), 1, 1, 2, 16, P(FAKE), P(FAKE), P(FAKE),

@@ -63,6 +63,28 @@ def test_mlp_weight_mse_12288x4096(orc):
     assert torch.all(obj.view(-1) <= e_max * (1 + 1e-5) + 1e-30)
 
 
+def test_mlp_weight_four_over_six_12288x4096(orc):
+    case("Four Over Six bf16 12288x4096 (3.1M blocks)")
+    w = synth.mlp_weight(0)
+    wd = w.to(DEV)
+    S = nvfp4.global_scale(wd)
+    wn = f32(w)
+    sc, obj = nvfp4.scale_search_four_over_six(wd, S, return_obj=True)
+    rows = np.random.default_rng(2).choice(w.shape[0], 24, replace=False)
+    sr, orf = orc.scales_four_over_six(wn[rows], S.item(), with_obj=True)
+    assert np.array_equal(sc.cpu().numpy()[rows], sr)
+    assert np.array_equal(obj.cpu().numpy()[rows], orf)
+    # whole tensor: the exhaustive MSE objective is a lower bound (same fp32 objective over a
+    # superset of candidates), the max-scaling error an upper bound
+    _, obj_mse = nvfp4.scale_search_mse(wd, S, return_obj=True)
+    assert torch.all(obj_mse <= obj)
+    mx = nvfp4.scale_search_max(wd, S)
+    codes_max, _ = nvfp4.quantize(wd, S, mx)
+    y_max = nvfp4.dequantize(codes_max, mx, S, out_dtype=torch.float32)
+    e_max = ((y_max - wd.float()) ** 2).view(-1, 16).sum(1)
+    assert torch.all(obj.view(-1) <= e_max * (1 + 1e-5) + 1e-30)
+
+
 def test_projection_hessian_and_local_hessian_full(orc):
     case("block Hessian of 131072x4096 bf16 t4 tokens + Local-Hessian on 4096x4096")
     w, x = synth.projection(0)

@@ -288,6 +288,72 @@ def test_mse_batched_and_zero_blocks(orc):
     assert sc[2, 5, 1].item() == 0
 
 
+# ------------------------------------------------------------------ Four Over Six
+
+def _fos_check(orc, w, S):
+    x = w if isinstance(w, torch.Tensor) else torch.from_numpy(w)
+    sc, obj = nvfp4.scale_search_four_over_six(x.to(DEV), dev_S(S), return_obj=True)
+    sr, orf = orc.scales_four_over_six(f32(x), S, with_obj=True)
+    g = sc.cpu().numpy()
+    assert np.array_equal(g, sr), (np.sum(g != sr), np.argwhere(g != sr)[:5])
+    assert np.array_equal(obj.cpu().numpy().view(np.uint32), orf.view(np.uint32))
+    return g
+
+
+@pytest.mark.parametrize("which", ["tiny_fp32", "ragged_bf16", "proj_bf16"])
+def test_four_over_six(orc, tiny, which):
+    case(f"four over six {which}")
+    if which == "tiny_fp32":
+        w = tiny[0]
+    elif which == "ragged_bf16":
+        w = synth.mlp_weight(4, 77, 272)           # 17 blocks per row, odd rows
+    else:
+        w = synth.projection(12, rows=96, cols=512, tokens=16)[0]
+    S = orc.tensor_scale(f32(w))
+    g = _fos_check(orc, w, S)
+    # the choice is one of the two candidates and never worse than max scaling
+    mx = orc.scales_max(f32(w), S)
+    assert np.mean(g == mx) > 0.2 and np.mean(g != mx) > 0.05
+
+
+@pytest.mark.parametrize("S", [None, 1.0, 2.0 ** -20, 1e30])
+def test_four_over_six_edges(orc, S):
+    """Lone exact values 24*2^j (tie: both candidates exact), blocks on the k = 4 grid,
+    constant and zero blocks, denormal inputs, midpoint values, and S that saturates every
+    byte (tiny S) or pushes the scales to subnormal E4M3 (huge S)."""
+    case(f"four over six edges S={S}")
+    rng = np.random.default_rng(31)
+    blocks = [rng.standard_normal((64, 16)).astype(np.float32) * np.float32(0.02)]
+    lone = np.zeros((6, 16), np.float32)
+    for i, j in enumerate((-6, -3, 0, 1, 2, 4)):
+        lone[i, (5 * i) % 16] = np.float32(24.0 * 2.0 ** j) * (1 if i % 2 else -1)
+    blocks.append(lone)
+    g4 = np.array([4, -3, 2, 1.5, -1, 0.5, 0, 3, -4, 2, 1, -0.5, 1.5, 0, 4, -2], np.float32)
+    blocks.append(np.stack([g4 * np.float32(2.0 ** k) for k in range(-8, 8)]))
+    blocks.append(np.repeat(rng.uniform(-1, 1, (8, 1)).astype(np.float32), 16, axis=1))
+    blocks.append(np.zeros((2, 16), np.float32))
+    blocks.append((rng.standard_normal((4, 16)) * 1e-39).astype(np.float32))  # denormals
+    blocks.append(synth.on_grid_block_values(5, 16 * 16).reshape(16, 16) * np.float32(0.375))
+    x = np.concatenate(blocks).reshape(-1, 16)
+    Sv = orc.tensor_scale(x) if S is None else np.float32(S)
+    _fos_check(orc, x, Sv)
+
+
+def test_four_over_six_batched(orc):
+    case("four over six batch of 3 experts with per-entry S and a zero block")
+    w = synth.moe(13, experts=3, rows=24, cols=96, tokens=8, topk=1)[0]
+    w[1, 4, 32:48] = 0
+    wd = w.to(DEV)
+    S = nvfp4.global_scale(wd)
+    sc, obj = nvfp4.scale_search_four_over_six(wd, S, return_obj=True)
+    Sn = S.cpu().numpy()
+    for b in range(3):
+        sr, orf = orc.scales_four_over_six(f32(w[b]), Sn[b], with_obj=True)
+        assert np.array_equal(sc[b].cpu().numpy(), sr)
+        assert np.array_equal(obj[b].cpu().numpy().view(np.uint32), orf.view(np.uint32))
+    assert sc[1, 4, 2].item() == 0
+
+
 # ------------------------------------------------------------------ block Hessian
 
 @pytest.mark.parametrize("which", ["tiny_fp32", "proj_bf16", "ragged_bf16", "narrow_bf16"])
