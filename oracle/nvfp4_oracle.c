@@ -21,7 +21,8 @@
  *  [BT]   "Baseten on high-quality NVFP4 quantization" (attain.fans translation):
  *         "Why do we need a scale" (the 16 FP4 values; an FP32 per-tensor scale also
  *         exists), "Block scaling" (16 consecutive values per block), "Why blocks"
- *         (worked example: max 84 gives scale 14 and magnitudes 0..84).
+ *         (worked example: max 84 gives scale 14 and magnitudes 0..84), "Calibration"
+ *         (activation ranges from sample inputs; min/max or outlier-clipping ranges).
  *  [LH]   "How much dumber does 4-bit make a model? The answer is in the scale shared by
  *         every 16 weights" (2kiu.com/news/4970560), a write-up of NVIDIA Model
  *         Optimizer's "Improving NVFP4 Accuracy with Local-Hessian Weight Scales":
@@ -44,7 +45,9 @@
  *    multiply-add (one rounding per term);
  *  - argmins take the first (smallest byte) minimum; a block whose H_b is all zero
  *    takes the MSE choice;
- *  - Four Over Six's two candidates are the bytes nearest amax_b / (6 S) and amax_b / (4 S).
+ *  - Four Over Six's two candidates are the bytes nearest amax_b / (6 S) and amax_b / (4 S);
+ *  - calibration clip value: the k-th smallest |x| (k = ceil(p N)) rounded toward zero to
+ *    bf16, from an exact histogram with one bin per bf16 magnitude.
  */
 #include <float.h>
 #include <math.h>
@@ -132,6 +135,46 @@ int oracle_byte_for_divisor(float amax, float S, double k)
         if (a > mid || (a == mid && (b & 1))) ++b; /* ties to the even byte */
     }
     return b == 0 ? 1 : b;
+}
+
+/* Static activation calibration ([BT] "Calibration": feed representative inputs, record the
+ * activation distribution, pick a clipping range -- min/max, or percentile / histogram
+ * methods that clip a few outliers -- then scale each block). Reading: an exact histogram
+ * of |x| with one bin per bf16 magnitude, bin = (fp32 bits of |x|) >> 16 (32768 bins),
+ * accumulated over calibration batches; the clip value for a fraction p in (0, 1] is the
+ * lower edge of the first bin whose cumulative count reaches ceil(p N), i.e. the k-th
+ * smallest magnitude rounded toward zero to bf16 (exact for bf16 data; p = 1 gives amax);
+ * the tensor scale is the tensor-scale formula applied to the clip value. */
+void oracle_calib_histogram(const float *x, int64_t n, uint64_t *hist)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u;
+        memcpy(&u, &x[i], 4);
+        hist[(u & 0x7FFFFFFFu) >> 16] += 1;
+    }
+}
+
+float oracle_calib_scale(const uint64_t *hist, double fraction)
+{
+    uint64_t total = 0;
+    for (int b = 0; b < 32768; ++b) total += hist[b];
+    if (total == 0) return 1.0f;
+    uint64_t k = (uint64_t)ceil(fraction * (double)total);
+    if (k < 1) k = 1;
+    if (k > total) k = total;
+    uint64_t cum = 0;
+    int b = 0;
+    for (; b < 32768; ++b) {
+        cum += hist[b];
+        if (cum >= k) break;
+    }
+    uint32_t u = (uint32_t)b << 16;
+    float clip;
+    memcpy(&clip, &u, 4);
+    if (clip == 0.0f) return 1.0f;
+    float S = clip / 2688.0f;
+    if (S < FLT_MIN) S = FLT_MIN;
+    return S;
 }
 
 int oracle_max_byte(float amax, float S)

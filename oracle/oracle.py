@@ -67,6 +67,10 @@ def lib():
         L.oracle_block_sq_error.argtypes = [P, ctypes.c_int, f32]
         L.oracle_scales_mse.restype = None
         L.oracle_scales_mse.argtypes = [P, i64, i64, f32, P, P]
+        L.oracle_calib_histogram.restype = None
+        L.oracle_calib_histogram.argtypes = [P, i64, P]
+        L.oracle_calib_scale.restype = f32
+        L.oracle_calib_scale.argtypes = [P, ctypes.c_double]
         L.oracle_byte_for_divisor.restype = ctypes.c_int
         L.oracle_byte_for_divisor.argtypes = [f32, f32, ctypes.c_double]
         L.oracle_scales_four_over_six.restype = None
@@ -121,6 +125,23 @@ def bf16_rne_array(y: np.ndarray) -> np.ndarray:
 def tensor_scale(x) -> np.float32:
     a = _f32(x)
     return np.float32(lib().oracle_tensor_scale(_p(a), a.size))
+
+
+CALIB_BINS = 32768
+
+
+def calib_histogram(x, hist=None) -> np.ndarray:
+    """Accumulate the |x| histogram (one bin per bf16 magnitude) into hist (uint64)."""
+    a = _f32(x)
+    if hist is None:
+        hist = np.zeros(CALIB_BINS, dtype=np.uint64)
+    lib().oracle_calib_histogram(_p(a), a.size, _p(hist))
+    return hist
+
+
+def calib_scale(hist, fraction: float) -> np.float32:
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    return np.float32(lib().oracle_calib_scale(_p(h), float(fraction)))
 
 
 def max_byte(amax: float, S: float) -> int:
