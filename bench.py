@@ -37,6 +37,7 @@ VALU_LANE_TOPS = 256 * 64 * 2.4e9 / 1e12   # non-packed lane-ops/s: 256 CU x 64 
 MSE_OPS_PER_EVAL = 5           # compare/select x3, subtract, fma per element x candidate
 FQ_BYTES_PER_ELEM = 2 + 2 + 0.5 + 1 / 16   # read bf16, write bf16 + packed code + 1/16 byte
 FQ_SETS = 4                    # activation batches fake-quantised per step
+CALIB_FRACTION = 0.9999        # activation clip value: this fraction of calibration values
 
 
 def _sha_of(paths):
@@ -109,6 +110,10 @@ def main():
     codes2s = [torch.empty(r2, c2 // 2, dtype=torch.uint8, device=dev) for _ in range(FQ_SETS)]
     sc2s = [torch.empty(r2, c2 // 16, dtype=torch.uint8, device=dev) for _ in range(FQ_SETS)]
 
+    # static calibration: every step adds one activation batch to a running histogram
+    hist2 = torch.zeros(nvfp4.CALIB_BINS, dtype=torch.int64, device=dev)
+    S2c = torch.empty(1, dtype=torch.float32, device=dev)
+
     w3 = synth.mlp_weight(0).to(dev)                       # [12288, 4096]
     r3, c3 = w3.shape
     S3 = torch.empty(1, dtype=torch.float32, device=dev)
@@ -163,6 +168,10 @@ def main():
                 ok(L.nvfp4_fakequant(P(a2s[k]), BF16, 1, r2, c2, P(S2), None, P(y2s[k]),
                                      P(codes2s[k]), P(sc2s[k]), sptr), "fakequant")
         stage("fakequant_act", fq)
+        stage("calib_act", lambda: (ok(L.nvfp4_calib_histogram(P(a2), BF16, r2 * c2, P(hist2), sptr),
+                                       "calibration histogram"),
+                                    ok(L.nvfp4_calib_scale(P(hist2), ctypes.c_double(CALIB_FRACTION),
+                                                           P(S2c), sptr), "calibration scale")))
         stage("scale_mlp", lambda: ok(L.nvfp4_global_scale(P(w3), BF16, 1, r3 * c3, P(S3), sptr), "scale"))
         stage("mse_mlp", lambda: ok(L.nvfp4_scale_search_mse(
             P(w3), BF16, 1, r3, c3, P(S3), P(sc3), None, sptr), "mse"))
@@ -231,6 +240,7 @@ def main():
     lh5_blocks_s = n_lh5 / (lh5_time * 1e-3)
     mse_evals = r3 * (c3 // 16) * 126 * 16
     fos_bytes = r3 * c3 * 2 + r3 * (c3 // 16)
+    cal_bytes = r2 * c2 * 2
     h4_bytes = t4 * c4 * 2
     h5_bytes = t5 * topk * c5 * 2
 
@@ -247,6 +257,7 @@ def main():
         "fakequant_act": roof("hbm", fq_gbs, HBM_PEAK_GBS, "GB/s", fq_traffic),
         "mse_mlp": roof("alu", mse_evals * MSE_OPS_PER_EVAL / (ms["mse_mlp"] * 1e-3) / 1e12,
                         round(VALU_LANE_TOPS, 2), "TOP/s"),
+        "calib_act": roof("hbm", cal_bytes / (ms["calib_act"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "four_over_six_mlp": roof("hbm", fos_bytes / (ms["four_over_six_mlp"] * 1e-3) / 1e9,
                                   HBM_PEAK_GBS, "GB/s"),
         "hessian_proj": roof("hbm", h4_bytes / (ms["hessian_proj"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
@@ -272,7 +283,8 @@ def main():
         "data": "synthetic (seeded generators; no datasets or checkpoints)",
         "config": {
             "workload": "activation fake-quant bf16 8192x4096, max scaling (headline); per step "
-                        "also MSE and Four Over Six on bf16 12288x4096, block Hessian of "
+                        "also the activation's calibration histogram and clip scale, MSE and "
+                        "Four Over Six on bf16 12288x4096, block Hessian of "
                         "131072x4096 + Local-Hessian on 4096x4096, MoE 128 experts 512x2048 with "
                         "65536 tokens top-8",
             "fakequant_bytes_per_launch": int(fq_bytes),
@@ -314,6 +326,9 @@ def main():
         t = time.perf_counter()
         oracle.scales_four_over_six(wm, s3)
         dt_fos = time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.calib_scale(oracle.calib_histogram(xa.ravel()), CALIB_FRACTION)
+        dt_cal = time.perf_counter() - t
         n_exp = 16
         We = w5[:n_exp].float().cpu().numpy()
         He = H5[:n_exp].cpu().numpy()
@@ -329,14 +344,16 @@ def main():
             "kind": "oracle",
             "sample": f"fake-quant of the whole 8192x4096 activation; Local-Hessian on "
                       f"{rows_lh} rows ({rows_lh * (c4 // 16)} blocks) of the 4096x4096 weight; "
+                      f"calibration histogram of the activation; "
                       f"MSE and Four Over Six on {rows_mse} rows ({rows_mse * (c3 // 16)} "
                       f"blocks) of the 12288x4096 weight; Local-Hessian on {n_exp} of the 128 "
                       f"experts",
             "local_hessian_blocks_per_s": round(rows_lh * (c4 // 16) / dt_lh, 1),
             "mse_blocks_per_s": round(rows_mse * (c3 // 16) / dt_mse, 1),
             "four_over_six_blocks_per_s": round(rows_mse * (c3 // 16) / dt_fos, 1),
+            "calibration_gbs": round(xa.size * 2 / dt_cal / 1e9, 3),
             "local_hessian_moe_blocks_per_s": round(n_exp * r5 * (c5 // 16) / dt_lh5, 1),
-            "seconds": round(dt_fq + dt_lh + dt_mse + dt_fos + dt_lh5, 2),
+            "seconds": round(dt_fq + dt_lh + dt_mse + dt_fos + dt_cal + dt_lh5, 2),
         }
         out["gpu_over_cpu"] = {
             "fakequant": round(out["value"] / out["cpu_baseline"]["value"], 1),

@@ -112,6 +112,26 @@ NVFP4_API int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, in
  * block gets 0x00 and objective 0. Shapes, alignment and errors as for
  * nvfp4_scale_search_mse; obj (nullable) receives the winning objective.
  */
+/*
+ * Static activation calibration ([BT] "Calibration": the activation distribution recorded
+ * over sample inputs sets the clipping range -- the min/max, or percentile / histogram
+ * methods that clip a few outliers). Reading:
+ *  - nvfp4_calib_histogram adds the magnitudes of x [n] (n % 8 == 0, 16-byte aligned) to
+ *    hist [NVFP4_CALIB_BINS] (device uint64, 8-byte aligned, caller-zeroed once and then
+ *    accumulated over calibration batches): bin = (fp32 bits of |x|) >> 16, i.e. one bin per
+ *    bf16 magnitude. Counts are integers, so the result does not depend on launch order.
+ *  - nvfp4_calib_scale writes S[0] (device fp32): with N the total count and k =
+ *    ceil(fraction * N), the clip value is the lower edge of the first bin whose cumulative
+ *    count reaches k (the k-th smallest magnitude, rounded toward zero to bf16; exact for
+ *    bf16 data, and fraction = 1 gives the max), and S = fp32(clip / 2688) as for
+ *    nvfp4_global_scale (1 for an empty or all-zero histogram). fraction must lie in
+ *    (0, 1], else NVFP4_ERR_ARG.
+ */
+#define NVFP4_CALIB_BINS 32768
+NVFP4_API int nvfp4_calib_histogram(const void *x, int dtype, int64_t n, uint64_t *hist,
+                          void *stream);
+NVFP4_API int nvfp4_calib_scale(const uint64_t *hist, double fraction, float *S, void *stream);
+
 NVFP4_API int nvfp4_scale_search_four_over_six(const void *w, int dtype, int64_t batch,
                            int64_t rows, int64_t cols, const float *S, uint8_t *scales,
                            float *obj, void *stream);

@@ -99,6 +99,24 @@ int nvfp4_scale_search_four_over_six(const void *w, int dtype, int64_t batch, in
   return launch_four_over_six(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
 }
 
+int nvfp4_calib_histogram(const void *x, int dtype, int64_t n, uint64_t *hist, void *stream) {
+  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+  if (n < 0 || (n % 8) != 0) return NVFP4_ERR_SHAPE;
+  if (!hist || (n > 0 && !x)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(hist, 8)) return NVFP4_ERR_ALIGN;
+  if (n == 0) return NVFP4_OK;
+  return launch_calib_histogram(x, dtype, n, reinterpret_cast<unsigned long long *>(hist),
+                                as_stream(stream));
+}
+
+int nvfp4_calib_scale(const uint64_t *hist, double fraction, float *S, void *stream) {
+  if (!hist || !S) return NVFP4_ERR_NULL;
+  if (!(fraction > 0.0 && fraction <= 1.0)) return NVFP4_ERR_ARG;
+  if (!aligned(hist, 8) || !aligned(S, 4)) return NVFP4_ERR_ALIGN;
+  return launch_calib_scale(reinterpret_cast<const unsigned long long *>(hist), fraction, S,
+                            as_stream(stream));
+}
+
 size_t nvfp4_block_hessian_workspace_size(int64_t tokens, int64_t cols, int64_t groups,
                                           int64_t n_ids) {
   if (tokens < 0 || cols < 0 || groups < 0 || n_ids < 0) return 0;

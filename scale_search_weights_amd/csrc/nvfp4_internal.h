@@ -17,6 +17,9 @@ int launch_quant(const void *x, int dtype, int64_t batch, int64_t rows, int64_t 
                  void *y, hipStream_t st);
 int launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *S, int64_t batch,
                    int64_t rows, int64_t cols, void *y, int out_dtype, hipStream_t st);
+int launch_calib_histogram(const void *x, int dtype, int64_t n, unsigned long long *hist,
+                           hipStream_t st);
+int launch_calib_scale(const unsigned long long *hist, double fraction, float *S, hipStream_t st);
 int launch_four_over_six(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
                          const float *S, uint8_t *scales, float *obj, hipStream_t st);
 int launch_mse(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,

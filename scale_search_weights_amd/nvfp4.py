@@ -38,6 +38,8 @@ _SIGS = {
     "nvfp4_scale_search_max": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P]),
     "nvfp4_scale_search_mse": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_scale_search_four_over_six": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_calib_histogram": (_I, [_P, _I, _I64, _P, _P]),
+    "nvfp4_calib_scale": (_I, [_P, ctypes.c_double, _P, _P]),
     "nvfp4_block_hessian_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
     "nvfp4_block_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_scale_search_local_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -161,6 +163,27 @@ def scale_search_four_over_six(w: torch.Tensor, S: torch.Tensor, return_obj: boo
                                                   _ptr(obj), _stream()),
            "nvfp4_scale_search_four_over_six")
     return (sc, obj) if return_obj else sc
+
+
+CALIB_BINS = 32768
+
+
+def calib_histogram(x: torch.Tensor, hist: torch.Tensor | None = None) -> torch.Tensor:
+    """Add |x| to a calibration histogram ([CALIB_BINS] int64 on x's device; new if None)."""
+    _need(x, "x")
+    if hist is None:
+        hist = torch.zeros(CALIB_BINS, dtype=torch.int64, device=x.device)
+    _check(lib().nvfp4_calib_histogram(_ptr(x), _dt(x), x.numel(), _ptr(hist), _stream()),
+           "nvfp4_calib_histogram")
+    return hist
+
+
+def calib_scale(hist: torch.Tensor, fraction: float) -> torch.Tensor:
+    """Tensor scale S [1] from the clip value at `fraction` of the histogram's values."""
+    S = torch.empty(1, dtype=torch.float32, device=hist.device)
+    _check(lib().nvfp4_calib_scale(_ptr(hist), float(fraction), _ptr(S), _stream()),
+           "nvfp4_calib_scale")
+    return S
 
 
 def block_hessian_workspace_size(tokens: int, cols: int, groups: int = 1, n_ids: int = 0) -> int:

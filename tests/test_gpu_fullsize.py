@@ -42,6 +42,19 @@ def test_activation_fakequant_8192x4096(orc):
     assert np.array_equal(got, orc.bf16_rne_array(dq))
 
 
+def test_activation_calibration_8192x4096(orc):
+    case("calibration histogram and scale over the bf16 8192x4096 activation")
+    x = synth.activation(0)
+    xd = x.to(DEV)
+    h = nvfp4.calib_histogram(xd.view(-1))
+    href = orc.calib_histogram(f32(x).ravel())
+    assert np.array_equal(h.cpu().numpy().view(np.uint64), href)
+    for frac in (0.999, 0.9999, 1.0):
+        assert nvfp4.calib_scale(h, frac).item() == orc.calib_scale(href, frac)
+    # the whole range reproduces the max calibration
+    assert nvfp4.calib_scale(h, 1.0).item() == nvfp4.global_scale(xd).item()
+
+
 def test_mlp_weight_mse_12288x4096(orc):
     case("MSE search bf16 12288x4096 (3.1M blocks)")
     w = synth.mlp_weight(0)

@@ -354,6 +354,43 @@ def test_four_over_six_batched(orc):
     assert sc[1, 4, 2].item() == 0
 
 
+# ------------------------------------------------------------------ calibration
+
+@pytest.mark.parametrize("which", ["act_bf16", "fp32", "ragged_bf16", "tiny", "zeros_denormals"])
+def test_calib_histogram_and_scale(orc, which):
+    case(f"calibration histogram and scale: {which}")
+    rng = np.random.default_rng(41)
+    if which == "act_bf16":
+        x = synth.activation(3, tokens=300, hidden=512)                   # 153,600 values
+    elif which == "fp32":
+        x = torch.from_numpy((rng.standard_t(3, 70_000) * 2).astype(np.float32))
+    elif which == "ragged_bf16":
+        x = synth.activation(4, tokens=3, hidden=32768 + 8)               # chunks + a tail
+    elif which == "tiny":
+        x = torch.tensor([0.5, -1.5, 3.0, 0.0, -0.0, 2.0, 1e-3, -7.0])
+    else:
+        x = torch.tensor([0.0, -0.0, 1e-40, -3e-41, 0.0, 0.0, 2e-39, -0.0] * 5)
+    xd = x.to(DEV).contiguous().view(-1)
+    h = nvfp4.calib_histogram(xd)
+    href = orc.calib_histogram(f32(x).ravel())
+    assert np.array_equal(h.cpu().numpy().view(np.uint64), href)
+    for frac in (0.5, 0.99, 0.9999, 1.0):
+        S = nvfp4.calib_scale(h, frac)
+        assert S.item() == orc.calib_scale(href, frac), frac
+
+
+def test_calib_accumulates_over_batches(orc):
+    case("calibration histogram over three batches")
+    xs = [synth.activation(s, tokens=64, hidden=1024) for s in (7, 8, 9)]
+    h = None
+    href = None
+    for x in xs:
+        h = nvfp4.calib_histogram(x.to(DEV).view(-1), h)
+        href = orc.calib_histogram(f32(x).ravel(), href)
+    assert np.array_equal(h.cpu().numpy().view(np.uint64), href)
+    assert nvfp4.calib_scale(h, 0.999).item() == orc.calib_scale(href, 0.999)
+
+
 # ------------------------------------------------------------------ block Hessian
 
 @pytest.mark.parametrize("which", ["tiny_fp32", "proj_bf16", "ragged_bf16", "narrow_bf16"])
