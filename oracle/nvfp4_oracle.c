@@ -17,7 +17,8 @@
  *         bit; one FP8 scale shared by 16 elements), sec. 2.1 (values go to the nearest
  *         representable level), sec. 2.3 (block scale = block max / 6), sec. 3.2 (the
  *         fake-quant sketch: blocks of 16, amax, divide by 6, clamp, quantise, multiply
- *         back), sec. 4.2 (clamp the scale at the FP8 maximum).
+ *         back; straight-through gradient, clamped in practice), sec. 4.1 (moving-average
+ *         scale), sec. 4.2 (clamp the scale at the FP8 maximum).
  *  [BT]   "Baseten on high-quality NVFP4 quantization" (attain.fans translation):
  *         "Why do we need a scale" (the 16 FP4 values; an FP32 per-tensor scale also
  *         exists), "Block scaling" (16 consecutive values per block), "Why blocks"
@@ -47,7 +48,9 @@
  *    takes the MSE choice;
  *  - Four Over Six's two candidates are the bytes nearest amax_b / (6 S) and amax_b / (4 S);
  *  - calibration clip value: the k-th smallest |x| (k = ceil(p N)) rounded toward zero to
- *    bf16, from an exact histogram with one bin per bf16 magnitude.
+ *    bf16, from an exact histogram with one bin per bf16 magnitude;
+ *  - straight-through backward: clamp to [-c, c] in fp32; scale moving average
+ *    S = fmaf(m, S, fp32(fp32(1 - m) * S_batch)).
  */
 #include <float.h>
 #include <math.h>
@@ -135,6 +138,27 @@ int oracle_byte_for_divisor(float amax, float S, double k)
         if (a > mid || (a == mid && (b & 1))) ++b; /* ties to the even byte */
     }
     return b == 0 ? 1 : b;
+}
+
+/* Straight-through estimator for fake-quant training ([QAD] sec. 3.2: the forward pass goes
+ * through the quantiser, the backward pass hands the gradient straight back; in practice
+ * the gradient is clamped to a reasonable range; sec. 4.1: the scale is smoothed with a
+ * moving average, momentum about 0.9). Readings: the backward clamps each gradient value to
+ * [-c, c] (c = +inf: identity), in fp32 after widening, with bf16 output rounded to nearest
+ * even; the moving average is kept on the per-tensor fp32 scale S as
+ * S = fmaf(m, S, fp32(fp32(1 - m) * S_batch)). */
+float oracle_ste_clamp(float g, float c)
+{
+    if (g > c) return c;
+    if (g < -c) return -c;
+    return g;
+}
+
+float oracle_scale_ema(float S_prev, float S_batch, float m)
+{
+    float a = 1.0f - m;
+    float b = a * S_batch;
+    return fmaf(m, S_prev, b);
 }
 
 /* Static activation calibration ([BT] "Calibration": feed representative inputs, record the

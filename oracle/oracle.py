@@ -67,6 +67,10 @@ def lib():
         L.oracle_block_sq_error.argtypes = [P, ctypes.c_int, f32]
         L.oracle_scales_mse.restype = None
         L.oracle_scales_mse.argtypes = [P, i64, i64, f32, P, P]
+        L.oracle_ste_clamp.restype = f32
+        L.oracle_ste_clamp.argtypes = [f32, f32]
+        L.oracle_scale_ema.restype = f32
+        L.oracle_scale_ema.argtypes = [f32, f32, f32]
         L.oracle_calib_histogram.restype = None
         L.oracle_calib_histogram.argtypes = [P, i64, P]
         L.oracle_calib_scale.restype = f32
@@ -125,6 +129,21 @@ def bf16_rne_array(y: np.ndarray) -> np.ndarray:
 def tensor_scale(x) -> np.float32:
     a = _f32(x)
     return np.float32(lib().oracle_tensor_scale(_p(a), a.size))
+
+
+def ste_backward(grad, c: float) -> np.ndarray:
+    """Straight-through gradient of fake-quant, clamped to [-c, c] (fp32 result)."""
+    g = _f32(grad)
+    f = lib().oracle_ste_clamp
+    cf = float(np.float32(c))
+    return np.array([f(float(v), cf) for v in g.ravel()], dtype=np.float32).reshape(g.shape)
+
+
+def scale_ema(S_prev, S_batch, m: float) -> np.ndarray:
+    a, b = np.atleast_1d(_f32(S_prev)), np.atleast_1d(_f32(S_batch))
+    f = lib().oracle_scale_ema
+    return np.array([f(float(x), float(y), float(np.float32(m))) for x, y in zip(a, b)],
+                    dtype=np.float32)
 
 
 CALIB_BINS = 32768
