@@ -38,6 +38,7 @@ MSE_OPS_PER_EVAL = 5           # compare/select x3, subtract, fma per element x 
 FQ_BYTES_PER_ELEM = 2 + 2 + 0.5 + 1 / 16   # read bf16, write bf16 + packed code + 1/16 byte
 FQ_SETS = 4                    # activation batches fake-quantised per step
 CALIB_FRACTION = 0.9999        # activation clip value: this fraction of calibration values
+STE_CLIP = 8.0               # gradient clamp of the straight-through backward
 
 
 def _sha_of(paths):
@@ -114,6 +115,12 @@ def main():
     hist2 = torch.zeros(nvfp4.CALIB_BINS, dtype=torch.int64, device=dev)
     S2c = torch.empty(1, dtype=torch.float32, device=dev)
 
+    # training support: the straight-through backward of the activation's fake-quant
+    # (gradient clamped to +-CLIP) and the moving-average update of its tensor scale
+    g2 = a2s[1]                                            # stands in for dL/dy
+    gx2 = torch.empty_like(g2)
+    S2run = S2.clone()
+
     w3 = synth.mlp_weight(0).to(dev)                       # [12288, 4096]
     r3, c3 = w3.shape
     S3 = torch.empty(1, dtype=torch.float32, device=dev)
@@ -172,6 +179,10 @@ def main():
                                        "calibration histogram"),
                                     ok(L.nvfp4_calib_scale(P(hist2), ctypes.c_double(CALIB_FRACTION),
                                                            P(S2c), sptr), "calibration scale")))
+        stage("ste_act", lambda: (ok(L.nvfp4_ste_backward(P(g2), BF16, r2 * c2, ctypes.c_float(STE_CLIP),
+                                                          P(gx2), sptr), "ste backward"),
+                                  ok(L.nvfp4_scale_ema(P(S2run), P(S2), 1, ctypes.c_float(0.9), sptr),
+                                     "scale ema")))
         stage("scale_mlp", lambda: ok(L.nvfp4_global_scale(P(w3), BF16, 1, r3 * c3, P(S3), sptr), "scale"))
         stage("mse_mlp", lambda: ok(L.nvfp4_scale_search_mse(
             P(w3), BF16, 1, r3, c3, P(S3), P(sc3), None, sptr), "mse"))
@@ -241,6 +252,7 @@ def main():
     mse_evals = r3 * (c3 // 16) * 126 * 16
     fos_bytes = r3 * c3 * 2 + r3 * (c3 // 16)
     cal_bytes = r2 * c2 * 2
+    ste_bytes = r2 * c2 * 2 * 2
     h4_bytes = t4 * c4 * 2
     h5_bytes = t5 * topk * c5 * 2
 
@@ -258,6 +270,7 @@ def main():
         "mse_mlp": roof("alu", mse_evals * MSE_OPS_PER_EVAL / (ms["mse_mlp"] * 1e-3) / 1e12,
                         round(VALU_LANE_TOPS, 2), "TOP/s"),
         "calib_act": roof("hbm", cal_bytes / (ms["calib_act"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "ste_act": roof("hbm", ste_bytes / (ms["ste_act"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "four_over_six_mlp": roof("hbm", fos_bytes / (ms["four_over_six_mlp"] * 1e-3) / 1e9,
                                   HBM_PEAK_GBS, "GB/s"),
         "hessian_proj": roof("hbm", h4_bytes / (ms["hessian_proj"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
@@ -283,7 +296,8 @@ def main():
         "data": "synthetic (seeded generators; no datasets or checkpoints)",
         "config": {
             "workload": "activation fake-quant bf16 8192x4096, max scaling (headline); per step "
-                        "also the activation's calibration histogram and clip scale, MSE and "
+                        "also the activation's calibration histogram and clip scale, its "
+                        "straight-through backward and moving-average scale, MSE and "
                         "Four Over Six on bf16 12288x4096, block Hessian of "
                         "131072x4096 + Local-Hessian on 4096x4096, MoE 128 experts 512x2048 with "
                         "65536 tokens top-8",

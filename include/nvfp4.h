@@ -127,6 +127,23 @@ NVFP4_API int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, in
  *    nvfp4_global_scale (1 for an empty or all-zero histogram). fraction must lie in
  *    (0, 1], else NVFP4_ERR_ARG.
  */
+/*
+ * Fake-quant training support ([QAD] sec. 3.2: forward through the quantiser, gradient
+ * handed straight back -- a straight-through estimator -- and clamped to a reasonable range
+ * in practice; sec. 4.1: a moving-average scale, momentum about 0.9).
+ *  - nvfp4_ste_backward: grad_out = clamp(grad, -clip, clip) elementwise, computed in fp32
+ *    (bf16 results rounded to nearest even); clip = +inf gives the plain straight-through
+ *    gradient; clip must be > 0 (else NVFP4_ERR_ARG). n % 8 == 0, 16-byte aligned; grad_out
+ *    may equal grad.
+ *  - nvfp4_scale_ema: for each of batch entries, S = fmaf(m, S, fp32(fp32(1 - m) *
+ *    S_batch)) (reading: the moving average is kept on the per-tensor fp32 scale);
+ *    momentum in [0, 1], else NVFP4_ERR_ARG.
+ */
+NVFP4_API int nvfp4_ste_backward(const void *grad, int dtype, int64_t n, float clip,
+                       void *grad_out, void *stream);
+NVFP4_API int nvfp4_scale_ema(float *S, const float *S_batch, int64_t batch, float momentum,
+                    void *stream);
+
 #define NVFP4_CALIB_BINS 32768
 NVFP4_API int nvfp4_calib_histogram(const void *x, int dtype, int64_t n, uint64_t *hist,
                           void *stream);

@@ -99,6 +99,27 @@ int nvfp4_scale_search_four_over_six(const void *w, int dtype, int64_t batch, in
   return launch_four_over_six(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
 }
 
+int nvfp4_ste_backward(const void *grad, int dtype, int64_t n, float clip, void *grad_out,
+                       void *stream) {
+  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+  if (n < 0 || (n % 8) != 0) return NVFP4_ERR_SHAPE;
+  if (!(clip > 0.0f)) return NVFP4_ERR_ARG;  // also rejects NaN
+  if (n == 0) return NVFP4_OK;
+  if (!grad || !grad_out) return NVFP4_ERR_NULL;
+  if (!aligned(grad, 16) || !aligned(grad_out, 16)) return NVFP4_ERR_ALIGN;
+  return launch_ste_backward(grad, dtype, n, clip, grad_out, as_stream(stream));
+}
+
+int nvfp4_scale_ema(float *S, const float *S_batch, int64_t batch, float momentum,
+                    void *stream) {
+  if (batch < 0) return NVFP4_ERR_SHAPE;
+  if (!(momentum >= 0.0f && momentum <= 1.0f)) return NVFP4_ERR_ARG;
+  if (batch == 0) return NVFP4_OK;
+  if (!S || !S_batch) return NVFP4_ERR_NULL;
+  if (!aligned(S, 4) || !aligned(S_batch, 4)) return NVFP4_ERR_ALIGN;
+  return launch_scale_ema(S, S_batch, batch, momentum, as_stream(stream));
+}
+
 int nvfp4_calib_histogram(const void *x, int dtype, int64_t n, uint64_t *hist, void *stream) {
   if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
   if (n < 0 || (n % 8) != 0) return NVFP4_ERR_SHAPE;

@@ -17,6 +17,9 @@ int launch_quant(const void *x, int dtype, int64_t batch, int64_t rows, int64_t 
                  void *y, hipStream_t st);
 int launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *S, int64_t batch,
                    int64_t rows, int64_t cols, void *y, int out_dtype, hipStream_t st);
+int launch_ste_backward(const void *g, int dtype, int64_t n, float clip, void *out,
+                        hipStream_t st);
+int launch_scale_ema(float *S, const float *S_batch, int64_t batch, float m, hipStream_t st);
 int launch_calib_histogram(const void *x, int dtype, int64_t n, unsigned long long *hist,
                            hipStream_t st);
 int launch_calib_scale(const unsigned long long *hist, double fraction, float *S, hipStream_t st);

@@ -39,6 +39,8 @@ _SIGS = {
     "nvfp4_scale_search_mse": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_scale_search_four_over_six": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_calib_histogram": (_I, [_P, _I, _I64, _P, _P]),
+    "nvfp4_ste_backward": (_I, [_P, _I, _I64, ctypes.c_float, _P, _P]),
+    "nvfp4_scale_ema": (_I, [_P, _P, _I64, ctypes.c_float, _P]),
     "nvfp4_calib_scale": (_I, [_P, ctypes.c_double, _P, _P]),
     "nvfp4_block_hessian_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
     "nvfp4_block_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P, _SZ, _P]),
@@ -163,6 +165,25 @@ def scale_search_four_over_six(w: torch.Tensor, S: torch.Tensor, return_obj: boo
                                                   _ptr(obj), _stream()),
            "nvfp4_scale_search_four_over_six")
     return (sc, obj) if return_obj else sc
+
+
+def ste_backward(grad: torch.Tensor, clip: float = float("inf"),
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """Straight-through gradient of fake-quant: grad clamped to [-clip, clip]."""
+    _need(grad, "grad")
+    out = torch.empty_like(grad) if out is None else out
+    _check(lib().nvfp4_ste_backward(_ptr(grad), _dt(grad), grad.numel(), float(clip), _ptr(out),
+                                    _stream()), "nvfp4_ste_backward")
+    return out
+
+
+def scale_ema(S: torch.Tensor, S_batch: torch.Tensor, momentum: float) -> torch.Tensor:
+    """In place: S = momentum * S + (1 - momentum) * S_batch (fixed fp32 order)."""
+    _need(S, "S")
+    _need(S_batch, "S_batch")
+    _check(lib().nvfp4_scale_ema(_ptr(S), _ptr(S_batch), S.numel(), float(momentum), _stream()),
+           "nvfp4_scale_ema")
+    return S
 
 
 CALIB_BINS = 32768

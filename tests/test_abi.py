@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = nvfp4.declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
     assert L.nvfp4_version() == 100
@@ -75,6 +75,13 @@ def test_each_entry_point_validates(L):
     assert L.nvfp4_calib_scale(P(FAKE), ctypes.c_double(0.0), P(FAKE), None) == EARG
     assert L.nvfp4_calib_scale(P(FAKE), ctypes.c_double(1.5), P(FAKE), None) == EARG
     assert L.nvfp4_calib_scale(None, ctypes.c_double(0.5), P(FAKE), None) == ENULL
+    assert L.nvfp4_ste_backward(P(FAKE), 1, 16, ctypes.c_float(0.0), P(FAKE), None) == EARG
+    assert L.nvfp4_ste_backward(P(FAKE), 1, 16, ctypes.c_float(float("nan")), P(FAKE), None) == EARG
+    assert L.nvfp4_ste_backward(P(FAKE), 1, 12, ctypes.c_float(1.0), P(FAKE), None) == ESHAPE
+    assert L.nvfp4_ste_backward(P(FAKE), 1, 16, ctypes.c_float(1.0), P(FAKE + 8), None) == EALIGN
+    assert L.nvfp4_ste_backward(None, 1, 0, ctypes.c_float(1.0), None, None) == OK
+    assert L.nvfp4_scale_ema(P(FAKE), P(FAKE), 1, ctypes.c_float(1.5), None) == EARG
+    assert L.nvfp4_scale_ema(None, P(FAKE), 1, ctypes.c_float(0.9), None) == ENULL
     f46 = L.nvfp4_scale_search_four_over_six
     assert f46(P(FAKE), 1, 1, 2, 24, P(FAKE), P(FAKE), None, None) == ESHAPE
     assert f46(P(FAKE), 4, 1, 2, 16, P(FAKE), P(FAKE), None, None) == EDTYPE

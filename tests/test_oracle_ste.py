@@ -59,3 +59,9 @@ def test_ema_fixed_point_and_extremes(orc):
     assert np.array_equal(orc.scale_ema(S, S, 0.5), S)
     assert np.array_equal(orc.scale_ema(S, S * 4, 0.0), S * 4)   # momentum 0: the new value
     assert np.array_equal(orc.scale_ema(S, S * 4, 1.0), S)       # momentum 1: frozen
+
+
+def test_clamp_passes_nan_and_clamps_infinities(orc):
+    g = np.array([np.nan, np.inf, -np.inf], np.float32)
+    out = orc.ste_backward(g, 2.0)
+    assert np.isnan(out[0]) and out[1] == 2.0 and out[2] == -2.0
