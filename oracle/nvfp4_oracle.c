@@ -50,7 +50,10 @@
  *  - calibration clip value: the k-th smallest |x| (k = ceil(p N)) rounded toward zero to
  *    bf16, from an exact histogram with one bin per bf16 magnitude;
  *  - straight-through backward: clamp to [-c, c] in fp32; scale moving average
- *    S = fmaf(m, S, fp32(fp32(1 - m) * S_batch)).
+ *    S = fmaf(m, S, fp32(fp32(1 - m) * S_batch));
+ *  - GPTQ rounding at fixed block scales (the page names GPTQ; its steps follow the
+ *    published algorithm, Frantar et al. 2022): damping lambda = damp * mean(diag H),
+ *    columns in natural order, every decision on the double-precision updated weight.
  */
 #include <float.h>
 #include <math.h>
@@ -466,4 +469,142 @@ int oracle_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk,
         }
     free(fill);
     return 0;
+}
+
+/* ------------------------------------------------------------------ GPTQ ([LH] "Change the
+ * objective" gives the layer-output error tr(dW X X^T dW^T); the closing paragraphs of the
+ * same page say GPTQ changes the rounding where Local-Hessian changes the scale, and that
+ * the two can be combined. GPTQ itself is Frantar et al., 2022.) */
+
+/* Full Gram matrix H[i][j] = sum_t x[t][i] x[t][j], double, ascending t (all of X X^T; the
+ * Local-Hessian search uses only its 16x16 diagonal blocks). */
+void oracle_full_hessian(const float *X, int64_t tokens, int64_t cols, double *H)
+{
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < cols; ++i)
+        for (int64_t j = i; j < cols; ++j) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < tokens; ++t)
+                acc += (double)X[t * cols + i] * (double)X[t * cols + j];
+            H[i * cols + j] = acc;
+            H[j * cols + i] = acc;
+        }
+}
+
+/* E2M1 code of a double value: the element rule above (round half to even on the exact
+ * ratio |v| / (s S), saturating at 6), applied to GPTQ's updated weights, which are not fp32.
+ * The products mid * s * S are exact in double, so the comparisons are exact. */
+int oracle_e2m1_code_d(double v, int byte, float S)
+{
+    if (byte == 0) return 0;
+    double av = fabs(v);
+    double sS = oracle_e4m3_value(byte) * (double)S;
+    int k = 0;
+    while (k < 7 && E2M1_MAG[k + 1] * sS <= av) ++k;
+    if (k < 7) {
+        double mid = 0.5 * (E2M1_MAG[k] + E2M1_MAG[k + 1]) * sS;
+        if (av > mid || (av == mid && (k & 1))) ++k;
+    }
+    return (v < 0.0 && k > 0) ? (8 | k) : k;
+}
+
+/* Lower Cholesky factor in place (A = L L^T, lower triangle read); returns 0, or 1 + the
+ * first column whose pivot is not positive. */
+static int64_t chol_lower(double *A, int64_t n)
+{
+    for (int64_t j = 0; j < n; ++j) {
+        double d = A[j * n + j];
+        for (int64_t k = 0; k < j; ++k) d -= A[j * n + k] * A[j * n + k];
+        if (!(d > 0.0)) return 1 + j;
+        double ljj = sqrt(d);
+        A[j * n + j] = ljj;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = j + 1; i < n; ++i) {
+            double s = A[i * n + j];
+            for (int64_t k = 0; k < j; ++k) s -= A[i * n + k] * A[j * n + k];
+            A[i * n + j] = s / ljj;
+        }
+    }
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = i + 1; j < n; ++j) A[i * n + j] = 0.0;
+    return 0;
+}
+
+/* GPTQ's factor: U upper triangular with U^T U = (H + lambda I)^{-1}, computed the way the
+ * algorithm states it: Cholesky of the damped H, its inverse, then the upper Cholesky
+ * factor of that inverse. lambda = damp * (sum_j H_jj, index order) / n; an all-zero
+ * diagonal (all-zero inputs) gives H + lambda I := I, so GPTQ reduces to plain rounding.
+ * H is read from its lower triangle. Returns 0, or 1 + a failing pivot's column. */
+int64_t oracle_gptq_factor(const double *H, int64_t n, double damp, double *U)
+{
+    double *L = (double *)malloc(sizeof(double) * n * n);
+    double *Li = (double *)malloc(sizeof(double) * n * n); /* row c = column c of L^{-1} */
+    if (!L || !Li) { free(L); free(Li); return -1; }
+    double tr = 0.0;
+    for (int64_t j = 0; j < n; ++j) tr += H[j * n + j];
+    double lambda = damp * (tr / (double)n);
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j <= i; ++j) {
+            double h = tr == 0.0 ? (i == j ? 1.0 : 0.0) : H[i * n + j];
+            L[i * n + j] = (i == j && tr != 0.0) ? h + lambda : h;
+        }
+    int64_t rc = chol_lower(L, n);
+    if (rc) { free(L); free(Li); return rc; }
+    /* columns of L^{-1} by forward substitution: y_c = 1 / L_cc, y_i = -(sum_k L_ik y_k) / L_ii */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t c = 0; c < n; ++c) {
+        double *y = Li + c * n;
+        for (int64_t i = 0; i < c; ++i) y[i] = 0.0;
+        y[c] = 1.0 / L[c * n + c];
+        for (int64_t i = c + 1; i < n; ++i) {
+            double s = 0.0;
+            for (int64_t k = c; k < i; ++k) s += L[i * n + k] * y[k];
+            y[i] = -s / L[i * n + i];
+        }
+    }
+    /* Hinv = L^{-T} L^{-1}: Hinv_ij = sum_{k >= max(i,j)} (L^{-1})_ki (L^{-1})_kj, lower part */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j <= i; ++j) {
+            double s = 0.0;
+            for (int64_t k = i; k < n; ++k) s += Li[i * n + k] * Li[j * n + k];
+            L[i * n + j] = s;
+        }
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = i + 1; j < n; ++j) L[i * n + j] = 0.0;
+    rc = chol_lower(L, n); /* Hinv = L2 L2^T, so U = L2^T */
+    if (!rc)
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t j = 0; j < n; ++j) U[i * n + j] = L[j * n + i];
+    free(L);
+    free(Li);
+    return rc;
+}
+
+/* GPTQ's column loop for each row (rows are independent): v = w; for j = 0..n-1 the code
+ * of v_j is taken at the block's byte and S, e = (v_j - q_j) / U_jj with q_j the exact
+ * dequantised value, and v_k -= e U_jk for every k > j. codes use the packed layout;
+ * vout (optional) receives each v_j as it was rounded. */
+void oracle_gptq_rows(const float *w, int64_t rows, int64_t n, float S, const uint8_t *scales,
+                      const double *U, uint8_t *codes, double *vout)
+{
+    int64_t nb = n / 16;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        double *v = (double *)malloc(sizeof(double) * n);
+        for (int64_t k = 0; k < n; ++k) v[k] = (double)w[r * n + k];
+        for (int64_t j = 0; j < n; ++j) {
+            int byte = scales[r * nb + j / 16];
+            int code = oracle_e2m1_code_d(v[j], byte, S);
+            if (vout) vout[r * n + j] = v[j];
+            double q = E2M1_MAG[code & 7] * oracle_e4m3_value(byte) * (double)S; /* exact */
+            if (code & 8) q = -q;
+            double e = (v[j] - q) / U[j * n + j];
+            for (int64_t k = j + 1; k < n; ++k) v[k] -= e * U[j * n + k];
+            uint8_t *cb = codes + r * (n / 2) + j / 2;
+            if (j & 1) *cb = (uint8_t)((*cb & 0x0F) | (code << 4));
+            else *cb = (uint8_t)code;
+        }
+        free(v);
+    }
 }

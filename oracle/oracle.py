@@ -87,6 +87,14 @@ def lib():
         L.oracle_scales_local_hessian.argtypes = [P, i64, i64, f32, P, P, P]
         L.oracle_route_groups.restype = ctypes.c_int
         L.oracle_route_groups.argtypes = [P, i64, i64, i64, P, P]
+        L.oracle_full_hessian.restype = None
+        L.oracle_full_hessian.argtypes = [P, i64, i64, P]
+        L.oracle_e2m1_code_d.restype = ctypes.c_int
+        L.oracle_e2m1_code_d.argtypes = [ctypes.c_double, ctypes.c_int, f32]
+        L.oracle_gptq_factor.restype = i64
+        L.oracle_gptq_factor.argtypes = [P, i64, ctypes.c_double, P]
+        L.oracle_gptq_rows.restype = None
+        L.oracle_gptq_rows.argtypes = [P, i64, i64, f32, P, P, P, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         _lib = L
@@ -276,3 +284,42 @@ def route_groups(expert_ids, experts: int):
     if rc != 0:
         raise ValueError("expert id out of range")
     return offsets, tok
+
+
+def full_hessian(X) -> np.ndarray:
+    """fp64 H [cols, cols] = X^T X of X [tokens, cols]."""
+    a = _f32(X)
+    tokens, cols = a.shape
+    H = np.empty((cols, cols), dtype=np.float64)
+    lib().oracle_full_hessian(_p(a), tokens, cols, _p(H))
+    return H
+
+
+def e2m1_code_d(v: float, byte: int, S: float) -> int:
+    return lib().oracle_e2m1_code_d(float(v), int(byte), float(np.float32(S)))
+
+
+def gptq_factor(H, damp: float = 0.01) -> np.ndarray:
+    """U (upper, fp64) with U^T U = (H + damp * mean(diag H) I)^{-1}; H's lower triangle."""
+    h = np.ascontiguousarray(H, dtype=np.float64)
+    n = h.shape[0]
+    U = np.empty((n, n), dtype=np.float64)
+    rc = lib().oracle_gptq_factor(_p(h), n, float(damp), _p(U))
+    if rc != 0:
+        raise ValueError(f"damped H is not positive definite (column {rc - 1})")
+    return U
+
+
+def gptq(w, S, scales, H=None, damp: float = 0.01, U=None, return_v: bool = False):
+    """GPTQ codes [rows, cols/2] of w at the given block bytes and S (and the values each
+    column was rounded from, if asked). Pass U from gptq_factor to reuse it."""
+    a = _f32(w)
+    rows, cols = a.shape
+    if U is None:
+        U = gptq_factor(H, damp)
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    codes = np.empty((rows, cols // 2), dtype=np.uint8)
+    v = np.empty((rows, cols), dtype=np.float64) if return_v else None
+    lib().oracle_gptq_rows(_p(a), rows, cols, float(np.float32(S)), _p(sc),
+                           _p(np.ascontiguousarray(U)), _p(codes), _p(v) if return_v else None)
+    return (codes, v) if return_v else codes
