@@ -227,6 +227,50 @@ NVFP4_API int nvfp4_route_groups(const int32_t *expert_ids, int64_t tokens, int6
                        int64_t experts, int32_t *offsets, int32_t *token_ids,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Full Gram matrix H = X^T X of a layer input ([LH] "Change the objective": the output
+ * error is tr(dW X X^T dW^T); Local-Hessian needs only its 16x16 diagonal blocks, GPTQ
+ * rounding -- which the same page says combines with Local-Hessian -- needs all of it).
+ * x: [tokens][cols] bf16 or fp32 (bf16 products are exact, accumulation is fp32);
+ * cols % 16 == 0. H: [cols][cols] fp32 (out), exactly symmetric; accumulate != 0 adds to
+ * the existing H (streaming over calibration batches). Partial sums per token chunk are
+ * added in a fixed order, so results are bitwise reproducible.
+ * workspace_bytes must be >= nvfp4_full_hessian_workspace_size().
+ */
+NVFP4_API size_t nvfp4_full_hessian_workspace_size(int64_t tokens, int64_t cols);
+NVFP4_API int nvfp4_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, float *H,
+                                 int accumulate, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
+ * GPTQ's factor (GPTQ, Frantar et al. 2022, as combined with Local-Hessian in [LH]'s closing
+ * paragraphs): U upper triangular, positive diagonal, with U^T U = (H + lambda I)^-1, where
+ * lambda = damp * (sum of diag H, in index order) / cols. A zero diagonal sum (all-zero
+ * inputs) gives H + lambda I := I. Computed in double precision. Only the lower triangle of
+ * H [cols][cols] (fp32) is read; U: [cols][cols] double (out, zeros below the diagonal).
+ * status (nullable, device int32): 0, or non-zero if H + lambda I is not positive definite
+ * (U is then not usable). damp >= 0 and finite, else NVFP4_ERR_ARG.
+ * workspace_bytes must be >= nvfp4_gptq_factor_workspace_size().
+ */
+NVFP4_API size_t nvfp4_gptq_factor_workspace_size(int64_t cols);
+NVFP4_API int nvfp4_gptq_factor(const float *H, int64_t cols, double damp, double *U,
+                                int32_t *status, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
+ * GPTQ rounding at fixed block scales: columns of w [rows][cols] in order; column j of each
+ * row is rounded (the element rule of nvfp4_quantize, on the double-precision updated
+ * value, exact comparisons) at its block byte scales[row][j/16] and S[0], then
+ * e = (v_j - q_j) / U_jj and v_k -= e U_jk for k > j. The block bytes are an input (for
+ * example from nvfp4_scale_search_local_hessian): GPTQ changes rounding, not scale.
+ * codes: [rows][cols/2] packed (out, 8-byte aligned). U from nvfp4_gptq_factor.
+ * workspace_bytes must be >= nvfp4_gptq_workspace_size().
+ */
+NVFP4_API size_t nvfp4_gptq_workspace_size(int64_t rows, int64_t cols);
+NVFP4_API int nvfp4_gptq(const void *w, int dtype, int64_t rows, int64_t cols, const float *S,
+                         const uint8_t *scales, const double *U, uint8_t *codes,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

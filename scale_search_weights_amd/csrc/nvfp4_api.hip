@@ -242,4 +242,62 @@ int nvfp4_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk, 
                              as_stream(stream));
 }
 
+size_t nvfp4_full_hessian_workspace_size(int64_t tokens, int64_t cols) {
+  if (tokens < 0 || cols <= 0) return 0;
+  return gram_workspace_size(tokens, cols);
+}
+
+int nvfp4_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, float *H,
+                       int accumulate, void *workspace, size_t workspace_bytes, void *stream) {
+  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+  if (tokens < 0 || cols < 0 || (cols % 16) != 0) return NVFP4_ERR_SHAPE;
+  int64_t t1, t2, h1;
+  if (!mul_ok(tokens, cols, &t1) || !mul_ok(t1, 4, &t2) || !mul_ok(cols, cols, &h1))
+    return NVFP4_ERR_SHAPE;
+  if (cols > 65536 || tokens > INT32_MAX) return NVFP4_ERR_SHAPE;
+  if (cols == 0) return NVFP4_OK;
+  if (!H || (tokens > 0 && !x)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(H, 4)) return NVFP4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < gram_workspace_size(tokens, cols)) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  return launch_full_hessian(x, dtype, tokens, cols, H, accumulate, workspace, as_stream(stream));
+}
+
+size_t nvfp4_gptq_factor_workspace_size(int64_t cols) {
+  if (cols <= 0 || cols > 65536) return 0;
+  return gptq_factor_workspace_size(cols);
+}
+
+int nvfp4_gptq_factor(const float *H, int64_t cols, double damp, double *U, int32_t *status,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (cols < 0 || (cols % 16) != 0 || cols > 65536) return NVFP4_ERR_SHAPE;
+  if (!(damp >= 0.0) || damp > 1e300) return NVFP4_ERR_ARG;  // also rejects NaN and inf
+  if (cols == 0) return NVFP4_OK;
+  if (!H || !U) return NVFP4_ERR_NULL;
+  if (!aligned(H, 4) || !aligned(U, 16) || !aligned(status, 4)) return NVFP4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < gptq_factor_workspace_size(cols)) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  return launch_gptq_factor(H, cols, damp, U, status, workspace, as_stream(stream));
+}
+
+size_t nvfp4_gptq_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return 0;
+  return gptq_rows_workspace_size(rows, cols);
+}
+
+int nvfp4_gptq(const void *w, int dtype, int64_t rows, int64_t cols, const float *S,
+               const uint8_t *scales, const double *U, uint8_t *codes, void *workspace,
+               size_t workspace_bytes, void *stream) {
+  bool empty = false;
+  int rc = check_tensor(dtype, 1, rows, cols, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (cols > 65536 || (rows + 63) / 64 > INT32_MAX) return NVFP4_ERR_SHAPE;
+  if (!w || !S || !scales || !U || !codes) return NVFP4_ERR_NULL;
+  if (!aligned(w, 4) || !aligned(S, 4) || !aligned(U, 16) || !aligned(codes, 8))
+    return NVFP4_ERR_ALIGN;
+  if (!workspace || workspace_bytes < gptq_rows_workspace_size(rows, cols)) return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  return launch_gptq_rows(w, dtype, rows, cols, S, scales, U, codes, workspace, as_stream(stream));
+}
+
 }  // extern "C"

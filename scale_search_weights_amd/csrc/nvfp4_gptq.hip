@@ -1,0 +1,531 @@
+// GPTQ rounding at fixed NVFP4 block scales, in double precision.
+//
+// [LH] (closing paragraphs): Local-Hessian picks the block scale, GPTQ picks the rounding,
+// and the two combine. GPTQ (Frantar et al., 2022) quantises the columns of W in order and,
+// after each column, moves the columns not yet quantised so as to cancel its rounding error
+// under the layer's Gram matrix H = X^T X: with U upper triangular and U^T U = (H + lambda I)^-1,
+// e_j = (v_j - q_j) / U_jj and v_k -= e_j U_jk for k > j.
+//
+// MI355X runs fp64 FMA and fp64 MFMA at 78.6 TFLOP/s, so the whole method stays in double:
+// the codes then depend on summation order only for values within ~1e-12 (relative) of a
+// rounding midpoint. Two entry points:
+//  * factor: lambda = damp * mean(diag H) (index-order sum); U from one Cholesky
+//    factorisation and one triangular inverse, using the reversal J (J_ij = [i + j = n-1]):
+//    if J (H + lambda I) J = L L^T then H + lambda I = R R^T with R = J L J upper, and
+//    U = R^-1 = J L^-1 J. Blocked right-looking Cholesky (64 x 64 blocks: one workgroup
+//    factors the diagonal block in LDS, one thread per row solves the panel, fp64 MFMA
+//    updates the trailing matrix), then a bottom-up recursive inverse
+//    [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] (two fp64 MFMA products per level).
+//  * rows: the column loop in blocks of 64 columns. In a block, four lanes share a row,
+//    each holding the 16 values of one scale block in registers; for every column the
+//    owning lane rounds, forms e and broadcasts it to its quad (DPP), and all four update
+//    their values with the block's row of U from LDS. Between blocks, an fp64 MFMA product
+//    V[:, later] -= E_block U[block, later] applies the block's errors (lazy batch update).
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+typedef double gq_v4d __attribute__((ext_vector_type(4)));
+
+constexpr int DB = 64;       // block edge
+constexpr int DP = DB + 1;   // LDS pitch of a K-major tile (doubles)
+
+static inline int64_t pad64(int64_t n) { return (n + DB - 1) / DB * DB; }
+
+size_t gptq_factor_workspace_size(int64_t n) {
+  const int64_t np = pad64(n);
+  return 256 + 2 * sizeof(double) * (size_t)np * (size_t)np;
+}
+
+size_t gptq_rows_workspace_size(int64_t rows, int64_t n) {
+  const int64_t rp = pad64(rows), np = pad64(n);
+  return sizeof(double) * ((size_t)rp * (size_t)np + (size_t)rp * DB);
+}
+
+// ------------------------------------------------------------------ fp64 64x64 tiles
+// LDS tiles are K-major: T[k * DP + m]. A workgroup of 256 threads (4 waves) owns one
+// 64 x 64 output tile; wave w computes the 32 x 32 quarter (w >> 1, w & 1) as 2 x 2
+// v_mfma_f64_16x16x4_f64 tiles (A: lane l holds row l & 15 at k = l >> 4; B likewise for
+// columns; D: lane l, register r holds row (l >> 4) + 4 r of column l & 15, unlike the
+// fp32 16x16x4 form, whose rows are 4 (l >> 4) + r).
+
+// element (m, k) at src[m * ld + k] (k contiguous), zero outside m < mlim, k < klim
+__device__ __forceinline__ void dload_mk(double *T, const double *src, int64_t ld, int mlim,
+                                         int klim) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + t;
+    const int m = idx >> 5, k = (idx & 31) * 2;
+    double2 v = make_double2(0.0, 0.0);
+    if (m < mlim && k < klim) v = *reinterpret_cast<const double2 *>(src + (int64_t)m * ld + k);
+    T[k * DP + m] = v.x;
+    T[(k + 1) * DP + m] = v.y;
+  }
+}
+
+// element (k, n) at src[k * ld + n] (n contiguous), zero outside k < klim, n < nlim
+__device__ __forceinline__ void dload_kn(double *T, const double *src, int64_t ld, int klim,
+                                         int nlim) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + t;
+    const int k = idx >> 5, n = (idx & 31) * 2;
+    double2 v = make_double2(0.0, 0.0);
+    if (k < klim && n < nlim) v = *reinterpret_cast<const double2 *>(src + (int64_t)k * ld + n);
+    T[k * DP + n] = v.x;
+    T[k * DP + n + 1] = v.y;
+  }
+}
+
+struct DAcc {
+  gq_v4d c[2][2];
+};
+
+__device__ __forceinline__ void dacc_zero(DAcc &a) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) a.c[i][j] = (gq_v4d){0.0, 0.0, 0.0, 0.0};
+}
+
+__device__ __forceinline__ void dmma(DAcc &acc, const double *LA, const double *LB) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll 4
+  for (int kk = 0; kk < DB / 4; ++kk) {
+    const int kr = kk * 4 + (lane >> 4);
+    double a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = LA[kr * DP + wr * 32 + i * 16 + (lane & 15)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = LB[kr * DP + wc * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+// visit the tile elements a thread owns: f(row, col, value)
+template <class F>
+__device__ __forceinline__ void dacc_each(const DAcc &acc, F f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 32 + j * 16 + (lane & 15), acc.c[i][j][r]);
+}
+
+// ------------------------------------------------------------------ factor
+// hdr[0] = lambda, hdr[1] = 1 if diag(H) sums to zero (then H + lambda I := I)
+__global__ void __launch_bounds__(256)
+    k_gptq_lambda(const float *__restrict__ H, int64_t n, double damp, double *__restrict__ hdr,
+                  int32_t *__restrict__ status) {
+  __shared__ double dg[4096];
+  double tr = 0.0;
+  for (int64_t base = 0; base < n; base += 4096) {
+    const int64_t m = n - base < 4096 ? n - base : 4096;
+    for (int64_t i = threadIdx.x; i < m; i += 256) dg[i] = (double)H[(base + i) * n + base + i];
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int64_t i = 0; i < m; ++i) tr += dg[i];  // index order
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    hdr[0] = damp * (tr / (double)n);
+    hdr[1] = tr == 0.0 ? 1.0 : 0.0;
+    *status = 0;
+  }
+}
+
+// A (np x np) = J (H + lambda I) J, lower triangle from H's lower triangle, identity padding
+__global__ void __launch_bounds__(256)
+    k_gptq_load_h(const float *__restrict__ H, int64_t n, int64_t np,
+                  const double *__restrict__ hdr, double *__restrict__ A) {
+  const double lam = hdr[0];
+  const bool ident = hdr[1] != 0.0;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < np * np;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t i = e / np, j = e % np;
+    double v = 0.0;
+    if (j <= i) {
+      if (i >= n) {
+        v = i == j ? 1.0 : 0.0;
+      } else {
+        const int64_t a = n - 1 - i, b = n - 1 - j;  // a <= b: H[b][a] is in H's lower part
+        v = ident ? (i == j ? 1.0 : 0.0) : (double)H[b * n + a] + (i == j ? lam : 0.0);
+      }
+    }
+    A[e] = v;
+  }
+}
+
+// Cholesky factor of diagonal block k, in place (lower; upper part of the block zeroed)
+__global__ void __launch_bounds__(256)
+    k_chol_diag(double *__restrict__ A, int64_t np, int64_t k, int32_t *__restrict__ status) {
+  __shared__ double D[DB * DP];
+  const int t = threadIdx.x;
+  double *blk = A + k * DB * np + k * DB;
+  for (int e = t; e < DB * DB; e += 256) {
+    const int i = e >> 6, j = e & 63;
+    D[i * DP + j] = j <= i ? blk[i * np + j] : 0.0;
+  }
+  for (int j = 0; j < DB; ++j) {
+    __syncthreads();
+    const double d = D[j * DP + j];
+    if (!(d > 0.0) && t == 0) atomicCAS(status, 0, (int32_t)(1 + k * DB + j));
+    const double ljj = sqrt(d);
+    __syncthreads();
+    if (t > j && t < DB) D[t * DP + j] = D[t * DP + j] / ljj;
+    if (t == 0) D[j * DP + j] = ljj;
+    __syncthreads();
+    const int m = DB - 1 - j;
+    for (int e = t; e < m * m; e += 256) {
+      const int i = j + 1 + e / m, l = j + 1 + e % m;
+      if (l <= i) D[i * DP + l] = fma(-D[i * DP + j], D[l * DP + j], D[i * DP + l]);
+    }
+  }
+  __syncthreads();
+  for (int e = t; e < DB * DB; e += 256) {
+    const int i = e >> 6, j = e & 63;
+    blk[i * np + j] = j <= i ? D[i * DP + j] : 0.0;
+  }
+}
+
+// panel below diagonal block k: each row solves x L_kk^T = a by forward substitution
+__global__ void __launch_bounds__(64)
+    k_chol_panel(double *__restrict__ A, int64_t np, int64_t k) {
+  __shared__ double Lk[DB * DP];
+  const int t = threadIdx.x;
+  const double *dk = A + k * DB * np + k * DB;
+  for (int e = t; e < DB * DB; e += 64) Lk[(e >> 6) * DP + (e & 63)] = dk[(e >> 6) * np + (e & 63)];
+  __syncthreads();
+  const int64_t row = (k + 1 + blockIdx.x) * DB + t;
+  double *ar = A + row * np + k * DB;
+  double a[DB];
+#pragma unroll
+  for (int j = 0; j < DB; j += 2) {
+    const double2 v = *reinterpret_cast<const double2 *>(ar + j);
+    a[j] = v.x;
+    a[j + 1] = v.y;
+  }
+#pragma unroll
+  for (int j = 0; j < DB; ++j) {
+    a[j] = a[j] / Lk[j * DP + j];
+#pragma unroll
+    for (int m = j + 1; m < DB; ++m) a[m] = fma(-a[j], Lk[m * DP + j], a[m]);
+  }
+#pragma unroll
+  for (int j = 0; j < DB; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
+}
+
+// trailing update after step k: A[bi][bj] -= L[bi][k] L[bj][k]^T for k < bj <= bi
+__global__ void __launch_bounds__(256)
+    k_chol_update(double *__restrict__ A, int64_t np, int64_t k) {
+  __shared__ double LA[DB * DP], LB[DB * DP];
+  int64_t e = blockIdx.x, bi = 0;
+  while (e > bi) {  // lower-triangular enumeration: row bi holds bi + 1 blocks
+    e -= bi + 1;
+    ++bi;
+  }
+  const int64_t bj = e;
+  bi += k + 1;
+  const int64_t bjj = bj + k + 1;
+  dload_mk(LA, A + bi * DB * np + k * DB, np, DB, DB);
+  dload_mk(LB, A + bjj * DB * np + k * DB, np, DB, DB);
+  __syncthreads();
+  DAcc acc;
+  dacc_zero(acc);
+  dmma(acc, LA, LB);
+  double *C = A + bi * DB * np + bjj * DB;
+  dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
+}
+
+// inverses of the diagonal blocks: column c of L_bb^-1 by forward substitution
+__global__ void __launch_bounds__(64)
+    k_trtri_diag(const double *__restrict__ A, double *__restrict__ X, int64_t np) {
+  __shared__ double Lb[DB * DP];
+  const int64_t b = blockIdx.x;
+  const int c = threadIdx.x;
+  const double *src = A + b * DB * np + b * DB;
+  for (int e = c; e < DB * DB; e += 64) Lb[(e >> 6) * DP + (e & 63)] = src[(e >> 6) * np + (e & 63)];
+  __syncthreads();
+  double y[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    double s = 0.0;
+#pragma unroll
+    for (int m = 0; m < i; ++m) s = fma(Lb[i * DP + m], y[m], s);  // y[m] = 0 for m < c
+    y[i] = i < c ? 0.0 : (i == c ? 1.0 / Lb[i * DP + i] : -s / Lb[i * DP + i]);
+  }
+  double *dst = X + b * DB * np + b * DB;
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dst[i * np + c] = y[i];
+}
+
+// One level of the recursive inverse. Groups of 2s rows: A-range [a0, a0 + s), C-range
+// [c0, c0 + sc). phase 0: T = L[C][A] X[A][A], stored transposed in X's unused upper part
+// (X[A rows][C cols]); phase 1: X[C][A] = -X[C][C] T.
+__global__ void __launch_bounds__(256)
+    k_trtri_level(const double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
+                  int phase) {
+  __shared__ double LA[DB * DP], LB[DB * DP];
+  const int64_t a0 = (int64_t)blockIdx.x * 2 * s, c0 = a0 + s;
+  const int64_t sc = np - c0 < s ? np - c0 : s;
+  const int64_t nbs = s / DB;
+  const int64_t ib = blockIdx.y / nbs, jb = blockIdx.y % nbs;  // output block (C row, A col)
+  if (ib * DB >= sc) return;
+  const int64_t r0 = c0 + ib * DB, q0 = a0 + jb * DB;  // global row / column of the block
+  DAcc acc;
+  dacc_zero(acc);
+  if (phase == 0) {
+    // sum over A-range blocks kb >= jb: L[r0][kb] X[kb][q0]
+    for (int64_t kb = jb; kb < nbs; ++kb) {
+      const int64_t k0 = a0 + kb * DB;
+      __syncthreads();
+      dload_mk(LA, A + r0 * np + k0, np, DB, DB);
+      dload_kn(LB, X + k0 * np + q0, np, DB, DB);
+      __syncthreads();
+      dmma(acc, LA, LB);
+    }
+    dacc_each(acc, [&](int r, int c, double v) { X[(q0 + c) * np + r0 + r] = v; });
+  } else {
+    // sum over C-range blocks kb <= ib: X[r0][kb] T[kb][q0], T[kb][q0] stored at X[q0][kb]
+    for (int64_t kb = 0; kb <= ib; ++kb) {
+      const int64_t k0 = c0 + kb * DB;
+      __syncthreads();
+      dload_mk(LA, X + r0 * np + k0, np, DB, DB);
+      dload_mk(LB, X + q0 * np + k0, np, DB, DB);
+      __syncthreads();
+      dmma(acc, LA, LB);
+    }
+    dacc_each(acc, [&](int r, int c, double v) { X[(r0 + r) * np + q0 + c] = -v; });
+  }
+}
+
+// U[i][j] = X[n-1-i][n-1-j] for i <= j, zero below the diagonal
+__global__ void __launch_bounds__(256)
+    k_gptq_store_u(const double *__restrict__ X, int64_t n, int64_t np, double *__restrict__ U) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n * n;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t i = e / n, j = e % n;
+    U[e] = i <= j ? X[(n - 1 - i) * np + (n - 1 - j)] : 0.0;
+  }
+}
+
+static unsigned grid_for(int64_t elems) {
+  int64_t g = (elems + 255) / 256;
+  if (g > 65536) g = 65536;
+  return (unsigned)(g > 0 ? g : 1);
+}
+
+int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_t *status,
+                       void *workspace, hipStream_t st) {
+  const int64_t np = pad64(n), nb = np / DB;
+  double *hdr = static_cast<double *>(workspace);
+  int32_t *stat = status ? status : reinterpret_cast<int32_t *>(hdr + 2);
+  double *A = reinterpret_cast<double *>(static_cast<char *>(workspace) + 256);
+  double *X = A + np * np;
+  hipLaunchKernelGGL(k_gptq_lambda, dim3(1), dim3(256), 0, st, H, n, damp, hdr, stat);
+  hipLaunchKernelGGL(k_gptq_load_h, dim3(grid_for(np * np)), dim3(256), 0, st, H, n, np, hdr, A);
+  for (int64_t k = 0; k < nb; ++k) {
+    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, st, A, np, k, stat);
+    const int64_t T = nb - k - 1;
+    if (T > 0) {
+      hipLaunchKernelGGL(k_chol_panel, dim3((unsigned)T), dim3(64), 0, st, A, np, k);
+      hipLaunchKernelGGL(k_chol_update, dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0, st, A,
+                         np, k);
+    }
+  }
+  hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, A, X, np);
+  for (int64_t s = DB; s < np; s *= 2) {
+    const int64_t groups = (np + 2 * s - 1) / (2 * s);
+    int64_t g = groups;
+    if (groups * 2 * s - s >= np) --g;  // the last group has no C range
+    if (g <= 0) continue;
+    const int64_t nbs = s / DB;
+    const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
+    hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 0);
+    hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 1);
+  }
+  hipLaunchKernelGGL(k_gptq_store_u, dim3(grid_for(n * n)), dim3(256), 0, st, X, n, np, U);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ rows
+template <int DT>
+__global__ void __launch_bounds__(256)
+    k_gptq_init(const void *__restrict__ w, int64_t rows, int64_t n, int64_t rp, int64_t np,
+                double *__restrict__ V) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rp * np;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / np, c = e % np;
+    double v = 0.0;
+    if (r < rows && c < n) {
+      if (DT == NVFP4_DTYPE_BF16)
+        v = (double)__uint_as_float((unsigned)static_cast<const uint16_t *>(w)[r * n + c] << 16);
+      else
+        v = (double)static_cast<const float *>(w)[r * n + c];
+    }
+    V[e] = v;
+  }
+}
+
+__device__ __forceinline__ double dpp_quad_bcast(double x, int src) {
+  // src is a compile-time constant at every call site (the column loop is unrolled)
+  const int ctrl = src | (src << 2) | (src << 4) | (src << 6);
+  int lo = __double2loint(x), hi = __double2hiint(x);
+  switch (ctrl) {
+    case 0x00:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x00, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x00, 0xF, 0xF, false);
+      break;
+    case 0x55:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x55, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x55, 0xF, 0xF, false);
+      break;
+    case 0xAA:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xAA, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xAA, 0xF, 0xF, false);
+      break;
+    default:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xFF, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xFF, 0xF, 0xF, false);
+      break;
+  }
+  return __hiloint2double(hi, lo);
+}
+
+// Column block b (columns 64 b .. 64 b + 63). Thread (row r, part p = t & 3) holds the 16
+// values of scale block 4 b + p. Codes go to `codes`, errors e to E[r][16 p + i].
+__global__ void __launch_bounds__(256)
+    k_gptq_block(double *__restrict__ V, int64_t np, int64_t rows, int64_t n,
+                 const float *__restrict__ Sp, const uint8_t *__restrict__ scales,
+                 const double *__restrict__ U, int64_t b, double *__restrict__ E,
+                 uint8_t *__restrict__ codes) {
+  __shared__ double LU[DB * 68];  // row j: 4 parts of 16, pitch 17 (distinct banks per part)
+  const int t = threadIdx.x;
+  const int64_t c0 = b * DB;
+  for (int e = t; e < DB * DB; e += 256) {
+    const int j = e >> 6, k = e & 63;
+    const int64_t gj = c0 + j, gk = c0 + k;
+    double u = 0.0;
+    if (gj < n && gk < n) u = U[gj * n + gk];  // zero below the diagonal
+    else if (gj == gk) u = 1.0;                // padding columns
+    LU[j * 68 + (k >> 4) * 17 + (k & 15)] = u;
+  }
+  __syncthreads();
+  const int p = t & 3;
+  const int64_t r = (int64_t)blockIdx.x * 64 + (t >> 2);
+  const int64_t cb = c0 + 16 * p;  // first column of this thread's scale block
+  const bool live = r < rows && cb < n;
+  double v[16];
+  double *vr = V + r * np + cb;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const double2 x = *reinterpret_cast<const double2 *>(vr + i);
+    v[i] = x.x;
+    v[i + 1] = x.y;
+  }
+  const int byte = live ? scales[r * (n / 16) + cb / 16] : 0;
+  // s * S (exact in double) and the midpoints between grid values at that scale; a zero
+  // byte gives infinite midpoints, so every value rounds to code 0
+  double sS = 0.0;
+  if (byte != 0) {
+    const int ex = (byte >> 3) & 15, mant = byte & 7;
+    const double s = ex == 0 ? ldexp((double)mant, -9) : ldexp((double)(8 + mant), ex - 10);
+    sS = s * (double)Sp[0];
+  }
+  const double big = __builtin_inf();
+  const double T0 = byte ? 0.25 * sS : big, T1 = byte ? 0.75 * sS : big,
+               T2 = byte ? 1.25 * sS : big, T3 = byte ? 1.75 * sS : big,
+               T4 = byte ? 2.5 * sS : big, T5 = byte ? 3.5 * sS : big, T6 = byte ? 5.0 * sS : big;
+  const double half = 0.5 * sS, twice = 2.0 * sS;
+  unsigned cw0 = 0u, cw1 = 0u;
+  double ev[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ev[i] = 0.0;
+#pragma unroll
+  for (int j = 0; j < DB; ++j) {
+    const int pj = j >> 4, jj = j & 15;
+    const double x = v[jj];
+    const double a = fabs(x);
+    // round half to even onto {0, .5, 1, 1.5, 2, 3, 4, 6} sS: crossing midpoint i moves up
+    // one grid step; on a tie, odd i (whose upper neighbour has an even index) moves up
+    const int b0 = a > T0, b1 = a >= T1, b2 = a > T2, b3 = a >= T3, b4 = a > T4, b5 = a >= T5,
+              b6 = a > T6;
+    const int k = b0 + b1 + b2 + b3 + b4 + b5 + b6;
+    const double qm = (double)(b0 + b1 + b2 + b3) * half + (double)(b4 + b5) * sS +
+                      (b6 ? twice : 0.0);  // exact: small multiples of sS / 2
+    const double q = x < 0.0 ? -qm : qm;
+    const unsigned code = (unsigned)k | ((x < 0.0 && k > 0) ? 8u : 0u);
+    const double e_own = (x - q) / LU[j * 68 + pj * 17 + jj];
+    const bool mine = p == pj;
+    if (jj < 8) cw0 |= mine ? code << (4 * jj) : 0u;
+    else cw1 |= mine ? code << (4 * (jj - 8)) : 0u;
+    ev[jj] = mine ? e_own : ev[jj];
+    const double e = dpp_quad_bcast(e_own, pj);
+    const double *ur = LU + j * 68 + p * 17;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = fma(-e, ur[i], v[i]);
+    // keep each column's U row loads next to their use (hoisting them all spills)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (live) {
+    *reinterpret_cast<uint2 *>(codes + r * (n / 2) + cb / 2) = make_uint2(cw0, cw1);
+  }
+  double *er = E + r * DB + 16 * p;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) *reinterpret_cast<double2 *>(er + i) = make_double2(ev[i], ev[i + 1]);
+}
+
+// V[:, later columns] -= E U[block rows, later columns]; tile (row block, column block)
+__global__ void __launch_bounds__(256)
+    k_gptq_update(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
+                  const double *__restrict__ E, int64_t b) {
+  __shared__ double LA[DB * DP], LB[DB * DP];
+  const int64_t rb = blockIdx.x, cbk = b + 1 + blockIdx.y;
+  const int64_t r0 = rb * DB, c0 = cbk * DB, k0 = b * DB;
+  const int klim = (int)(n - k0 < DB ? n - k0 : DB);
+  const int nlim = (int)(n - c0 < DB ? n - c0 : DB);
+  dload_mk(LA, E + r0 * DB, DB, DB, DB);
+  dload_kn(LB, U + k0 * n + c0, n, klim, nlim);
+  __syncthreads();
+  DAcc acc;
+  dacc_zero(acc);
+  dmma(acc, LA, LB);
+  double *C = V + r0 * np + c0;
+  dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
+}
+
+int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const float *S,
+                     const uint8_t *scales, const double *U, uint8_t *codes, void *workspace,
+                     hipStream_t st) {
+  const int64_t rp = pad64(rows), np = pad64(n), nbc = np / DB;
+  double *V = static_cast<double *>(workspace);
+  double *E = V + rp * np;
+  if (dtype == NVFP4_DTYPE_BF16)
+    hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_BF16>, dim3(grid_for(rp * np)), dim3(256), 0, st, w,
+                       rows, n, rp, np, V);
+  else
+    hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_F32>, dim3(grid_for(rp * np)), dim3(256), 0, st, w,
+                       rows, n, rp, np, V);
+  for (int64_t b = 0; b < nbc; ++b) {
+    hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)(rp / DB)), dim3(256), 0, st, V, np, rows, n, S,
+                       scales, U, b, E, codes);
+    if (b + 1 < nbc)
+      hipLaunchKernelGGL(k_gptq_update, dim3((unsigned)(rp / DB), (unsigned)(nbc - b - 1)),
+                         dim3(256), 0, st, V, np, n, U, E, b);
+  }
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,328 @@
+// Full Gram matrix H = X^T X of the layer input X [tokens, cols] (fp32 result).
+//
+// The Local-Hessian search needs only the 16x16 diagonal blocks of X X^T ([LH] "Change the
+// objective"); GPTQ rounding, which the same page says combines with it, needs all of it.
+// This is a dense contraction over tokens (2 T C^2 flops), so it runs on the matrix cores:
+//  * only tiles on or above the diagonal are computed (128 x 128 channels each); the
+//    reduction mirrors them, so H comes out exactly symmetric;
+//  * tokens are split into chunks so that the grid has about 2048 workgroups; each
+//    (chunk, tile) writes a partial tile, and k_gram_reduce adds the partials in chunk order
+//    (deterministic);
+//  * workgroups are numbered chunk-major, so the ~500 that run at once all stream the same
+//    token rows, which the L2 serves to every tile that needs them.
+//
+// bf16: v_mfma_f32_32x32x16_bf16. A lane's operand is 8 consecutive tokens of one channel,
+// while a token row is contiguous in memory, so each step (64 tokens x 256 channels: the
+// tile's row and column channels) is transposed on the way into LDS: a lane loads 8 token
+// rows x 8 channels (eight 16-byte loads), transposes the 8x8 block of 16-bit values in
+// registers and writes eight 16-byte channel rows. LDS rows are 128 bytes (64 tokens); the
+// 16-byte token groups are XOR-swizzled by (c ^ c >> 3) & 7 so that both the transposing
+// writes (8 lanes = 8 channels 8 apart) and the MFMA reads (8 lanes = 8 adjacent channels)
+// touch 8 distinct bank groups. Any order of tokens inside a K slice is valid as long as
+// both operands use the same one, which holds because A and B come from the same rows.
+// fp32: v_mfma_f32_32x32x2_f32 straight from a [token][channel] tile (no transpose needed).
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+typedef __bf16 gram_v8bf __attribute__((ext_vector_type(8)));
+typedef float gram_v16f __attribute__((ext_vector_type(16)));
+
+constexpr int GT = 128;   // output tile edge (channels)
+constexpr int GK = 64;    // tokens per step, bf16
+constexpr int GKF = 32;   // tokens per step, fp32
+constexpr int GRAM_TARGET_WGS = 2048;
+
+struct GramGeom {
+  int64_t nt, tiles, nc, tc;
+};
+
+static GramGeom gram_geom(int64_t tokens, int64_t cols) {
+  GramGeom g;
+  g.nt = (cols + GT - 1) / GT;
+  g.tiles = g.nt * (g.nt + 1) / 2;
+  const int64_t steps = (tokens + GK - 1) / GK;
+  int64_t nc = (GRAM_TARGET_WGS + g.tiles - 1) / (g.tiles > 0 ? g.tiles : 1);
+  const int64_t max_nc = steps / 16 > 1 ? steps / 16 : 1;  // chunks of >= 1024 tokens
+  if (nc > max_nc) nc = max_nc;
+  if (nc < 1) nc = 1;
+  const int64_t spc = (steps + nc - 1) / nc > 0 ? (steps + nc - 1) / nc : 1;
+  g.tc = spc * GK;
+  g.nc = tokens > 0 ? (tokens + g.tc - 1) / g.tc : 1;
+  return g;
+}
+
+size_t gram_workspace_size(int64_t tokens, int64_t cols) {
+  const GramGeom g = gram_geom(tokens, cols);
+  return sizeof(float) * (size_t)g.nc * (size_t)g.tiles * GT * GT;
+}
+
+// upper-triangle tile index -> (ti, tj), ti <= tj, row by row
+__device__ __forceinline__ void gram_tile(int64_t t, int64_t nt, int64_t &ti, int64_t &tj) {
+  int64_t i = 0;
+  while (t >= nt - i) {
+    t -= nt - i;
+    ++i;
+  }
+  ti = i;
+  tj = i + t;
+}
+
+__device__ __forceinline__ int gram_swz(int c) { return (c ^ (c >> 3)) & 7; }
+
+__global__ void __launch_bounds__(256)
+    k_gram_bf16(const uint16_t *__restrict__ x, int64_t tokens, int64_t cols, int64_t nt,
+                int64_t tiles, int64_t tc, float *__restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][256 * GK];
+  const int64_t wid = blockIdx.x;
+  const int64_t chunk = wid / tiles;
+  int64_t ti, tj;
+  gram_tile(wid % tiles, nt, ti, tj);
+  const int64_t p0 = chunk * tc;
+  const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // staging role: 8 channels (group q of the 32 groups: 16 row-tile, 16 column-tile) x
+  // 8 tokens (group g of the step's 8)
+  const int q = tid & 31, g = tid >> 5;
+  const int64_t chg = q < 16 ? ti * GT + q * 8 : tj * GT + (q - 16) * 8;
+  const bool ch_ok = chg < cols;  // cols % 16 == 0: a group of 8 is all in or all out
+  uint4 in[8];
+  auto load = [&](int64_t pos) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int64_t tok = pos + g * 8 + s;
+      in[s] = (ch_ok && tok < p1) ? *reinterpret_cast<const uint4 *>(x + tok * cols + chg)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store = [&](uint16_t *buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      unsigned o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint4 a4 = in[2 * e], b4 = in[2 * e + 1];
+        const unsigned a = (i >> 1) == 0 ? a4.x : (i >> 1) == 1 ? a4.y : (i >> 1) == 2 ? a4.z : a4.w;
+        const unsigned b = (i >> 1) == 0 ? b4.x : (i >> 1) == 1 ? b4.y : (i >> 1) == 2 ? b4.z : b4.w;
+        o[e] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      }
+      const int c = q * 8 + i;
+      *reinterpret_cast<uint4 *>(buf + c * GK + ((g ^ gram_swz(c)) << 3)) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
+  const int wr = wave >> 1, wc = wave & 1;  // wave's 64 x 64 quarter of the tile
+  gram_v16f acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  int cur = 0;
+  if (p0 < p1) {
+    load(p0);
+    store(lds[0]);
+  }
+  __syncthreads();
+  for (int64_t pos = p0; pos < p1; pos += GK) {
+    const bool more = pos + GK < p1;
+    if (more) load(pos + GK);
+    const uint16_t *buf = lds[cur];
+#pragma unroll
+    for (int s4 = 0; s4 < GK / 16; ++s4) {
+      const int gg = 2 * s4 + (lane >> 5);
+      gram_v8bf A[2], B[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int c = wr * 64 + a * 32 + (lane & 31);
+        A[a] = __builtin_bit_cast(gram_v8bf, *reinterpret_cast<const uint4 *>(
+                                                 buf + c * GK + ((gg ^ gram_swz(c)) << 3)));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int c = 128 + wc * 64 + b * 32 + (lane & 31);
+        B[b] = __builtin_bit_cast(gram_v8bf, *reinterpret_cast<const uint4 *>(
+                                                 buf + c * GK + ((gg ^ gram_swz(c)) << 3)));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) store(lds[cur ^ 1]);
+    lds_barrier();
+    cur ^= 1;
+  }
+
+  // D layout of a 32x32 MFMA: lane l, register r -> row (r & 3) + 4 (l >> 5) + 8 (r >> 2),
+  // column l & 31
+  float *P = partial + wid * (int64_t)(GT * GT);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * 64 + a * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+        const int col = wc * 64 + b * 32 + (lane & 31);
+        P[row * GT + col] = acc[a][b][r];
+      }
+}
+
+__global__ void __launch_bounds__(256)
+    k_gram_f32(const float *__restrict__ x, int64_t tokens, int64_t cols, int64_t nt,
+               int64_t tiles, int64_t tc, float *__restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) float lds[2][GKF * 256];
+  const int64_t wid = blockIdx.x;
+  const int64_t chunk = wid / tiles;
+  int64_t ti, tj;
+  gram_tile(wid % tiles, nt, ti, tj);
+  const int64_t p0 = chunk * tc;
+  const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  const int q = tid & 63, r0 = tid >> 6;  // 4 channels (64 groups), token rows r0 + 4 s
+  const int64_t chg = q < 32 ? ti * GT + q * 4 : tj * GT + (q - 32) * 4;
+  const bool ch_ok = chg < cols;
+  float4 in[8];
+  auto load = [&](int64_t pos) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int64_t tok = pos + r0 + 4 * s;
+      in[s] = (ch_ok && tok < p1) ? *reinterpret_cast<const float4 *>(x + tok * cols + chg)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&](float *buf) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) *reinterpret_cast<float4 *>(buf + (r0 + 4 * s) * 256 + q * 4) = in[s];
+  };
+
+  const int wr = wave >> 1, wc = wave & 1;
+  gram_v16f acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  int cur = 0;
+  if (p0 < p1) {
+    load(p0);
+    store(lds[0]);
+  }
+  __syncthreads();
+  for (int64_t pos = p0; pos < p1; pos += GKF) {
+    const bool more = pos + GKF < p1;
+    if (more) load(pos + GKF);
+    const float *buf = lds[cur];
+#pragma unroll 4
+    for (int kk = 0; kk < GKF / 2; ++kk) {
+      const float *rowp = buf + (kk * 2 + (lane >> 5)) * 256;
+      float A[2], B[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) A[a] = rowp[wr * 64 + a * 32 + (lane & 31)];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) B[b] = rowp[128 + wc * 64 + b * 32 + (lane & 31)];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[a], B[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) store(lds[cur ^ 1]);
+    lds_barrier();
+    cur ^= 1;
+  }
+
+  float *P = partial + wid * (int64_t)(GT * GT);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wr * 64 + a * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+        const int col = wc * 64 + b * 32 + (lane & 31);
+        P[row * GT + col] = acc[a][b][r];
+      }
+}
+
+// One workgroup per 32x32 piece of an upper tile: sums the chunk partials in order and
+// writes the piece and its mirror image (diagonal pieces: the upper triangle, mirrored).
+__global__ void __launch_bounds__(256)
+    k_gram_reduce(const float *__restrict__ partial, int64_t nt, int64_t tiles, int64_t nc,
+                  int64_t cols, float *__restrict__ H, int accumulate) {
+  __shared__ float sm[32][33];
+  const int64_t tile = blockIdx.x;
+  const int pr = blockIdx.y >> 2, pc = blockIdx.y & 3;  // piece within the tile
+  int64_t ti, tj;
+  gram_tile(tile, nt, ti, tj);
+  if (ti == tj && pr > pc) return;  // covered by the mirror of (pc, pr)
+  const int t = threadIdx.x;
+  const int rr = t >> 3, cc = (t & 7) * 4;
+  const int64_t off = (int64_t)(pr * 32 + rr) * GT + pc * 32 + cc;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t c = 0; c < nc; ++c) {
+    const float4 v = *reinterpret_cast<const float4 *>(partial + (c * tiles + tile) * GT * GT + off);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  sm[rr][cc] = s.x;
+  sm[rr][cc + 1] = s.y;
+  sm[rr][cc + 2] = s.z;
+  sm[rr][cc + 3] = s.w;
+  __syncthreads();
+  const int64_t I0 = ti * GT + pr * 32, J0 = tj * GT + pc * 32;
+  const bool diag = (ti == tj && pr == pc);
+  // direct: H[I0 + rr][J0 + cc + k]
+  if (I0 + rr < cols) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = cc + k;
+      if (J0 + j >= cols) continue;
+      const float v = (diag && j < rr) ? sm[j][rr] : sm[rr][j];
+      float *h = H + (I0 + rr) * cols + J0 + j;
+      *h = accumulate ? *h + v : v;
+    }
+  }
+  if (diag) return;
+  // mirror: H[J0 + rr][I0 + cc + k] = sum[cc + k][rr]
+  if (J0 + rr < cols) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = cc + k;
+      if (I0 + i >= cols) continue;
+      float *h = H + (J0 + rr) * cols + I0 + i;
+      const float v = sm[i][rr];
+      *h = accumulate ? *h + v : v;
+    }
+  }
+}
+
+int launch_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, float *H,
+                        int accumulate, void *workspace, hipStream_t st) {
+  const GramGeom g = gram_geom(tokens, cols);
+  float *partial = static_cast<float *>(workspace);
+  const dim3 grid((unsigned)(g.nc * g.tiles));
+  if (dtype == NVFP4_DTYPE_BF16)
+    hipLaunchKernelGGL(k_gram_bf16, grid, dim3(256), 0, st, static_cast<const uint16_t *>(x),
+                       tokens, cols, g.nt, g.tiles, g.tc, partial);
+  else
+    hipLaunchKernelGGL(k_gram_f32, grid, dim3(256), 0, st, static_cast<const float *>(x), tokens,
+                       cols, g.nt, g.tiles, g.tc, partial);
+  hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)g.tiles, 16), dim3(256), 0, st, partial, g.nt,
+                     g.tiles, g.nc, cols, H, accumulate);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+}  // namespace nvfp4

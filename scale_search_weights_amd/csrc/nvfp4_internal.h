@@ -36,6 +36,17 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
                          const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
                          float *H, int accumulate, void *workspace, hipStream_t st);
 
+size_t gram_workspace_size(int64_t tokens, int64_t cols);
+int launch_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, float *H,
+                        int accumulate, void *workspace, hipStream_t st);
+size_t gptq_factor_workspace_size(int64_t n);
+int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_t *status,
+                       void *workspace, hipStream_t st);
+size_t gptq_rows_workspace_size(int64_t rows, int64_t n);
+int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const float *S,
+                     const uint8_t *scales, const double *U, uint8_t *codes, void *workspace,
+                     hipStream_t st);
+
 size_t route_workspace_size(int64_t tokens, int64_t topk, int64_t experts);
 int launch_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk, int64_t experts,
                         int32_t *offsets, int32_t *token_ids, void *workspace, hipStream_t st);

@@ -48,6 +48,12 @@ _SIGS = {
     "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "nvfp4_fakequant": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "nvfp4_full_hessian_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_full_hessian": (_I, [_P, _I, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "nvfp4_gptq_factor_workspace_size": (_SZ, [_I64]),
+    "nvfp4_gptq_factor": (_I, [_P, _I64, ctypes.c_double, _P, _P, _P, _SZ, _P]),
+    "nvfp4_gptq_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_gptq": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_route_groups_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_route_groups": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
 }
@@ -234,6 +240,61 @@ def block_hessian(x: torch.Tensor, group_offsets: torch.Tensor | None = None,
                                      _ptr(workspace), workspace.numel(), _stream()),
            "nvfp4_block_hessian")
     return H
+
+
+def _workspace(need: int, device, workspace: torch.Tensor | None) -> torch.Tensor:
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def full_hessian(x: torch.Tensor, H: torch.Tensor | None = None, accumulate: bool = False,
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Full Gram matrix X^T X [cols, cols] (fp32) of x [tokens, cols]."""
+    _need(x, "x")
+    tokens, cols = x.shape
+    if H is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing H")
+        H = torch.empty(cols, cols, dtype=torch.float32, device=x.device)
+    need = int(lib().nvfp4_full_hessian_workspace_size(tokens, cols))
+    workspace = _workspace(need, x.device, workspace)
+    _check(lib().nvfp4_full_hessian(_ptr(x), _dt(x), tokens, cols, _ptr(H), int(accumulate),
+                                    _ptr(workspace), workspace.numel(), _stream()),
+           "nvfp4_full_hessian")
+    return H
+
+
+def gptq_factor(H: torch.Tensor, damp: float = 0.01, workspace: torch.Tensor | None = None):
+    """GPTQ's factor of H [cols, cols] fp32: (U [cols, cols] fp64 upper with
+    U^T U = (H + damp * mean(diag H) I)^-1, status [1] int32: 0 when H was positive definite
+    after damping)."""
+    _need(H, "H")
+    cols = H.shape[0]
+    U = torch.empty(cols, cols, dtype=torch.float64, device=H.device)
+    status = torch.empty(1, dtype=torch.int32, device=H.device)
+    need = int(lib().nvfp4_gptq_factor_workspace_size(cols))
+    workspace = _workspace(need, H.device, workspace)
+    _check(lib().nvfp4_gptq_factor(_ptr(H), cols, float(damp), _ptr(U), _ptr(status),
+                                   _ptr(workspace), workspace.numel(), _stream()),
+           "nvfp4_gptq_factor")
+    return U, status
+
+
+def gptq(w: torch.Tensor, S: torch.Tensor, scales: torch.Tensor, U: torch.Tensor,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """GPTQ codes [rows, cols/2] of w [rows, cols] at the given block bytes, S and factor U."""
+    _need(w, "w")
+    for t, name in ((S, "S"), (scales, "scales"), (U, "U")):
+        _need(t, name)
+    rows, cols = w.shape
+    codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=w.device)
+    need = int(lib().nvfp4_gptq_workspace_size(rows, cols))
+    workspace = _workspace(need, w.device, workspace)
+    _check(lib().nvfp4_gptq(_ptr(w), _dt(w), rows, cols, _ptr(S), _ptr(scales), _ptr(U),
+                            _ptr(codes), _ptr(workspace), workspace.numel(), _stream()),
+           "nvfp4_gptq")
+    return codes
 
 
 def scale_search_local_hessian(w: torch.Tensor, S: torch.Tensor, H: torch.Tensor,

@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = nvfp4.declared_symbols()
-    assert len(names) == 18
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
     assert L.nvfp4_version() == 100
@@ -82,6 +82,25 @@ def test_each_entry_point_validates(L):
     assert L.nvfp4_ste_backward(None, 1, 0, ctypes.c_float(1.0), None, None) == OK
     assert L.nvfp4_scale_ema(P(FAKE), P(FAKE), 1, ctypes.c_float(1.5), None) == EARG
     assert L.nvfp4_scale_ema(None, P(FAKE), 1, ctypes.c_float(0.9), None) == ENULL
+    assert L.nvfp4_full_hessian(P(FAKE), 1, 8, 24, P(FAKE), 0, P(FAKE), 1 << 20, None) == ESHAPE
+    assert L.nvfp4_full_hessian(P(FAKE), 5, 8, 32, P(FAKE), 0, P(FAKE), 1 << 20, None) == EDTYPE
+    assert L.nvfp4_full_hessian(P(FAKE), 1, 8, 32, P(FAKE), 0, P(FAKE), 16, None) == EWS
+    assert L.nvfp4_gptq_factor(P(FAKE), 32, ctypes.c_double(-1.0), P(FAKE), None, P(FAKE),
+                               1 << 30, None) == EARG
+    assert L.nvfp4_gptq_factor(P(FAKE), 32, ctypes.c_double(float("nan")), P(FAKE), None,
+                               P(FAKE), 1 << 30, None) == EARG
+    assert L.nvfp4_gptq_factor(P(FAKE), 32, ctypes.c_double(0.01), P(FAKE + 8), None, P(FAKE),
+                               1 << 30, None) == EALIGN
+    assert L.nvfp4_gptq_factor(P(FAKE), 32, ctypes.c_double(0.01), P(FAKE), None, P(FAKE),
+                               16, None) == EWS
+    assert L.nvfp4_gptq(P(FAKE), 1, 4, 40, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                        1 << 30, None) == ESHAPE
+    assert L.nvfp4_gptq(P(FAKE), 1, 4, 32, P(FAKE), None, P(FAKE), P(FAKE), P(FAKE),
+                        1 << 30, None) == ENULL
+    assert L.nvfp4_gptq(P(FAKE), 1, 4, 32, P(FAKE), P(FAKE), P(FAKE), P(FAKE + 4), P(FAKE),
+                        1 << 30, None) == EALIGN
+    assert L.nvfp4_gptq(P(FAKE), 1, 0, 32, None, None, None, None, None, 0, None) == OK
+    assert L.nvfp4_gptq_workspace_size(4, 32) > 0 and L.nvfp4_gptq_factor_workspace_size(32) > 0
     f46 = L.nvfp4_scale_search_four_over_six
     assert f46(P(FAKE), 1, 1, 2, 24, P(FAKE), P(FAKE), None, None) == ESHAPE
     assert f46(P(FAKE), 4, 1, 2, 16, P(FAKE), P(FAKE), None, None) == EDTYPE

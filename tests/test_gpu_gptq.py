@@ -1,0 +1,176 @@
+"""GPU parity of the full Gram matrix and of GPTQ rounding (factor and column loop) against
+the CPU oracle.
+
+Bar: H within 1e-4 relative Frobenius error per 16x16 block (fp32 accumulation against the
+oracle's fp64 sums), exactly symmetric and bitwise reproducible; the factor U within 1e-8
+of the oracle's (both in double; relative to max |U|); GPTQ codes identical to the oracle's
+when both start from the same fp32 H. Codes are decided on double-precision values whose
+last bits depend on summation order, so a row may differ from some column on only if the
+oracle's value there lies within 1e-9 (relative to the block scale) of a rounding midpoint;
+the end-to-end case (GPU H against the oracle's fp64 H) allows 1e-4 there.
+"""
+import numpy as np
+import pytest
+import torch
+
+from scale_search_weights_amd import nvfp4, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def block_rel_frob(Hg: np.ndarray, Hr: np.ndarray) -> float:
+    n = Hr.shape[0]
+    a = Hg.astype(np.float64).reshape(n // 16, 16, n // 16, 16).transpose(0, 2, 1, 3)
+    b = Hr.reshape(n // 16, 16, n // 16, 16).transpose(0, 2, 1, 3)
+    num = np.linalg.norm((a - b).reshape(-1, 256), axis=1)
+    den = np.linalg.norm(b.reshape(-1, 256), axis=1)
+    return float(np.where(den > 0, num / np.where(den > 0, den, 1), num).max())
+
+
+def unpack(codes: np.ndarray) -> np.ndarray:
+    return np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
+
+
+def check_codes(got, want, v_ref, scales, S, orc, tie_tol, max_rows_frac=0.0):
+    """Identical codes, except that a row may diverge from a column where the oracle's
+    value sits within tie_tol * s * S of a rounding midpoint."""
+    g, w = unpack(got), unpack(want)
+    bad_rows = np.flatnonzero((g != w).any(axis=1))
+    for r in bad_rows:
+        j = int(np.flatnonzero(g[r] != w[r])[0])
+        byte = int(scales[r, j // 16])
+        sS = orc.e4m3_value(byte) * float(S)
+        dist = np.min(np.abs(abs(v_ref[r, j]) - MIDS * sS)) / sS
+        assert dist <= tie_tol, f"row {r} col {j}: codes {g[r, j]} vs {w[r, j]}, {dist:.3g} from a midpoint"
+    assert len(bad_rows) <= max_rows_frac * g.shape[0], f"{len(bad_rows)} rows differ"
+
+
+# ------------------------------------------------------------------ full Gram matrix
+
+@pytest.mark.parametrize("which", ["bf16_ragged", "bf16_proj", "fp32", "bf16_narrow"])
+def test_full_hessian(orc, which):
+    if which == "bf16_ragged":
+        x = synth.projection(5, rows=16, cols=272, tokens=1000)[1]        # 2 tiles + 16 cols
+    elif which == "bf16_proj":
+        x = synth.projection(6, rows=16, cols=512, tokens=4096)[1]
+    elif which == "fp32":
+        x = torch.from_numpy((np.random.default_rng(7).standard_t(4, (700, 144))).astype(np.float32))
+    else:
+        x = synth.projection(8, rows=16, cols=32, tokens=77)[1]
+    case(f"full hessian {which} {tuple(x.shape)} {x.dtype}")
+    xd = x.to(DEV)
+    H = nvfp4.full_hessian(xd)
+    Hn = H.cpu().numpy()
+    ref = orc.full_hessian(f32(x))
+    assert block_rel_frob(Hn, ref) <= 1e-4
+    assert np.array_equal(Hn, Hn.T)
+    assert np.array_equal(nvfp4.full_hessian(xd).cpu().numpy(), Hn)       # reproducible
+    Hb = nvfp4.block_hessian(xd).cpu().numpy()
+    for b in range(Hn.shape[0] // 16):
+        blk = Hn[16 * b:16 * b + 16, 16 * b:16 * b + 16]
+        assert np.abs(blk - Hb[b]).max() <= 1e-5 * np.abs(Hb[b]).max() + 1e-30
+
+
+def test_full_hessian_accumulate_and_empty(orc):
+    case("full hessian: two batches accumulated, and zero tokens")
+    xs = [synth.projection(s, rows=16, cols=256, tokens=600)[1] for s in (9, 10)]
+    H = nvfp4.full_hessian(xs[0].to(DEV))
+    nvfp4.full_hessian(xs[1].to(DEV), H=H, accumulate=True)
+    ref = orc.full_hessian(np.concatenate([f32(x) for x in xs]))
+    assert block_rel_frob(H.cpu().numpy(), ref) <= 1e-4
+    e = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    assert not nvfp4.full_hessian(e).cpu().numpy().any()
+    H2 = H.clone()
+    nvfp4.full_hessian(e, H=H2, accumulate=True)
+    assert torch.equal(H2, H)
+
+
+# ------------------------------------------------------------------ factor
+
+def _h_problem(orc, seed, n, corr=1.0):
+    """fp32 H = X^T X of 2n correlated tokens (condition number about 10 n)."""
+    rng = np.random.default_rng(seed)
+    X = (corr * rng.standard_normal((2 * n, 1)) + rng.standard_normal((2 * n, n))).astype(np.float32)
+    return orc.full_hessian(X).astype(np.float32)
+
+
+@pytest.mark.parametrize("n", [48, 208, 512, 1040])
+def test_gptq_factor(orc, n):
+    case(f"gptq factor n={n}")
+    H = _h_problem(orc, n, n)
+    U, status = nvfp4.gptq_factor(torch.from_numpy(H).to(DEV), 0.01)
+    assert status.item() == 0
+    Ug = U.cpu().numpy()
+    Ur = orc.gptq_factor(H.astype(np.float64), 0.01)
+    # backward-stable fp64 factorisations: error ~ n eps kappa, kappa ~ 10 n here
+    assert np.abs(Ug - Ur).max() <= 1e-8 * np.abs(Ur).max()
+    assert not np.tril(Ug, -1).any()
+
+
+def test_gptq_factor_degenerate(orc):
+    case("gptq factor: zero H gives I; an indefinite H is reported")
+    U, status = nvfp4.gptq_factor(torch.zeros(64, 64, device=DEV), 0.01)
+    assert status.item() == 0 and torch.equal(U.cpu(), torch.eye(64, dtype=torch.float64))
+    H = np.eye(96, dtype=np.float32)
+    H[40, 40] = -3.0
+    _, status = nvfp4.gptq_factor(torch.from_numpy(H).to(DEV), 0.0)
+    assert status.item() != 0
+
+
+# ------------------------------------------------------------------ GPTQ rows
+
+@pytest.mark.parametrize("which", ["bf16_lh", "fp32_ragged", "zero_blocks"])
+def test_gptq_rows_same_factor(orc, which):
+    """The oracle's own U feeds both sides: only the column loop is compared."""
+    rng = np.random.default_rng(11)
+    if which == "bf16_lh":
+        w, x = synth.projection(12, rows=64, cols=208, tokens=600)
+    elif which == "fp32_ragged":
+        w = torch.from_numpy((rng.standard_normal((100, 512)) * 0.02).astype(np.float32))
+        x = synth.projection(13, rows=16, cols=512, tokens=1500)[1]
+    else:
+        w, x = synth.projection(14, rows=70, cols=128, tokens=400)
+        w = w.clone()
+        w[3, :48] = 0
+        w[:, 64:80] = 0
+    case(f"gptq rows {which} {tuple(w.shape)} {w.dtype}")
+    wn = f32(w)
+    S = orc.tensor_scale(wn)
+    H = orc.full_hessian(f32(x)).astype(np.float32)
+    sc = orc.scales_local_hessian(wn, S, orc.block_hessian(f32(x)))
+    Ur = orc.gptq_factor(H.astype(np.float64), 0.01)
+    want, v_ref = orc.gptq(wn, S, sc, U=Ur, return_v=True)
+    got = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV),
+                     torch.from_numpy(Ur).to(DEV))
+    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9)
+
+
+def test_gptq_end_to_end(orc):
+    """GPU H -> GPU factor -> GPU GPTQ against the oracle's chain from the same X."""
+    case("gptq end to end 128x512 bf16")
+    w, x = synth.projection(15, rows=128, cols=512, tokens=2048)
+    wn, xn = f32(w), f32(x)
+    S = orc.tensor_scale(wn)
+    sc = orc.scales_local_hessian(wn, S, orc.block_hessian(xn))
+    Href = orc.full_hessian(xn)
+    want, v_ref = orc.gptq(wn, S, sc, Href, 0.01, return_v=True)
+    Hd = nvfp4.full_hessian(x.to(DEV))
+    U, status = nvfp4.gptq_factor(Hd, 0.01)
+    assert status.item() == 0
+    got = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV), U)
+    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-4, max_rows_frac=0.1)
+    # GPTQ lowers the layer-output error against plain rounding at the same bytes
+    rows, cols = wn.shape
+    deq = lambda c: orc.dequantize(c, sc, S, rows, cols).astype(np.float64) - wn
+    err = lambda c: np.einsum("ri,ij,rj->", deq(c), Href, deq(c))
+    assert err(got.cpu().numpy()) < 0.95 * err(orc.quantize(wn, S, sc))
