@@ -38,6 +38,9 @@ MSE_OPS_PER_EVAL = 5           # compare/select x3, subtract, fma per element x 
 FQ_BYTES_PER_ELEM = 2 + 2 + 0.5 + 1 / 16   # read bf16, write bf16 + packed code + 1/16 byte
 FQ_SETS = 4                    # activation batches fake-quantised per step
 CALIB_FRACTION = 0.9999        # activation clip value: this fraction of calibration values
+GPTQ_DAMP = 0.01               # GPTQ damping: 1% of the mean diagonal of H
+BF16_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+FP64_TFLOPS = 78.6             # MI355X fp64 (vector and matrix) peak
 STE_CLIP = 8.0               # gradient clamp of the straight-through backward
 
 
@@ -140,6 +143,18 @@ def main():
     sc4 = torch.empty(r4, c4 // 16, dtype=torch.uint8, device=dev)
     codes4 = torch.empty(r4, c4 // 2, dtype=torch.uint8, device=dev)
 
+    # LH + GPTQ on the projection: full Gram matrix, GPTQ factor, GPTQ rounding at the LH bytes
+    Hf4 = torch.empty(c4, c4, dtype=torch.float32, device=dev)
+    wsf_n = L.nvfp4_full_hessian_workspace_size(t4, c4)
+    wsf = torch.empty(wsf_n, dtype=torch.uint8, device=dev)
+    U4 = torch.empty(c4, c4, dtype=torch.float64, device=dev)
+    st4 = torch.zeros(1, dtype=torch.int32, device=dev)
+    wsu_n = L.nvfp4_gptq_factor_workspace_size(c4)
+    wsu = torch.empty(wsu_n, dtype=torch.uint8, device=dev)
+    wsg_n = L.nvfp4_gptq_workspace_size(r4, c4)
+    wsg = torch.empty(wsg_n, dtype=torch.uint8, device=dev)
+    codes4g = torch.empty(r4, c4 // 2, dtype=torch.uint8, device=dev)
+
     w5c, x5c, ids5c = synth.moe(0)
     w5, x5, ids5 = w5c.to(dev), x5c.to(dev), ids5c.to(dev)
     del w5c, x5c
@@ -197,6 +212,12 @@ def main():
             P(w4), BF16, 1, r4, c4, P(S4), P(H4), P(sc4), None, sptr), "lh"))
         stage("quantize_proj", lambda: ok(L.nvfp4_quantize(
             P(w4), BF16, 1, r4, c4, P(S4), P(sc4), P(codes4), None, sptr), "quantize"))
+        stage("full_hessian_proj", lambda: ok(L.nvfp4_full_hessian(
+            P(x4), BF16, t4, c4, P(Hf4), 0, P(wsf), wsf_n, sptr), "full hessian"))
+        stage("gptq_factor_proj", lambda: ok(L.nvfp4_gptq_factor(
+            P(Hf4), c4, ctypes.c_double(GPTQ_DAMP), P(U4), P(st4), P(wsu), wsu_n, sptr), "gptq factor"))
+        stage("gptq_proj", lambda: ok(L.nvfp4_gptq(
+            P(w4), BF16, r4, c4, P(S4), P(sc4), P(U4), P(codes4g), P(wsg), wsg_n, sptr), "gptq"))
         stage("route_moe", lambda: ok(L.nvfp4_route_groups(
             P(ids5), t5, topk, E, P(off5), P(tok5), P(wsr), wsr_n, sptr), "route"))
         stage("hessian_moe", lambda: ok(L.nvfp4_block_hessian(
@@ -255,6 +276,9 @@ def main():
     ste_bytes = r2 * c2 * 2 * 2
     h4_bytes = t4 * c4 * 2
     h5_bytes = t5 * topk * c5 * 2
+    gram_flops = t4 * c4 * (c4 + 1)                 # 2 T flops per unique entry of X^T X
+    factor_flops = 4 * c4 ** 3 / 3                  # Cholesky + triangular inverse
+    gptq_flops = r4 * c4 * c4                       # rows x n^2 / 2 multiply-adds
 
     def roof(bound, achieved, peak, unit, traffic=None):
         return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
@@ -276,6 +300,12 @@ def main():
         "hessian_proj": roof("hbm", h4_bytes / (ms["hessian_proj"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "lh_proj": roof("mfma", n_lh4 * 126 * 512 / (ms["lh_proj"] * 1e-3) / 1e12, FP32_MFMA_TFLOPS,
                         "TFLOP/s"),
+        "full_hessian_proj": roof("mfma", gram_flops / (ms["full_hessian_proj"] * 1e-3) / 1e12,
+                                  BF16_MFMA_TFLOPS, "TFLOP/s"),
+        "gptq_factor_proj": roof("mfma", factor_flops / (ms["gptq_factor_proj"] * 1e-3) / 1e12,
+                                 FP64_TFLOPS, "TFLOP/s"),
+        "gptq_proj": roof("mfma", gptq_flops / (ms["gptq_proj"] * 1e-3) / 1e12, FP64_TFLOPS,
+                          "TFLOP/s"),
         "hessian_moe": roof("hbm", h5_bytes / (ms["hessian_moe"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "lh_moe": roof("mfma", n_lh5 * 126 * 512 / (ms["lh_moe"] * 1e-3) / 1e12, FP32_MFMA_TFLOPS,
                        "TFLOP/s"),
@@ -299,7 +329,8 @@ def main():
                         "also the activation's calibration histogram and clip scale, its "
                         "straight-through backward and moving-average scale, MSE and "
                         "Four Over Six on bf16 12288x4096, block Hessian of "
-                        "131072x4096 + Local-Hessian on 4096x4096, MoE 128 experts 512x2048 with "
+                        "131072x4096 + Local-Hessian on 4096x4096, full Gram matrix + GPTQ "
+                        "(fp64) at the Local-Hessian bytes on 4096x4096, MoE 128 experts 512x2048 with "
                         "65536 tokens top-8",
             "fakequant_bytes_per_launch": int(fq_bytes),
             "fakequant_launches_per_step": FQ_SETS,

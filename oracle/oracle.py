@@ -295,6 +295,13 @@ def full_hessian(X) -> np.ndarray:
     return H
 
 
+def full_hessian_blas(X) -> np.ndarray:
+    """The same Gram matrix through a library fp64 matmul (for inputs too large for the
+    loop above; the two agree to fp64 rounding)."""
+    a = _f32(X).astype(np.float64)
+    return a.T @ a
+
+
 def e2m1_code_d(v: float, byte: int, S: float) -> int:
     return lib().oracle_e2m1_code_d(float(v), int(byte), float(np.float32(S)))
 

@@ -117,6 +117,48 @@ def test_projection_hessian_and_local_hessian_full(orc):
     assert np.array_equal(obj.cpu().numpy()[rows], orf)
 
 
+def test_projection_full_hessian_and_gptq(orc):
+    case("full Gram matrix of 131072x4096 bf16 (sampled); GPTQ factor and rows on 4096x4096")
+    w, x = synth.projection(0)
+    xd = x.to(DEV)
+    H = nvfp4.full_hessian(xd)
+    torch.cuda.synchronize()
+    del xd
+    Hn = H.cpu().numpy()
+    del H
+    rng = np.random.default_rng(3)
+    idx = np.concatenate([[0, 4095], np.sort(rng.choice(np.arange(1, 4095), 46, replace=False))])
+    sub = orc.full_hessian_blas(f32(x[:, idx]))
+    d = np.sqrt(np.diag(sub))
+    assert (np.abs(Hn[np.ix_(idx, idx)] - sub) <= 1e-4 * np.outer(d, d)).all()
+    assert np.array_equal(Hn, Hn.T)
+    del Hn
+    # GPTQ on the 4096-channel layer, with H from 8192 tokens (an H the oracle forms here)
+    x8 = f32(x[:8192])
+    H8 = orc.full_hessian_blas(x8).astype(np.float32)
+    U, status = nvfp4.gptq_factor(torch.from_numpy(H8).to(DEV), 0.01)
+    Ur = orc.gptq_factor(H8.astype(np.float64), 0.01)
+    assert status.item() == 0
+    diff = float(np.abs(U.cpu().numpy() - Ur).max() / np.abs(Ur).max())
+    print(f"[info] factor max relative difference {diff:.3g}", flush=True)
+    assert diff <= 1e-7  # n eps kappa with n = 4096 and kappa <= 1 + 100 n (damping)
+    del U
+    wn = f32(w)
+    S = orc.tensor_scale(wn)
+    sc = orc.scales_max(wn, S)
+    codes = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV),
+                       torch.from_numpy(Ur).to(DEV)).cpu().numpy()
+    rows = np.concatenate([[0, 4095], rng.choice(np.arange(1, 4095), 30, replace=False)])
+    want, v_ref = orc.gptq(wn[rows], S, sc[rows], U=Ur, return_v=True)
+    g = np.stack([codes[rows] & 15, codes[rows] >> 4], -1).reshape(len(rows), -1)
+    r_ = np.stack([want & 15, want >> 4], -1).reshape(len(rows), -1)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    for i in np.flatnonzero((g != r_).any(axis=1)):
+        j = int(np.flatnonzero(g[i] != r_[i])[0])
+        sS = orc.e4m3_value(int(sc[rows[i], j // 16])) * float(S)
+        assert np.min(np.abs(abs(v_ref[i, j]) - mids * sS)) <= 1e-9 * sS, (rows[i], j)
+
+
 def test_moe_routing_hessian_local_hessian_full(orc):
     case("MoE: 128 experts 512x2048, 65536 tokens top-8 Zipf(1.1)")
     w, x, ids = synth.moe(0)

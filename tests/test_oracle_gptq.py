@@ -21,6 +21,12 @@ def test_full_hessian_integer_closed_form(orc):
     assert np.array_equal(H, (Xi.T @ Xi).astype(np.float64))
 
 
+def test_full_hessian_library_matmul_agrees(orc):
+    _, X = _problem(12, cols=96, tokens=700)
+    H, Hb = orc.full_hessian(X), orc.full_hessian_blas(X)
+    assert np.abs(H - Hb).max() <= 1e-13 * np.abs(H).max()
+
+
 def test_full_hessian_diagonal_blocks_match_block_hessian(orc):
     _, X = _problem(1, cols=64, tokens=300)
     H = orc.full_hessian(X)
