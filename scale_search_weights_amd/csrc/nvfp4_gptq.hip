@@ -12,15 +12,18 @@
 //  * factor: lambda = damp * mean(diag H) (index-order sum); U from one Cholesky
 //    factorisation and one triangular inverse, using the reversal J (J_ij = [i + j = n-1]):
 //    if J (H + lambda I) J = L L^T then H + lambda I = R R^T with R = J L J upper, and
-//    U = R^-1 = J L^-1 J. Blocked right-looking Cholesky (64 x 64 blocks: one workgroup
-//    factors the diagonal block in LDS, one thread per row solves the panel, fp64 MFMA
-//    updates the trailing matrix), then a bottom-up recursive inverse
+//    U = R^-1 = J L^-1 J. Blocked right-looking Cholesky (64 x 64 blocks: per step, one
+//    wave per workgroup factors the diagonal block in registers and solves one panel block,
+//    fp64 MFMA updates the trailing matrix), then a bottom-up recursive inverse
 //    [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] (two fp64 MFMA products per level).
 //  * rows: the column loop in blocks of 64 columns. In a block, four lanes share a row,
 //    each holding the 16 values of one scale block in registers; for every column the
 //    owning lane rounds, forms e and broadcasts it to its quad (DPP), and all four update
-//    their values with the block's row of U from LDS. Between blocks, an fp64 MFMA product
-//    V[:, later] -= E_block U[block, later] applies the block's errors (lazy batch update).
+//    their values with the block's row of U from LDS. Errors reach later columns through
+//    fp64 MFMA products V[:, later] -= E U[done, later] (GPTQ's lazy batch updates), on two
+//    levels: a block's errors update the rest of its 256-column outer block, and each outer
+//    block updates all later columns at once, so the working copy of W is read and written
+//    once per 256 columns.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -38,9 +41,11 @@ size_t gptq_factor_workspace_size(int64_t n) {
   return 256 + 2 * sizeof(double) * (size_t)np * (size_t)np;
 }
 
+constexpr int OB = 4 * DB;    // outer column block of the two-level lazy update
+
 size_t gptq_rows_workspace_size(int64_t rows, int64_t n) {
   const int64_t rp = pad64(rows), np = pad64(n);
-  return sizeof(double) * ((size_t)rp * (size_t)np + (size_t)rp * DB);
+  return sizeof(double) * ((size_t)rp * (size_t)np + (size_t)rp * OB);
 }
 
 // ------------------------------------------------------------------ fp64 64x64 tiles
@@ -168,48 +173,54 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Cholesky factor of diagonal block k, in place (lower; upper part of the block zeroed)
-__global__ void __launch_bounds__(256)
-    k_chol_diag(double *__restrict__ A, int64_t np, int64_t k, int32_t *__restrict__ status) {
-  __shared__ double D[DB * DP];
-  const int t = threadIdx.x;
-  double *blk = A + k * DB * np + k * DB;
-  for (int e = t; e < DB * DB; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    D[i * DP + j] = j <= i ? blk[i * np + j] : 0.0;
-  }
-  for (int j = 0; j < DB; ++j) {
-    __syncthreads();
-    const double d = D[j * DP + j];
-    if (!(d > 0.0) && t == 0) atomicCAS(status, 0, (int32_t)(1 + k * DB + j));
-    const double ljj = sqrt(d);
-    __syncthreads();
-    if (t > j && t < DB) D[t * DP + j] = D[t * DP + j] / ljj;
-    if (t == 0) D[j * DP + j] = ljj;
-    __syncthreads();
-    const int m = DB - 1 - j;
-    for (int e = t; e < m * m; e += 256) {
-      const int i = j + 1 + e / m, l = j + 1 + e % m;
-      if (l <= i) D[i * DP + l] = fma(-D[i * DP + j], D[l * DP + j], D[i * DP + l]);
-    }
-  }
-  __syncthreads();
-  for (int e = t; e < DB * DB; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    blk[i * np + j] = j <= i ? D[i * DP + j] : 0.0;
-  }
+__device__ __forceinline__ double readlane_d(double x, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+  return __hiloint2double(hi, lo);
 }
 
-// panel below diagonal block k: each row solves x L_kk^T = a by forward substitution
+// Step k of the blocked Cholesky factorisation, one wave per workgroup. Every workgroup
+// factors diagonal block k (lane i holds row i in registers; the pivot and column j are
+// broadcast with readlane), workgroup 0 stores it, and workgroup b >= 1 then solves the
+// 64 rows of panel block k + b: x L_kk^T = a by forward substitution, one row per lane,
+// with L_kk (transposed) in LDS.
 __global__ void __launch_bounds__(64)
-    k_chol_panel(double *__restrict__ A, int64_t np, int64_t k) {
-  __shared__ double Lk[DB * DP];
-  const int t = threadIdx.x;
-  const double *dk = A + k * DB * np + k * DB;
-  for (int e = t; e < DB * DB; e += 64) Lk[(e >> 6) * DP + (e & 63)] = dk[(e >> 6) * np + (e & 63)];
+    k_chol_step(double *__restrict__ A, int64_t np, int64_t k, int32_t *__restrict__ status) {
+  __shared__ double Lt[DB * DB];  // Lt[j * 64 + m] = L_kk[m][j]
+  __shared__ double rinv[DB];
+  const int i = threadIdx.x;
+  double *blk = A + k * DB * np + k * DB;
+  double d[DB];
+#pragma unroll
+  for (int j = 0; j < DB; j += 2) {
+    const double2 v = *reinterpret_cast<const double2 *>(blk + (int64_t)i * np + j);
+    d[j] = j <= i ? v.x : 0.0;
+    d[j + 1] = j + 1 <= i ? v.y : 0.0;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < DB; ++j) {
+    const double piv = readlane_d(d[j], j);
+    bad |= !(piv > 0.0);
+    const double ljj = sqrt(piv);
+    d[j] = i > j ? d[j] / ljj : (i == j ? ljj : 0.0);
+#pragma unroll
+    for (int l = j + 1; l < DB; ++l) d[l] = fma(-d[j], readlane_d(d[j], l), d[l]);
+  }
+  // lane i: d[j] = L_kk[i][j] for j <= i; entries right of the diagonal are not used
+  if (blockIdx.x == 0) {
+    if (bad && i == 0) atomicCAS(status, 0, (int32_t)(1 + k));
+#pragma unroll
+    for (int j = 0; j < DB; j += 2)
+      *reinterpret_cast<double2 *>(blk + (int64_t)i * np + j) =
+          make_double2(j <= i ? d[j] : 0.0, j + 1 <= i ? d[j + 1] : 0.0);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < DB; ++j) Lt[j * DB + i] = j <= i ? d[j] : 0.0;
+  rinv[i] = 1.0 / d[i];
   __syncthreads();
-  const int64_t row = (k + 1 + blockIdx.x) * DB + t;
-  double *ar = A + row * np + k * DB;
+  double *ar = A + ((k + blockIdx.x) * DB + i) * np + k * DB;
   double a[DB];
 #pragma unroll
   for (int j = 0; j < DB; j += 2) {
@@ -219,9 +230,9 @@ __global__ void __launch_bounds__(64)
   }
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
-    a[j] = a[j] / Lk[j * DP + j];
+    a[j] = a[j] * rinv[j];
 #pragma unroll
-    for (int m = j + 1; m < DB; ++m) a[m] = fma(-a[j], Lk[m * DP + j], a[m]);
+    for (int m = j + 1; m < DB; ++m) a[m] = fma(-a[j], Lt[j * DB + m], a[m]);
   }
 #pragma unroll
   for (int j = 0; j < DB; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
@@ -337,13 +348,11 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   hipLaunchKernelGGL(k_gptq_lambda, dim3(1), dim3(256), 0, st, H, n, damp, hdr, stat);
   hipLaunchKernelGGL(k_gptq_load_h, dim3(grid_for(np * np)), dim3(256), 0, st, H, n, np, hdr, A);
   for (int64_t k = 0; k < nb; ++k) {
-    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, st, A, np, k, stat);
     const int64_t T = nb - k - 1;
-    if (T > 0) {
-      hipLaunchKernelGGL(k_chol_panel, dim3((unsigned)T), dim3(64), 0, st, A, np, k);
+    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(64), 0, st, A, np, k, stat);
+    if (T > 0)
       hipLaunchKernelGGL(k_chol_update, dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0, st, A,
                          np, k);
-    }
   }
   hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, A, X, np);
   for (int64_t s = DB; s < np; s *= 2) {
@@ -411,6 +420,7 @@ __global__ void __launch_bounds__(256)
                  const float *__restrict__ Sp, const uint8_t *__restrict__ scales,
                  const double *__restrict__ U, int64_t b, double *__restrict__ E,
                  uint8_t *__restrict__ codes) {
+  // E: [rows][OB], this block's errors in columns 64 (b % 4) .. + 63
   __shared__ double LU[DB * 68];  // row j: 4 parts of 16, pitch 17 (distinct banks per part)
   const int t = threadIdx.x;
   const int64_t c0 = b * DB;
@@ -482,26 +492,31 @@ __global__ void __launch_bounds__(256)
   if (live) {
     *reinterpret_cast<uint2 *>(codes + r * (n / 2) + cb / 2) = make_uint2(cw0, cw1);
   }
-  double *er = E + r * DB + 16 * p;
+  double *er = E + r * OB + (b % 4) * DB + 16 * p;
 #pragma unroll
   for (int i = 0; i < 16; i += 2) *reinterpret_cast<double2 *>(er + i) = make_double2(ev[i], ev[i + 1]);
 }
 
-// V[:, later columns] -= E U[block rows, later columns]; tile (row block, column block)
+// V[:, column blocks cb0 + blockIdx.y] -= E[:, e0 .. e0 + kc) U[k0 .. k0 + kc, those columns]
+// (rows of U at or beyond n count as zero); one 64 x 64 tile of V per workgroup
 __global__ void __launch_bounds__(256)
     k_gptq_update(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
-                  const double *__restrict__ E, int64_t b) {
+                  const double *__restrict__ E, int64_t e0, int64_t k0, int kc, int64_t cb0) {
   __shared__ double LA[DB * DP], LB[DB * DP];
-  const int64_t rb = blockIdx.x, cbk = b + 1 + blockIdx.y;
-  const int64_t r0 = rb * DB, c0 = cbk * DB, k0 = b * DB;
-  const int klim = (int)(n - k0 < DB ? n - k0 : DB);
+  const int64_t r0 = (int64_t)blockIdx.x * DB, c0 = (cb0 + blockIdx.y) * DB;
   const int nlim = (int)(n - c0 < DB ? n - c0 : DB);
-  dload_mk(LA, E + r0 * DB, DB, DB, DB);
-  dload_kn(LB, U + k0 * n + c0, n, klim, nlim);
-  __syncthreads();
   DAcc acc;
   dacc_zero(acc);
-  dmma(acc, LA, LB);
+  for (int kb = 0; kb < kc; kb += DB) {
+    const int64_t kr = k0 + kb;
+    if (kr >= n) break;
+    const int klim = (int)(n - kr < DB ? n - kr : DB);
+    __syncthreads();
+    dload_mk(LA, E + r0 * OB + e0 + kb, OB, DB, DB);
+    dload_kn(LB, U + kr * n + c0, n, klim, nlim);
+    __syncthreads();
+    dmma(acc, LA, LB);
+  }
   double *C = V + r0 * np + c0;
   dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
 }
@@ -518,12 +533,19 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
   else
     hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_F32>, dim3(grid_for(rp * np)), dim3(256), 0, st, w,
                        rows, n, rp, np, V);
+  // blocks of 64 columns; inside an outer block of 256 a block's errors update only the
+  // rest of that outer block, and each outer block then updates every later column at once
+  const unsigned rgrid = (unsigned)(rp / DB);
   for (int64_t b = 0; b < nbc; ++b) {
-    hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)(rp / DB)), dim3(256), 0, st, V, np, rows, n, S,
-                       scales, U, b, E, codes);
-    if (b + 1 < nbc)
-      hipLaunchKernelGGL(k_gptq_update, dim3((unsigned)(rp / DB), (unsigned)(nbc - b - 1)),
-                         dim3(256), 0, st, V, np, n, U, E, b);
+    hipLaunchKernelGGL(k_gptq_block, dim3(rgrid), dim3(256), 0, st, V, np, rows, n, S, scales, U,
+                       b, E, codes);
+    const int64_t ob_end = (b / 4 + 1) * 4 < nbc ? (b / 4 + 1) * 4 : nbc;  // in blocks
+    if (b + 1 < ob_end)
+      hipLaunchKernelGGL(k_gptq_update, dim3(rgrid, (unsigned)(ob_end - b - 1)), dim3(256), 0, st,
+                         V, np, n, U, E, (int64_t)(b % 4) * DB, b * DB, DB, b + 1);
+    if (b + 1 == ob_end && ob_end < nbc)
+      hipLaunchKernelGGL(k_gptq_update, dim3(rgrid, (unsigned)(nbc - ob_end)), dim3(256), 0, st,
+                         V, np, n, U, E, (int64_t)0, (b / 4) * OB, OB, ob_end);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

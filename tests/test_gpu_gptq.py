@@ -129,7 +129,7 @@ def test_gptq_factor_degenerate(orc):
 
 # ------------------------------------------------------------------ GPTQ rows
 
-@pytest.mark.parametrize("which", ["bf16_lh", "fp32_ragged", "zero_blocks"])
+@pytest.mark.parametrize("which", ["bf16_lh", "fp32_ragged", "zero_blocks", "wide"])
 def test_gptq_rows_same_factor(orc, which):
     """The oracle's own U feeds both sides: only the column loop is compared."""
     rng = np.random.default_rng(11)
@@ -138,6 +138,8 @@ def test_gptq_rows_same_factor(orc, which):
     elif which == "fp32_ragged":
         w = torch.from_numpy((rng.standard_normal((100, 512)) * 0.02).astype(np.float32))
         x = synth.projection(13, rows=16, cols=512, tokens=1500)[1]
+    elif which == "wide":                                   # 17 column blocks: 4 outer + 1
+        w, x = synth.projection(16, rows=40, cols=1040, tokens=2500)
     else:
         w, x = synth.projection(14, rows=70, cols=128, tokens=400)
         w = w.clone()
