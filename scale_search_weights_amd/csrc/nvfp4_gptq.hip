@@ -16,10 +16,10 @@
 //    wave per workgroup factors the diagonal block in registers and solves one panel block,
 //    fp64 MFMA updates the trailing matrix), then a bottom-up recursive inverse
 //    [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] (two fp64 MFMA products per level).
-//  * rows: the column loop in blocks of 64 columns. In a block, four lanes share a row,
-//    each holding the 16 values of one scale block in registers; for every column the
-//    owning lane rounds, forms e and broadcasts it to its quad (DPP), and all four update
-//    their values with the block's row of U from LDS. Errors reach later columns through
+//  * rows: the column loop in blocks of 64 columns. In a block, sixteen lanes share a row,
+//    each holding 4 of its values in registers; for every column the owning lane rounds,
+//    forms e and broadcasts it to its row of 16 lanes (DPP row_newbcast), and all of them
+//    update their values with the block's row of U from LDS (e uses 1 / U_jj). Errors reach later columns through
 //    fp64 MFMA products V[:, later] -= E U[done, later] (GPTQ's lazy batch updates), on two
 //    levels: a block's errors update the rest of its 256-column outer block, and each outer
 //    block updates all later columns at once, so the working copy of W is read and written
@@ -173,20 +173,14 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-__device__ __forceinline__ double readlane_d(double x, int lane) {
-  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
-  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
-  return __hiloint2double(hi, lo);
-}
-
 // Step k of the blocked Cholesky factorisation, one wave per workgroup. Every workgroup
-// factors diagonal block k (lane i holds row i in registers; the pivot and column j are
-// broadcast with readlane), workgroup 0 stores it, and workgroup b >= 1 then solves the
-// 64 rows of panel block k + b: x L_kk^T = a by forward substitution, one row per lane,
-// with L_kk (transposed) in LDS.
+// factors diagonal block k (lane i holds row i in registers; each scaled column is
+// broadcast through LDS), workgroup 0 stores it, and workgroup b >= 1 then solves the 64
+// rows of panel block k + b: x L_kk^T = a by forward substitution, one row per lane, with
+// L_kk (transposed) in LDS.
 __global__ void __launch_bounds__(64)
     k_chol_step(double *__restrict__ A, int64_t np, int64_t k, int32_t *__restrict__ status) {
-  __shared__ double Lt[DB * DB];  // Lt[j * 64 + m] = L_kk[m][j]
+  __shared__ __attribute__((aligned(16))) double Lt[DB * DB];  // Lt[j * 64 + m] = L_kk[m][j]
   __shared__ double rinv[DB];
   const int i = threadIdx.x;
   double *blk = A + k * DB * np + k * DB;
@@ -198,15 +192,26 @@ __global__ void __launch_bounds__(64)
     d[j + 1] = j + 1 <= i ? v.y : 0.0;
   }
   bool bad = false;
+  double mydiag = 1.0;  // L_kk[i][i] (a register copy: indexing d by the lane would spill d)
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
-    const double piv = readlane_d(d[j], j);
+    // the pivot: lane j's d[j]
+    if (i == j) rinv[0] = d[j];
+    __syncthreads();
+    const double piv = rinv[0];
     bad |= !(piv > 0.0);
     const double ljj = sqrt(piv);
-    d[j] = i > j ? d[j] / ljj : (i == j ? ljj : 0.0);
+    mydiag = i == j ? ljj : mydiag;
+    const double sc = d[j] / ljj;
+    d[j] = i == j ? ljj : sc;               // right of the diagonal, d holds unused values
+    Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
+    __syncthreads();
+    const double *col = Lt + j * DB;
 #pragma unroll
-    for (int l = j + 1; l < DB; ++l) d[l] = fma(-d[j], readlane_d(d[j], l), d[l]);
+    for (int l = j + 1; l < DB; ++l) d[l] = fma(-d[j], col[l], d[l]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // lane i: d[j] = L_kk[i][j] for j <= i; entries right of the diagonal are not used
   // lane i: d[j] = L_kk[i][j] for j <= i; entries right of the diagonal are not used
   if (blockIdx.x == 0) {
     if (bad && i == 0) atomicCAS(status, 0, (int32_t)(1 + k));
@@ -216,9 +221,8 @@ __global__ void __launch_bounds__(64)
           make_double2(j <= i ? d[j] : 0.0, j + 1 <= i ? d[j + 1] : 0.0);
     return;
   }
-#pragma unroll
-  for (int j = 0; j < DB; ++j) Lt[j * DB + i] = j <= i ? d[j] : 0.0;
-  rinv[i] = 1.0 / d[i];
+  __syncthreads();
+  rinv[i] = 1.0 / mydiag;
   __syncthreads();
   double *ar = A + ((k + blockIdx.x) * DB + i) * np + k * DB;
   double a[DB];
@@ -233,6 +237,7 @@ __global__ void __launch_bounds__(64)
     a[j] = a[j] * rinv[j];
 #pragma unroll
     for (int m = j + 1; m < DB; ++m) a[m] = fma(-a[j], Lt[j * DB + m], a[m]);
+    __builtin_amdgcn_sched_barrier(0);  // keep column j's loads next to their use
   }
 #pragma unroll
   for (int j = 0; j < DB; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
@@ -388,63 +393,53 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-__device__ __forceinline__ double dpp_quad_bcast(double x, int src) {
-  // src is a compile-time constant at every call site (the column loop is unrolled)
-  const int ctrl = src | (src << 2) | (src << 4) | (src << 6);
+// value of lane `src` of this lane's row of 16 (DPP row_newbcast); src is a compile-time
+// constant at every call site (the column loop is unrolled), so the switch folds away
+__device__ __forceinline__ double row_bcast16(double x, int src) {
   int lo = __double2loint(x), hi = __double2hiint(x);
-  switch (ctrl) {
-    case 0x00:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x00, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x00, 0xF, 0xF, false);
-      break;
-    case 0x55:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x55, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x55, 0xF, 0xF, false);
-      break;
-    case 0xAA:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0xAA, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0xAA, 0xF, 0xF, false);
-      break;
-    default:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0xFF, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0xFF, 0xF, 0xF, false);
-      break;
+#define GQ_BCAST(S)                                              \
+  case S:                                                        \
+    lo = __builtin_amdgcn_mov_dpp(lo, 0x150 + S, 0xF, 0xF, false); \
+    hi = __builtin_amdgcn_mov_dpp(hi, 0x150 + S, 0xF, 0xF, false); \
+    break;
+  switch (src) {
+    GQ_BCAST(0) GQ_BCAST(1) GQ_BCAST(2) GQ_BCAST(3) GQ_BCAST(4) GQ_BCAST(5) GQ_BCAST(6)
+    GQ_BCAST(7) GQ_BCAST(8) GQ_BCAST(9) GQ_BCAST(10) GQ_BCAST(11) GQ_BCAST(12) GQ_BCAST(13)
+    GQ_BCAST(14) default: GQ_BCAST(15)
   }
+#undef GQ_BCAST
   return __hiloint2double(hi, lo);
 }
 
-// Column block b (columns 64 b .. 64 b + 63). Thread (row r, part p = t & 3) holds the 16
-// values of scale block 4 b + p. Codes go to `codes`, errors e to E[r][16 p + i].
+// Column block b (columns 64 b .. 64 b + 63). Sixteen lanes share a row (four rows per
+// wave): lane p holds columns 4 p .. 4 p + 3 of the block. Codes go to `codes`, errors e to
+// E[r][64 (b % 4) + 4 p + i] (E: [rows][OB]).
 __global__ void __launch_bounds__(256)
     k_gptq_block(double *__restrict__ V, int64_t np, int64_t rows, int64_t n,
                  const float *__restrict__ Sp, const uint8_t *__restrict__ scales,
                  const double *__restrict__ U, int64_t b, double *__restrict__ E,
                  uint8_t *__restrict__ codes) {
-  // E: [rows][OB], this block's errors in columns 64 (b % 4) .. + 63
-  __shared__ double LU[DB * 68];  // row j: 4 parts of 16, pitch 17 (distinct banks per part)
+  __shared__ __attribute__((aligned(16))) double LU[DB * DB];  // U's block, zero below diagonal
+  __shared__ double RU[DB];                                    // 1 / U_jj
   const int t = threadIdx.x;
   const int64_t c0 = b * DB;
   for (int e = t; e < DB * DB; e += 256) {
     const int j = e >> 6, k = e & 63;
     const int64_t gj = c0 + j, gk = c0 + k;
     double u = 0.0;
-    if (gj < n && gk < n) u = U[gj * n + gk];  // zero below the diagonal
-    else if (gj == gk) u = 1.0;                // padding columns
-    LU[j * 68 + (k >> 4) * 17 + (k & 15)] = u;
+    if (gj < n && gk < n) u = U[gj * n + gk];
+    else if (gj == gk) u = 1.0;  // padding columns
+    LU[e] = u;
   }
+  if (t < DB) RU[t] = 1.0 / (c0 + t < n ? U[(c0 + t) * n + c0 + t] : 1.0);
   __syncthreads();
-  const int p = t & 3;
-  const int64_t r = (int64_t)blockIdx.x * 64 + (t >> 2);
-  const int64_t cb = c0 + 16 * p;  // first column of this thread's scale block
+  const int p = t & 15;
+  const int64_t r = (int64_t)blockIdx.x * 16 + (t >> 4);
+  const int64_t cb = c0 + 4 * p;  // first of this lane's 4 columns
   const bool live = r < rows && cb < n;
-  double v[16];
-  double *vr = V + r * np + cb;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    const double2 x = *reinterpret_cast<const double2 *>(vr + i);
-    v[i] = x.x;
-    v[i + 1] = x.y;
-  }
+  const double2 v01 = *reinterpret_cast<const double2 *>(V + r * np + cb);
+  const double2 v23 = *reinterpret_cast<const double2 *>(V + r * np + cb + 2);
+  double v[4] = {v01.x, v01.y, v23.x, v23.y};
   const int byte = live ? scales[r * (n / 16) + cb / 16] : 0;
   // s * S (exact in double) and the midpoints between grid values at that scale; a zero
   // byte gives infinite midpoints, so every value rounds to code 0
@@ -459,13 +454,11 @@ __global__ void __launch_bounds__(256)
                T2 = byte ? 1.25 * sS : big, T3 = byte ? 1.75 * sS : big,
                T4 = byte ? 2.5 * sS : big, T5 = byte ? 3.5 * sS : big, T6 = byte ? 5.0 * sS : big;
   const double half = 0.5 * sS, twice = 2.0 * sS;
-  unsigned cw0 = 0u, cw1 = 0u;
-  double ev[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ev[i] = 0.0;
+  unsigned cw = 0u;
+  double ev[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
-    const int pj = j >> 4, jj = j & 15;
+    const int pj = j >> 2, jj = j & 3;
     const double x = v[jj];
     const double a = fabs(x);
     // round half to even onto {0, .5, 1, 1.5, 2, 3, 4, 6} sS: crossing midpoint i moves up
@@ -477,24 +470,23 @@ __global__ void __launch_bounds__(256)
                       (b6 ? twice : 0.0);  // exact: small multiples of sS / 2
     const double q = x < 0.0 ? -qm : qm;
     const unsigned code = (unsigned)k | ((x < 0.0 && k > 0) ? 8u : 0u);
-    const double e_own = (x - q) / LU[j * 68 + pj * 17 + jj];
+    const double e_own = (x - q) * RU[j];
     const bool mine = p == pj;
-    if (jj < 8) cw0 |= mine ? code << (4 * jj) : 0u;
-    else cw1 |= mine ? code << (4 * (jj - 8)) : 0u;
+    cw |= mine ? code << (4 * jj) : 0u;
     ev[jj] = mine ? e_own : ev[jj];
-    const double e = dpp_quad_bcast(e_own, pj);
-    const double *ur = LU + j * 68 + p * 17;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = fma(-e, ur[i], v[i]);
-    // keep each column's U row loads next to their use (hoisting them all spills)
+    const double e = row_bcast16(e_own, pj);
+    const double2 u01 = *reinterpret_cast<const double2 *>(LU + j * DB + 4 * p);
+    const double2 u23 = *reinterpret_cast<const double2 *>(LU + j * DB + 4 * p + 2);
+    v[0] = fma(-e, u01.x, v[0]);
+    v[1] = fma(-e, u01.y, v[1]);
+    v[2] = fma(-e, u23.x, v[2]);
+    v[3] = fma(-e, u23.y, v[3]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (live) {
-    *reinterpret_cast<uint2 *>(codes + r * (n / 2) + cb / 2) = make_uint2(cw0, cw1);
-  }
-  double *er = E + r * OB + (b % 4) * DB + 16 * p;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) *reinterpret_cast<double2 *>(er + i) = make_double2(ev[i], ev[i + 1]);
+  if (live) *reinterpret_cast<uint16_t *>(codes + r * (n / 2) + cb / 2) = (uint16_t)cw;
+  double *er = E + r * OB + (b % 4) * DB + 4 * p;
+  *reinterpret_cast<double2 *>(er) = make_double2(ev[0], ev[1]);
+  *reinterpret_cast<double2 *>(er + 2) = make_double2(ev[2], ev[3]);
 }
 
 // V[:, column blocks cb0 + blockIdx.y] -= E[:, e0 .. e0 + kc) U[k0 .. k0 + kc, those columns]
@@ -537,8 +529,8 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
   // rest of that outer block, and each outer block then updates every later column at once
   const unsigned rgrid = (unsigned)(rp / DB);
   for (int64_t b = 0; b < nbc; ++b) {
-    hipLaunchKernelGGL(k_gptq_block, dim3(rgrid), dim3(256), 0, st, V, np, rows, n, S, scales, U,
-                       b, E, codes);
+    hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)(rp / 16)), dim3(256), 0, st, V, np, rows, n, S,
+                       scales, U, b, E, codes);
     const int64_t ob_end = (b / 4 + 1) * 4 < nbc ? (b / 4 + 1) * 4 : nbc;  // in blocks
     if (b + 1 < ob_end)
       hipLaunchKernelGGL(k_gptq_update, dim3(rgrid, (unsigned)(ob_end - b - 1)), dim3(256), 0, st,
