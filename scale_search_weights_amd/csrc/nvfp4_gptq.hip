@@ -12,9 +12,9 @@
 //  * factor: lambda = damp * mean(diag H) (index-order sum); U from one Cholesky
 //    factorisation and one triangular inverse, using the reversal J (J_ij = [i + j = n-1]):
 //    if J (H + lambda I) J = L L^T then H + lambda I = R R^T with R = J L J upper, and
-//    U = R^-1 = J L^-1 J. Blocked right-looking Cholesky (64 x 64 blocks: per step, one
-//    wave per workgroup factors the diagonal block in registers and solves one panel block,
-//    fp64 MFMA updates the trailing matrix), then a bottom-up recursive inverse
+//    U = R^-1 = J L^-1 J. Blocked right-looking Cholesky (64 x 64 blocks: per step, each
+//    workgroup factors the diagonal block in one wave's registers and solves one panel
+//    block, fp64 MFMA updates the trailing matrix), then a bottom-up recursive inverse
 //    [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] (two fp64 MFMA products per level).
 //  * rows: the column loop in blocks of 64 columns. In a block, sixteen lanes share a row,
 //    each holding 4 of its values in registers; for every column the owning lane rounds,
@@ -173,74 +173,101 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Step k of the blocked Cholesky factorisation, one wave per workgroup. Every workgroup
-// factors diagonal block k (lane i holds row i in registers; each scaled column is
-// broadcast through LDS), workgroup 0 stores it, and workgroup b >= 1 then solves the 64
-// rows of panel block k + b: x L_kk^T = a by forward substitution, one row per lane, with
-// L_kk (transposed) in LDS.
-__global__ void __launch_bounds__(64)
+__device__ __forceinline__ double quad_bcast(double x, int src) {
+  // value of lane `src` of this lane's quad; src is a compile-time constant at every call
+  int lo = __double2loint(x), hi = __double2hiint(x);
+  switch (src) {
+    case 0:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x00, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x00, 0xF, 0xF, false);
+      break;
+    case 1:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x55, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x55, 0xF, 0xF, false);
+      break;
+    case 2:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xAA, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xAA, 0xF, 0xF, false);
+      break;
+    default:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xFF, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xFF, 0xF, 0xF, false);
+      break;
+  }
+  return __hiloint2double(hi, lo);
+}
+
+// Step k of the blocked Cholesky factorisation. Workgroups of four waves: wave 0 of every
+// workgroup factors diagonal block k (lane i holds row i in registers; the pivot comes by
+// readlane and each scaled column is broadcast through LDS); workgroup 0 stores it, and
+// workgroup b >= 1 then solves the 64 rows of panel block k + b, x L_kk^T = a, by forward
+// substitution: four lanes per row, 16 columns each, x_j broadcast in the quad by DPP.
+__global__ void __launch_bounds__(256)
     k_chol_step(double *__restrict__ A, int64_t np, int64_t k, int32_t *__restrict__ status) {
   __shared__ __attribute__((aligned(16))) double Lt[DB * DB];  // Lt[j * 64 + m] = L_kk[m][j]
   __shared__ double rinv[DB];
-  const int i = threadIdx.x;
+  const int t = threadIdx.x;
   double *blk = A + k * DB * np + k * DB;
-  double d[DB];
+  if (t < DB) {
+    const int i = t;
+    double d[DB];
 #pragma unroll
-  for (int j = 0; j < DB; j += 2) {
-    const double2 v = *reinterpret_cast<const double2 *>(blk + (int64_t)i * np + j);
-    d[j] = j <= i ? v.x : 0.0;
-    d[j + 1] = j + 1 <= i ? v.y : 0.0;
+    for (int j = 0; j < DB; j += 2) {
+      const double2 v = *reinterpret_cast<const double2 *>(blk + (int64_t)i * np + j);
+      d[j] = j <= i ? v.x : 0.0;
+      d[j + 1] = j + 1 <= i ? v.y : 0.0;
+    }
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      const int plo = __builtin_amdgcn_readlane(__double2loint(d[j]), j);
+      const int phi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j);
+      const double piv = __hiloint2double(phi, plo);
+      bad |= !(piv > 0.0);
+      const double ljj = sqrt(piv);
+      const double rl = 1.0 / ljj;
+      d[j] = i == j ? ljj : d[j] * rl;      // right of the diagonal, d holds unused values
+      Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
+      if (i == j) rinv[j] = rl;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const double *col = Lt + j * DB;
+#pragma unroll
+      for (int l = j + 1; l < DB; ++l) d[l] = fma(-d[j], col[l], d[l]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (blockIdx.x == 0) {
+      if (bad && i == 0) atomicCAS(status, 0, (int32_t)(1 + k));
+#pragma unroll
+      for (int j = 0; j < DB; j += 2)
+        *reinterpret_cast<double2 *>(blk + (int64_t)i * np + j) =
+            make_double2(j <= i ? d[j] : 0.0, j + 1 <= i ? d[j + 1] : 0.0);
+    }
   }
-  bool bad = false;
-  double mydiag = 1.0;  // L_kk[i][i] (a register copy: indexing d by the lane would spill d)
-#pragma unroll
-  for (int j = 0; j < DB; ++j) {
-    // the pivot: lane j's d[j]
-    if (i == j) rinv[0] = d[j];
-    __syncthreads();
-    const double piv = rinv[0];
-    bad |= !(piv > 0.0);
-    const double ljj = sqrt(piv);
-    mydiag = i == j ? ljj : mydiag;
-    const double sc = d[j] / ljj;
-    d[j] = i == j ? ljj : sc;               // right of the diagonal, d holds unused values
-    Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
-    __syncthreads();
-    const double *col = Lt + j * DB;
-#pragma unroll
-    for (int l = j + 1; l < DB; ++l) d[l] = fma(-d[j], col[l], d[l]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // lane i: d[j] = L_kk[i][j] for j <= i; entries right of the diagonal are not used
-  // lane i: d[j] = L_kk[i][j] for j <= i; entries right of the diagonal are not used
-  if (blockIdx.x == 0) {
-    if (bad && i == 0) atomicCAS(status, 0, (int32_t)(1 + k));
-#pragma unroll
-    for (int j = 0; j < DB; j += 2)
-      *reinterpret_cast<double2 *>(blk + (int64_t)i * np + j) =
-          make_double2(j <= i ? d[j] : 0.0, j + 1 <= i ? d[j + 1] : 0.0);
-    return;
-  }
+  if (blockIdx.x == 0) return;
   __syncthreads();
-  rinv[i] = 1.0 / mydiag;
-  __syncthreads();
-  double *ar = A + ((k + blockIdx.x) * DB + i) * np + k * DB;
-  double a[DB];
+  const int p = t & 3;
+  double *ar = A + ((k + blockIdx.x) * DB + (t >> 2)) * np + k * DB + 16 * p;
+  double a[16];
 #pragma unroll
-  for (int j = 0; j < DB; j += 2) {
+  for (int j = 0; j < 16; j += 2) {
     const double2 v = *reinterpret_cast<const double2 *>(ar + j);
     a[j] = v.x;
     a[j + 1] = v.y;
   }
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
-    a[j] = a[j] * rinv[j];
+    const int pj = j >> 4, jj = j & 15;
+    const double x_own = a[jj] * rinv[j];
+    const double x = quad_bcast(x_own, pj);
+    const double *lc = Lt + j * DB + 16 * p;  // L_kk[16 p + i][j], zero for 16 p + i < j
 #pragma unroll
-    for (int m = j + 1; m < DB; ++m) a[m] = fma(-a[j], Lt[j * DB + m], a[m]);
-    __builtin_amdgcn_sched_barrier(0);  // keep column j's loads next to their use
+    for (int i = 0; i < 16; ++i) a[i] = fma(-x, lc[i], a[i]);
+    if (p == pj) a[jj] = x;
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int j = 0; j < DB; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
+  for (int j = 0; j < 16; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
 }
 
 // trailing update after step k: A[bi][bj] -= L[bi][k] L[bj][k]^T for k < bj <= bi
@@ -354,7 +381,7 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   hipLaunchKernelGGL(k_gptq_load_h, dim3(grid_for(np * np)), dim3(256), 0, st, H, n, np, hdr, A);
   for (int64_t k = 0; k < nb; ++k) {
     const int64_t T = nb - k - 1;
-    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(64), 0, st, A, np, k, stat);
+    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(256), 0, st, A, np, k, stat);
     if (T > 0)
       hipLaunchKernelGGL(k_chol_update, dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0, st, A,
                          np, k);
