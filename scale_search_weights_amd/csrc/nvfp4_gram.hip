@@ -3,16 +3,16 @@
 // The Local-Hessian search needs only the 16x16 diagonal blocks of X X^T ([LH] "Change the
 // objective"); GPTQ rounding, which the same page says combines with it, needs all of it.
 // This is a dense contraction over tokens (2 T C^2 flops), so it runs on the matrix cores:
-//  * only tiles on or above the diagonal are computed (128 x 128 channels each); the
-//    reduction mirrors them, so H comes out exactly symmetric;
-//  * tokens are split into chunks so that the grid has about 2048 workgroups; each
-//    (chunk, tile) writes a partial tile, and k_gram_reduce adds the partials in chunk order
-//    (deterministic);
-//  * workgroups are numbered chunk-major, so the ~500 that run at once all stream the same
+//  * only tiles on or above the diagonal are computed (256 x 256 channels each, eight
+//    waves of 64 x 128); the reduction mirrors them, so H comes out exactly symmetric;
+//  * tokens are split into up to 16 chunks, as many as fill whole rounds of one workgroup
+//    per CU best; each (chunk, tile) writes a partial tile, and k_gram_reduce adds the
+//    partials in chunk order (deterministic);
+//  * workgroups are numbered chunk-major, so those running at once all stream the same
 //    token rows, which the L2 serves to every tile that needs them.
 //
 // bf16: v_mfma_f32_32x32x16_bf16. A lane's operand is 8 consecutive tokens of one channel,
-// while a token row is contiguous in memory, so each step (64 tokens x 256 channels: the
+// while a token row is contiguous in memory, so each step (64 tokens x 512 channels: the
 // tile's row and column channels) is transposed on the way into LDS: a lane loads 8 token
 // rows x 8 channels (eight 16-byte loads), transposes the 8x8 block of 16-bit values in
 // registers and writes eight 16-byte channel rows. LDS rows are 128 bytes (64 tokens); the
@@ -29,32 +29,53 @@ namespace nvfp4 {
 typedef __bf16 gram_v8bf __attribute__((ext_vector_type(8)));
 typedef float gram_v16f __attribute__((ext_vector_type(16)));
 
-constexpr int GT = 128;   // output tile edge (channels)
+constexpr int GT = 256;   // output tile edge (channels)
+constexpr int GC = 2 * GT;  // channels staged per step: the tile's row and column channels
 constexpr int GK = 64;    // tokens per step, bf16
 constexpr int GKF = 32;   // tokens per step, fp32
-constexpr int GRAM_TARGET_WGS = 2048;
+constexpr int GTHREADS = 512;  // 8 waves: 4 x 2 quarters of 64 x 128
 
 struct GramGeom {
   int64_t nt, tiles, nc, tc;
 };
 
-static GramGeom gram_geom(int64_t tokens, int64_t cols) {
+static int gram_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+// Token chunks per tile: whole rounds of one workgroup per CU where possible (up to 16
+// chunks of at least 2048 tokens each).
+static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   GramGeom g;
   g.nt = (cols + GT - 1) / GT;
   g.tiles = g.nt * (g.nt + 1) / 2;
   const int64_t steps = (tokens + GK - 1) / GK;
-  int64_t nc = (GRAM_TARGET_WGS + g.tiles - 1) / (g.tiles > 0 ? g.tiles : 1);
-  const int64_t max_nc = steps / 16 > 1 ? steps / 16 : 1;  // chunks of >= 1024 tokens
-  if (nc > max_nc) nc = max_nc;
-  if (nc < 1) nc = 1;
-  const int64_t spc = (steps + nc - 1) / nc > 0 ? (steps + nc - 1) / nc : 1;
+  int64_t max_nc = steps / 32;
+  if (max_nc > 16) max_nc = 16;
+  if (max_nc < 1) max_nc = 1;
+  int64_t best = 1;
+  double best_eff = -1.0;
+  for (int64_t nc = 1; nc <= max_nc; ++nc) {
+    const int64_t wgs = g.tiles * nc;
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    const double eff = (double)wgs / (double)(rounds * cus);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = nc;
+    }
+  }
+  const int64_t spc = (steps + best - 1) / best > 0 ? (steps + best - 1) / best : 1;
   g.tc = spc * GK;
   g.nc = tokens > 0 ? (tokens + g.tc - 1) / g.tc : 1;
   return g;
 }
 
 size_t gram_workspace_size(int64_t tokens, int64_t cols) {
-  const GramGeom g = gram_geom(tokens, cols);
+  const GramGeom g = gram_geom(tokens, cols, gram_cus());
   return sizeof(float) * (size_t)g.nc * (size_t)g.tiles * GT * GT;
 }
 
@@ -71,10 +92,10 @@ __device__ __forceinline__ void gram_tile(int64_t t, int64_t nt, int64_t &ti, in
 
 __device__ __forceinline__ int gram_swz(int c) { return (c ^ (c >> 3)) & 7; }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(GTHREADS)
     k_gram_bf16(const uint16_t *__restrict__ x, int64_t tokens, int64_t cols, int64_t nt,
                 int64_t tiles, int64_t tc, float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][256 * GK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][GC * GK];
   const int64_t wid = blockIdx.x;
   const int64_t chunk = wid / tiles;
   int64_t ti, tj;
@@ -83,10 +104,10 @@ __global__ void __launch_bounds__(256)
   const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // staging role: 8 channels (group q of the 32 groups: 16 row-tile, 16 column-tile) x
-  // 8 tokens (group g of the step's 8)
-  const int q = tid & 31, g = tid >> 5;
-  const int64_t chg = q < 16 ? ti * GT + q * 8 : tj * GT + (q - 16) * 8;
+  // staging role: 8 channels (group q of 64: 32 row-tile, 32 column-tile) x 8 tokens
+  // (group g of the step's 8)
+  const int q = tid & 63, g = tid >> 6;
+  const int64_t chg = q < 32 ? ti * GT + q * 8 : tj * GT + (q - 32) * 8;
   const bool ch_ok = chg < cols;  // cols % 16 == 0: a group of 8 is all in or all out
   uint4 in[8];
   auto load = [&](int64_t pos) {
@@ -114,12 +135,12 @@ __global__ void __launch_bounds__(256)
     }
   };
 
-  const int wr = wave >> 1, wc = wave & 1;  // wave's 64 x 64 quarter of the tile
-  gram_v16f acc[2][2];
+  const int wr = wave >> 1, wc = wave & 1;  // wave's 64 x 128 part of the tile
+  gram_v16f acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -136,7 +157,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int s4 = 0; s4 < GK / 16; ++s4) {
       const int gg = 2 * s4 + (lane >> 5);
-      gram_v8bf A[2], B[2];
+      gram_v8bf A[2], B[4];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int c = wr * 64 + a * 32 + (lane & 31);
@@ -144,15 +165,15 @@ __global__ void __launch_bounds__(256)
                                                  buf + c * GK + ((gg ^ gram_swz(c)) << 3)));
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int c = 128 + wc * 64 + b * 32 + (lane & 31);
+      for (int b = 0; b < 4; ++b) {
+        const int c = GT + wc * 128 + b * 32 + (lane & 31);
         B[b] = __builtin_bit_cast(gram_v8bf, *reinterpret_cast<const uint4 *>(
                                                  buf + c * GK + ((gg ^ gram_swz(c)) << 3)));
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
     }
     if (more) store(lds[cur ^ 1]);
@@ -166,19 +187,19 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wr * 64 + a * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-        const int col = wc * 64 + b * 32 + (lane & 31);
+        const int col = wc * 128 + b * 32 + (lane & 31);
         P[row * GT + col] = acc[a][b][r];
       }
 }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(GTHREADS)
     k_gram_f32(const float *__restrict__ x, int64_t tokens, int64_t cols, int64_t nt,
                int64_t tiles, int64_t tc, float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) float lds[2][GKF * 256];
+  __shared__ __attribute__((aligned(16))) float lds[2][GKF * GC];
   const int64_t wid = blockIdx.x;
   const int64_t chunk = wid / tiles;
   int64_t ti, tj;
@@ -187,8 +208,8 @@ __global__ void __launch_bounds__(256)
   const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  const int q = tid & 63, r0 = tid >> 6;  // 4 channels (64 groups), token rows r0 + 4 s
-  const int64_t chg = q < 32 ? ti * GT + q * 4 : tj * GT + (q - 32) * 4;
+  const int q = tid & 127, r0 = tid >> 7;  // 4 channels (128 groups), token rows r0 + 4 s
+  const int64_t chg = q < 64 ? ti * GT + q * 4 : tj * GT + (q - 64) * 4;
   const bool ch_ok = chg < cols;
   float4 in[8];
   auto load = [&](int64_t pos) {
@@ -201,15 +222,15 @@ __global__ void __launch_bounds__(256)
   };
   auto store = [&](float *buf) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) *reinterpret_cast<float4 *>(buf + (r0 + 4 * s) * 256 + q * 4) = in[s];
+    for (int s = 0; s < 8; ++s) *reinterpret_cast<float4 *>(buf + (r0 + 4 * s) * GC + q * 4) = in[s];
   };
 
   const int wr = wave >> 1, wc = wave & 1;
-  gram_v16f acc[2][2];
+  gram_v16f acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
@@ -225,16 +246,16 @@ __global__ void __launch_bounds__(256)
     const float *buf = lds[cur];
 #pragma unroll 4
     for (int kk = 0; kk < GKF / 2; ++kk) {
-      const float *rowp = buf + (kk * 2 + (lane >> 5)) * 256;
-      float A[2], B[2];
+      const float *rowp = buf + (kk * 2 + (lane >> 5)) * GC;
+      float A[2], B[4];
 #pragma unroll
       for (int a = 0; a < 2; ++a) A[a] = rowp[wr * 64 + a * 32 + (lane & 31)];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) B[b] = rowp[128 + wc * 64 + b * 32 + (lane & 31)];
+      for (int b = 0; b < 4; ++b) B[b] = rowp[GT + wc * 128 + b * 32 + (lane & 31)];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[a], B[b], acc[a][b], 0, 0, 0);
     }
     if (more) store(lds[cur ^ 1]);
@@ -246,11 +267,11 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wr * 64 + a * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-        const int col = wc * 64 + b * 32 + (lane & 31);
+        const int col = wc * 128 + b * 32 + (lane & 31);
         P[row * GT + col] = acc[a][b][r];
       }
 }
@@ -262,7 +283,7 @@ __global__ void __launch_bounds__(256)
                   int64_t cols, float *__restrict__ H, int accumulate) {
   __shared__ float sm[32][33];
   const int64_t tile = blockIdx.x;
-  const int pr = blockIdx.y >> 2, pc = blockIdx.y & 3;  // piece within the tile
+  const int pr = blockIdx.y / (GT / 32), pc = blockIdx.y % (GT / 32);  // piece within the tile
   int64_t ti, tj;
   gram_tile(tile, nt, ti, tj);
   if (ti == tj && pr > pc) return;  // covered by the mirror of (pc, pr)
@@ -311,17 +332,17 @@ __global__ void __launch_bounds__(256)
 
 int launch_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, float *H,
                         int accumulate, void *workspace, hipStream_t st) {
-  const GramGeom g = gram_geom(tokens, cols);
+  const GramGeom g = gram_geom(tokens, cols, gram_cus());
   float *partial = static_cast<float *>(workspace);
   const dim3 grid((unsigned)(g.nc * g.tiles));
   if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_gram_bf16, grid, dim3(256), 0, st, static_cast<const uint16_t *>(x),
+    hipLaunchKernelGGL(k_gram_bf16, grid, dim3(GTHREADS), 0, st, static_cast<const uint16_t *>(x),
                        tokens, cols, g.nt, g.tiles, g.tc, partial);
   else
-    hipLaunchKernelGGL(k_gram_f32, grid, dim3(256), 0, st, static_cast<const float *>(x), tokens,
-                       cols, g.nt, g.tiles, g.tc, partial);
-  hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)g.tiles, 16), dim3(256), 0, st, partial, g.nt,
-                     g.tiles, g.nc, cols, H, accumulate);
+    hipLaunchKernelGGL(k_gram_f32, grid, dim3(GTHREADS), 0, st, static_cast<const float *>(x),
+                       tokens, cols, g.nt, g.tiles, g.tc, partial);
+  hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)g.tiles, (GT / 32) * (GT / 32)), dim3(256), 0,
+                     st, partial, g.nt, g.tiles, g.nc, cols, H, accumulate);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
