@@ -5,11 +5,12 @@
 // This is a dense contraction over tokens (2 T C^2 flops), so it runs on the matrix cores:
 //  * only tiles on or above the diagonal are computed (256 x 256 channels each, eight
 //    waves of 64 x 128); the reduction mirrors them, so H comes out exactly symmetric;
-//  * tokens are split into up to 16 chunks, as many as fill whole rounds of one workgroup
-//    per CU best; each (chunk, tile) writes a partial tile, and k_gram_reduce adds the
-//    partials in chunk order (deterministic);
-//  * workgroups are numbered chunk-major, so those running at once all stream the same
-//    token rows, which the L2 serves to every tile that needs them.
+//  * tokens are split into chunks (16 or 8 for long inputs); each (chunk, tile) writes a
+//    partial tile, and k_gram_reduce adds the partials in chunk order (deterministic);
+//  * each XCD (with its own L2) takes whole chunks and walks their tiles row by row, so
+//    the workgroups running together on it share their row panel and stream the same
+//    token rows (spreading every chunk over all XCDs fetched X twelve times over; this
+//    fetches it about four times).
 //
 // bf16: v_mfma_f32_32x32x16_bf16. A lane's operand is 8 consecutive tokens of one channel,
 // while a token row is contiguous in memory, so each step (64 tokens x 512 channels: the
@@ -47,8 +48,11 @@ static int gram_cus() {
   return cus;
 }
 
-// Token chunks per tile: whole rounds of one workgroup per CU where possible (up to 16
-// chunks of at least 2048 tokens each).
+constexpr int GXCD = 8;  // XCDs; workgroups are dispatched to them round-robin
+
+// Token chunks per tile: 16 or 8 when the tokens allow chunks of at least 2048 (then each
+// XCD takes whole chunks, so its L2 streams only those rows), else as many as fill whole
+// rounds of one workgroup per CU best.
 static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   GramGeom g;
   g.nt = (cols + GT - 1) / GT;
@@ -57,9 +61,10 @@ static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   int64_t max_nc = steps / 32;
   if (max_nc > 16) max_nc = 16;
   if (max_nc < 1) max_nc = 1;
-  int64_t best = 1;
+  const bool by_xcd = max_nc >= 8;
+  int64_t best = max_nc >= 16 ? 16 : (max_nc >= 8 ? 8 : 1);
   double best_eff = -1.0;
-  for (int64_t nc = 1; nc <= max_nc; ++nc) {
+  for (int64_t nc = 1; nc <= max_nc && !by_xcd; ++nc) {
     const int64_t wgs = g.tiles * nc;
     const int64_t rounds = (wgs + cus - 1) / cus;
     const double eff = (double)wgs / (double)(rounds * cus);
@@ -71,7 +76,23 @@ static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   const int64_t spc = (steps + best - 1) / best > 0 ? (steps + best - 1) / best : 1;
   g.tc = spc * GK;
   g.nc = tokens > 0 ? (tokens + g.tc - 1) / g.tc : 1;
+  if (by_xcd && g.nc % GXCD != 0) g.nc = (g.nc + GXCD - 1) / GXCD * GXCD;  // empty tail chunks
   return g;
+}
+
+// workgroup -> (token chunk, tile). With nc % 8 == 0, XCD x (= wid % 8) takes chunks
+// x, x + 8, ...; its workgroups walk the tiles row by row, so the ones running together
+// share their row panel. Otherwise chunk-major.
+__device__ __forceinline__ void gram_work(int64_t wid, int64_t tiles, int64_t nc, int64_t &chunk,
+                                          int64_t &tile) {
+  if (nc % GXCD == 0) {
+    const int64_t x = wid % GXCD, slot = wid / GXCD;
+    chunk = x + GXCD * (slot / tiles);
+    tile = slot % tiles;
+  } else {
+    chunk = wid / tiles;
+    tile = wid % tiles;
+  }
 }
 
 size_t gram_workspace_size(int64_t tokens, int64_t cols) {
@@ -94,12 +115,11 @@ __device__ __forceinline__ int gram_swz(int c) { return (c ^ (c >> 3)) & 7; }
 
 __global__ void __launch_bounds__(GTHREADS)
     k_gram_bf16(const uint16_t *__restrict__ x, int64_t tokens, int64_t cols, int64_t nt,
-                int64_t tiles, int64_t tc, float *__restrict__ partial) {
+                int64_t tiles, int64_t nc, int64_t tc, float *__restrict__ partial) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][GC * GK];
-  const int64_t wid = blockIdx.x;
-  const int64_t chunk = wid / tiles;
-  int64_t ti, tj;
-  gram_tile(wid % tiles, nt, ti, tj);
+  int64_t chunk, tile, ti, tj;
+  gram_work(blockIdx.x, tiles, nc, chunk, tile);
+  gram_tile(tile, nt, ti, tj);
   const int64_t p0 = chunk * tc;
   const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -183,7 +203,7 @@ __global__ void __launch_bounds__(GTHREADS)
 
   // D layout of a 32x32 MFMA: lane l, register r -> row (r & 3) + 4 (l >> 5) + 8 (r >> 2),
   // column l & 31
-  float *P = partial + wid * (int64_t)(GT * GT);
+  float *P = partial + (chunk * tiles + tile) * (int64_t)(GT * GT);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -198,12 +218,11 @@ __global__ void __launch_bounds__(GTHREADS)
 
 __global__ void __launch_bounds__(GTHREADS)
     k_gram_f32(const float *__restrict__ x, int64_t tokens, int64_t cols, int64_t nt,
-               int64_t tiles, int64_t tc, float *__restrict__ partial) {
+               int64_t tiles, int64_t nc, int64_t tc, float *__restrict__ partial) {
   __shared__ __attribute__((aligned(16))) float lds[2][GKF * GC];
-  const int64_t wid = blockIdx.x;
-  const int64_t chunk = wid / tiles;
-  int64_t ti, tj;
-  gram_tile(wid % tiles, nt, ti, tj);
+  int64_t chunk, tile, ti, tj;
+  gram_work(blockIdx.x, tiles, nc, chunk, tile);
+  gram_tile(tile, nt, ti, tj);
   const int64_t p0 = chunk * tc;
   const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -263,7 +282,7 @@ __global__ void __launch_bounds__(GTHREADS)
     cur ^= 1;
   }
 
-  float *P = partial + wid * (int64_t)(GT * GT);
+  float *P = partial + (chunk * tiles + tile) * (int64_t)(GT * GT);
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -337,10 +356,10 @@ int launch_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, 
   const dim3 grid((unsigned)(g.nc * g.tiles));
   if (dtype == NVFP4_DTYPE_BF16)
     hipLaunchKernelGGL(k_gram_bf16, grid, dim3(GTHREADS), 0, st, static_cast<const uint16_t *>(x),
-                       tokens, cols, g.nt, g.tiles, g.tc, partial);
+                       tokens, cols, g.nt, g.tiles, g.nc, g.tc, partial);
   else
     hipLaunchKernelGGL(k_gram_f32, grid, dim3(GTHREADS), 0, st, static_cast<const float *>(x),
-                       tokens, cols, g.nt, g.tiles, g.tc, partial);
+                       tokens, cols, g.nt, g.tiles, g.nc, g.tc, partial);
   hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)g.tiles, (GT / 32) * (GT / 32)), dim3(256), 0,
                      st, partial, g.nt, g.tiles, g.nc, cols, H, accumulate);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;

@@ -81,6 +81,15 @@ def test_full_hessian(orc, which):
         assert np.abs(blk - Hb[b]).max() <= 1e-5 * np.abs(Hb[b]).max() + 1e-30
 
 
+def test_full_hessian_long_input_per_xcd_chunks(orc):
+    """Enough tokens for the per-XCD chunk layout (8 chunks), with a ragged tile edge."""
+    case("full hessian 20000 tokens x 272 bf16 (8 token chunks)")
+    x = synth.projection(17, rows=16, cols=272, tokens=20000)[1]
+    Hn = nvfp4.full_hessian(x.to(DEV)).cpu().numpy()
+    assert block_rel_frob(Hn, orc.full_hessian_blas(f32(x))) <= 1e-4
+    assert np.array_equal(Hn, Hn.T)
+
+
 def test_full_hessian_accumulate_and_empty(orc):
     case("full hessian: two batches accumulated, and zero tokens")
     xs = [synth.projection(s, rows=16, cols=256, tokens=600)[1] for s in (9, 10)]
