@@ -62,6 +62,7 @@ int nvfp4_global_scale(const void *x, int dtype, int64_t batch, int64_t n, float
   if (batch == 0) return NVFP4_OK;
   if (!S || (n > 0 && !x)) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(S, 4)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(x, dtype, batch * n, as_stream(stream));
   return launch_global_scale(x, dtype, batch, n, S, as_stream(stream));
 }
 
@@ -72,6 +73,7 @@ int nvfp4_scale_search_max(const void *w, int dtype, int64_t batch, int64_t rows
   if (rc != NVFP4_OK || empty) return rc;
   if (!w || !S || !scales) return NVFP4_ERR_NULL;
   if (!aligned(w, 16) || !aligned(S, 4)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
   return launch_quant(w, dtype, batch, rows, cols, S, nullptr, nullptr, scales, nullptr,
                       as_stream(stream));
 }
@@ -84,6 +86,7 @@ int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, int64_t rows
   if (!w || !S || !scales) return NVFP4_ERR_NULL;
   if (!aligned(w, 16) || !aligned(S, 4) || !aligned(obj, 4)) return NVFP4_ERR_ALIGN;
   if (rows * (cols / 16) / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
+  debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
   return launch_mse(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
 }
 
@@ -96,6 +99,7 @@ int nvfp4_scale_search_four_over_six(const void *w, int dtype, int64_t batch, in
   if (!w || !S || !scales) return NVFP4_ERR_NULL;
   if (!aligned(w, 16) || !aligned(S, 4) || !aligned(obj, 4)) return NVFP4_ERR_ALIGN;
   if (rows * (cols / 16) / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
+  debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
   return launch_four_over_six(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
 }
 
@@ -107,6 +111,7 @@ int nvfp4_ste_backward(const void *grad, int dtype, int64_t n, float clip, void 
   if (n == 0) return NVFP4_OK;
   if (!grad || !grad_out) return NVFP4_ERR_NULL;
   if (!aligned(grad, 16) || !aligned(grad_out, 16)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(grad, dtype, n, as_stream(stream));
   return launch_ste_backward(grad, dtype, n, clip, grad_out, as_stream(stream));
 }
 
@@ -126,6 +131,7 @@ int nvfp4_calib_histogram(const void *x, int dtype, int64_t n, uint64_t *hist, v
   if (!hist || (n > 0 && !x)) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(hist, 8)) return NVFP4_ERR_ALIGN;
   if (n == 0) return NVFP4_OK;
+  debug_check_finite(x, dtype, n, as_stream(stream));
   return launch_calib_histogram(x, dtype, n, reinterpret_cast<unsigned long long *>(hist),
                                 as_stream(stream));
 }
@@ -166,6 +172,7 @@ int nvfp4_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, 
   const size_t need = nvfp4_block_hessian_workspace_size(tokens, cols, groups, n_ids);
   if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(x, dtype, tokens * cols, as_stream(stream));
   return launch_block_hessian(x, dtype, tokens, cols, groups, grouped ? group_offsets : nullptr,
                               grouped ? token_ids : nullptr, n_ids, H, accumulate, workspace,
                               as_stream(stream));
@@ -181,6 +188,8 @@ int nvfp4_scale_search_local_hessian(const void *w, int dtype, int64_t batch, in
   if (!aligned(w, 16) || !aligned(S, 4) || !aligned(H, 4) || !aligned(obj, 8))
     return NVFP4_ERR_ALIGN;
   if (cols / 16 > kMaxGridY || rows / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
+  debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
+  debug_check_finite(H, NVFP4_DTYPE_F32, batch * (cols / 16) * 256, as_stream(stream));
   return launch_local_hessian(w, dtype, batch, rows, cols, S, H, scales, obj, as_stream(stream));
 }
 
@@ -192,6 +201,7 @@ int nvfp4_quantize(const void *x, int dtype, int64_t batch, int64_t rows, int64_
   if (rc != NVFP4_OK || empty) return rc;
   if (!x || !S || !codes) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(S, 4) || !aligned(codes, 8)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(x, dtype, batch * rows * cols, as_stream(stream));
   return launch_quant(x, dtype, batch, rows, cols, S, scales_in, codes,
                       scales_in ? nullptr : scales_out, nullptr, as_stream(stream));
 }
@@ -215,6 +225,7 @@ int nvfp4_fakequant(const void *x, int dtype, int64_t batch, int64_t rows, int64
   if (!x || !S || !y) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(S, 4) || !aligned(y, 16) || !aligned(codes_out, 8))
     return NVFP4_ERR_ALIGN;
+  debug_check_finite(x, dtype, batch * rows * cols, as_stream(stream));
   return launch_quant(x, dtype, batch, rows, cols, S, scales_in, codes_out,
                       scales_in ? nullptr : scales_out, y, as_stream(stream));
 }
@@ -242,6 +253,12 @@ int nvfp4_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk, 
                              as_stream(stream));
 }
 
+int nvfp4_debug_nonfinite(int32_t *flag_out, void *stream) {
+  if (!flag_out) return NVFP4_ERR_NULL;
+  if (!debug_checks_enabled()) return NVFP4_ERR_ARG;
+  return debug_read_flag(flag_out, as_stream(stream));
+}
+
 size_t nvfp4_full_hessian_workspace_size(int64_t tokens, int64_t cols) {
   if (tokens < 0 || cols <= 0) return 0;
   return gram_workspace_size(tokens, cols);
@@ -260,6 +277,7 @@ int nvfp4_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, f
   if (!aligned(x, 16) || !aligned(H, 4)) return NVFP4_ERR_ALIGN;
   if (!workspace || workspace_bytes < gram_workspace_size(tokens, cols)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(x, dtype, tokens * cols, as_stream(stream));
   return launch_full_hessian(x, dtype, tokens, cols, H, accumulate, workspace, as_stream(stream));
 }
 
@@ -277,6 +295,7 @@ int nvfp4_gptq_factor(const float *H, int64_t cols, double damp, double *U, int3
   if (!aligned(H, 4) || !aligned(U, 16) || !aligned(status, 4)) return NVFP4_ERR_ALIGN;
   if (!workspace || workspace_bytes < gptq_factor_workspace_size(cols)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(H, NVFP4_DTYPE_F32, cols * cols, as_stream(stream));
   return launch_gptq_factor(H, cols, damp, U, status, workspace, as_stream(stream));
 }
 
@@ -297,6 +316,7 @@ int nvfp4_gptq(const void *w, int dtype, int64_t rows, int64_t cols, const float
     return NVFP4_ERR_ALIGN;
   if (!workspace || workspace_bytes < gptq_rows_workspace_size(rows, cols)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(w, dtype, rows * cols, as_stream(stream));
   return launch_gptq_rows(w, dtype, rows, cols, S, scales, U, codes, workspace, as_stream(stream));
 }
 

@@ -36,6 +36,10 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
                          const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
                          float *H, int accumulate, void *workspace, hipStream_t st);
 
+bool debug_checks_enabled();
+void debug_check_finite(const void *x, int dtype, int64_t n, hipStream_t st);
+int debug_read_flag(int32_t *out, hipStream_t st);
+
 size_t gram_workspace_size(int64_t tokens, int64_t cols);
 int launch_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, float *H,
                         int accumulate, void *workspace, hipStream_t st);

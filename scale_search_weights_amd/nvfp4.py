@@ -54,6 +54,7 @@ _SIGS = {
     "nvfp4_gptq_factor": (_I, [_P, _I64, ctypes.c_double, _P, _P, _P, _SZ, _P]),
     "nvfp4_gptq_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_gptq": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_debug_nonfinite": (_I, [_P, _P]),
     "nvfp4_route_groups_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_route_groups": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
 }
@@ -240,6 +241,14 @@ def block_hessian(x: torch.Tensor, group_offsets: torch.Tensor | None = None,
                                      _ptr(workspace), workspace.numel(), _stream()),
            "nvfp4_block_hessian")
     return H
+
+
+def debug_nonfinite() -> bool:
+    """With NVFP4_DEBUG_CHECKS=1: whether any input since the last call held NaN or inf
+    (synchronises the current stream; clears the flag)."""
+    flag = ctypes.c_int32(0)
+    _check(lib().nvfp4_debug_nonfinite(ctypes.byref(flag), _stream()), "nvfp4_debug_nonfinite")
+    return bool(flag.value)
 
 
 def _workspace(need: int, device, workspace: torch.Tensor | None) -> torch.Tensor:

@@ -1,6 +1,7 @@
 """The C-ABI library loads, exports every declared entry point, and rejects bad arguments
 on the host before any launch (no GPU needed: no compute call is made)."""
 import ctypes
+import os
 
 import pytest
 
@@ -17,7 +18,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = nvfp4.declared_symbols()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
     assert L.nvfp4_version() == 100
@@ -101,6 +102,14 @@ def test_each_entry_point_validates(L):
                         1 << 30, None) == EALIGN
     assert L.nvfp4_gptq(P(FAKE), 1, 0, 32, None, None, None, None, None, 0, None) == OK
     assert L.nvfp4_gptq_workspace_size(4, 32) > 0 and L.nvfp4_gptq_factor_workspace_size(32) > 0
+    flag = ctypes.c_int32(7)
+    old = os.environ.pop("NVFP4_DEBUG_CHECKS", None)
+    try:
+        assert L.nvfp4_debug_nonfinite(ctypes.byref(flag), None) == EARG  # checks off
+        assert L.nvfp4_debug_nonfinite(None, None) == ENULL
+    finally:
+        if old is not None:
+            os.environ["NVFP4_DEBUG_CHECKS"] = old
     f46 = L.nvfp4_scale_search_four_over_six
     assert f46(P(FAKE), 1, 1, 2, 24, P(FAKE), P(FAKE), None, None) == ESHAPE
     assert f46(P(FAKE), 4, 1, 2, 16, P(FAKE), P(FAKE), None, None) == EDTYPE

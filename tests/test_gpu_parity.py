@@ -559,3 +559,32 @@ def test_local_hessian_batched_experts(orc):
     codes, _ = nvfp4.quantize(wd, S, sc)
     for e in range(4):
         assert np.array_equal(codes[e].cpu().numpy(), orc.quantize(f32(w[e]), Sn[e], sc[e].cpu().numpy()))
+
+
+# ------------------------------------------------------------------ debug input checks
+
+def test_debug_nonfinite_flag(monkeypatch):
+    case("NVFP4_DEBUG_CHECKS=1: non-finite inputs raise the device flag")
+    monkeypatch.setenv("NVFP4_DEBUG_CHECKS", "1")
+    nvfp4.debug_nonfinite()  # start clean
+    x = synth.activation(30, 64, 256).to(DEV)
+    S = nvfp4.global_scale(x)
+    nvfp4.fakequant(x, S)
+    assert nvfp4.debug_nonfinite() is False
+    x[3, 17] = float("nan")
+    nvfp4.fakequant(x, S)
+    assert nvfp4.debug_nonfinite() is True
+    assert nvfp4.debug_nonfinite() is False          # read clears it
+    g = torch.zeros(4096, device=DEV)
+    g[100] = float("-inf")
+    nvfp4.ste_backward(g, 1.0)
+    assert nvfp4.debug_nonfinite() is True
+    xh = synth.projection(31, rows=16, cols=64, tokens=100)[1].to(DEV)
+    nvfp4.block_hessian(xh)
+    assert nvfp4.debug_nonfinite() is False
+    xh[50, 7] = float("inf")
+    nvfp4.block_hessian(xh)
+    assert nvfp4.debug_nonfinite() is True
+    monkeypatch.delenv("NVFP4_DEBUG_CHECKS")
+    with pytest.raises(nvfp4.NVFP4Error):
+        nvfp4.debug_nonfinite()
