@@ -31,11 +31,12 @@ def test_activation_fakequant_8192x4096(orc):
     xd = x.to(DEV)
     S = nvfp4.global_scale(xd)
     xn = f32(x)
-    assert S.item() == orc.tensor_scale(xn)
+    S_ref = orc.tensor_scale(xn)
+    assert S.item() == S_ref
     y, codes, sc = nvfp4.fakequant(xd, S, return_codes=True)
     rows = np.random.default_rng(0).choice(x.shape[0], 192, replace=False)
     rows = np.concatenate([rows, [0, x.shape[0] - 1]])
-    dq, cr, sr = orc.fakequant(xn[rows], S.item())
+    dq, cr, sr = orc.fakequant(xn[rows], S_ref)
     assert np.array_equal(sc.cpu().numpy()[rows], sr)
     assert np.array_equal(codes.cpu().numpy()[rows], cr)
     got = y.cpu().view(torch.int16).numpy().view(np.uint16)[rows]
@@ -61,10 +62,11 @@ def test_mlp_weight_mse_12288x4096(orc):
     wd = w.to(DEV)
     S = nvfp4.global_scale(wd)
     wn = f32(w)
-    assert S.item() == orc.tensor_scale(wn)
+    S_ref = orc.tensor_scale(wn)
+    assert S.item() == S_ref
     sc, obj = nvfp4.scale_search_mse(wd, S, return_obj=True)
     rows = np.random.default_rng(1).choice(w.shape[0], 24, replace=False)
-    sr, orf = orc.scales_mse(wn[rows], S.item(), with_obj=True)
+    sr, orf = orc.scales_mse(wn[rows], S_ref, with_obj=True)
     assert np.array_equal(sc.cpu().numpy()[rows], sr)
     assert np.array_equal(obj.cpu().numpy()[rows], orf)
     # whole-tensor property: every block's MSE objective is at most its max-scaling error
@@ -82,9 +84,11 @@ def test_mlp_weight_four_over_six_12288x4096(orc):
     wd = w.to(DEV)
     S = nvfp4.global_scale(wd)
     wn = f32(w)
+    S_ref = orc.tensor_scale(wn)
+    assert S.item() == S_ref
     sc, obj = nvfp4.scale_search_four_over_six(wd, S, return_obj=True)
     rows = np.random.default_rng(2).choice(w.shape[0], 24, replace=False)
-    sr, orf = orc.scales_four_over_six(wn[rows], S.item(), with_obj=True)
+    sr, orf = orc.scales_four_over_six(wn[rows], S_ref, with_obj=True)
     assert np.array_equal(sc.cpu().numpy()[rows], sr)
     assert np.array_equal(obj.cpu().numpy()[rows], orf)
     # whole tensor: the exhaustive MSE objective is a lower bound (same fp32 objective over a
@@ -108,11 +112,18 @@ def test_projection_hessian_and_local_hessian_full(orc):
     for b in (0, 77, 200, 255):
         xb = np.ascontiguousarray(f32(x[:, 16 * b:16 * b + 16]))
         assert rel_frob(Hn[b], orc.block_hessian(xb)[0]) <= 1e-4, b
-    del xd
+    del xd, H
+    # the search at full size, both sides on the oracle's S and on an oracle H (from the
+    # first 8192 tokens: any H of the right shape exercises the search)
+    wn = f32(w)
+    S_ref = orc.tensor_scale(wn)
     S = nvfp4.global_scale(wd)
-    sc, obj = nvfp4.scale_search_local_hessian(wd, S, H, return_obj=True)
+    assert S.item() == S_ref
+    Href = orc.block_hessian(f32(x[:8192])).astype(np.float32)
+    sc, obj = nvfp4.scale_search_local_hessian(wd, torch.tensor([S_ref], device=DEV),
+                                               torch.from_numpy(Href).to(DEV), return_obj=True)
     rows = np.random.default_rng(2).choice(w.shape[0], 6, replace=False)
-    sr, orf = orc.scales_local_hessian(f32(w)[rows], S.item(), Hn, with_obj=True)
+    sr, orf = orc.scales_local_hessian(wn[rows], S_ref, Href, with_obj=True)
     assert np.array_equal(sc.cpu().numpy()[rows], sr)
     assert np.array_equal(obj.cpu().numpy()[rows], orf)
 
@@ -178,14 +189,20 @@ def test_moe_routing_hessian_local_hessian_full(orc):
         for b in (0, 127):
             xb = np.ascontiguousarray(xn[:, 16 * b:16 * b + 16])
             assert rel_frob(Hn[e, b], orc.block_hessian(xb, sel)[0]) <= 1e-4, (e, b)
+    del H, Hn
+    # the batched search at full size, both sides on the oracle's S and on oracle H (from up
+    # to 512 of each expert's routed tokens)
     wd = w.to(DEV)
-    S = nvfp4.global_scale(wd)
-    sc, obj = nvfp4.scale_search_local_hessian(wd, S, H, return_obj=True)
-    Sn = S.cpu().numpy()
+    wn = f32(w)
+    Sn = np.array([orc.tensor_scale(wn[e]) for e in range(128)], np.float32)
+    assert np.array_equal(nvfp4.global_scale(wd).cpu().numpy(), Sn)
+    Href = np.stack([orc.block_hessian(xn, tok_ref[off_ref[e]:min(off_ref[e + 1], off_ref[e] + 512)])
+                     for e in range(128)]).astype(np.float32)
+    sc, obj = nvfp4.scale_search_local_hessian(wd, torch.from_numpy(Sn).to(DEV),
+                                               torch.from_numpy(Href).to(DEV), return_obj=True)
     for e in picks:
-        we = f32(w[e])
-        assert Sn[e] == orc.tensor_scale(we)
+        we = wn[e]
         rows = np.random.default_rng(e).choice(512, 4, replace=False)
-        sr, orf = orc.scales_local_hessian(we[rows], Sn[e], Hn[e], with_obj=True)
+        sr, orf = orc.scales_local_hessian(we[rows], Sn[e], Href[e], with_obj=True)
         assert np.array_equal(sc[e].cpu().numpy()[rows], sr), e
         assert np.array_equal(obj[e].cpu().numpy()[rows], orf), e

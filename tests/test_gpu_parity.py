@@ -105,7 +105,8 @@ def test_fakequant_batched_per_entry_scale(orc):
     xd = x.to(DEV)
     S = nvfp4.global_scale(xd)
     y, codes, sc = nvfp4.fakequant(xd, S, return_codes=True)
-    Sn = S.cpu().numpy()
+    Sn = np.array([orc.tensor_scale(f32(x[b])) for b in range(3)], np.float32)
+    assert np.array_equal(S.cpu().numpy(), Sn)
     for b in range(3):
         dq, cr, sr = orc.fakequant(f32(x[b]), Sn[b])
         assert np.array_equal(sc[b].cpu().numpy(), sr)
@@ -280,7 +281,8 @@ def test_mse_batched_and_zero_blocks(orc):
     wd = w.to(DEV)
     S = nvfp4.global_scale(wd)
     sc, obj = nvfp4.scale_search_mse(wd, S, return_obj=True)
-    Sn = S.cpu().numpy()
+    Sn = np.array([orc.tensor_scale(f32(w[b])) for b in range(4)], np.float32)
+    assert np.array_equal(S.cpu().numpy(), Sn)
     for b in range(4):
         sr, orf = orc.scales_mse(f32(w[b]), Sn[b], with_obj=True)
         assert np.array_equal(sc[b].cpu().numpy(), sr)
@@ -346,7 +348,8 @@ def test_four_over_six_batched(orc):
     wd = w.to(DEV)
     S = nvfp4.global_scale(wd)
     sc, obj = nvfp4.scale_search_four_over_six(wd, S, return_obj=True)
-    Sn = S.cpu().numpy()
+    Sn = np.array([orc.tensor_scale(f32(w[b])) for b in range(3)], np.float32)
+    assert np.array_equal(S.cpu().numpy(), Sn)
     for b in range(3):
         sr, orf = orc.scales_four_over_six(f32(w[b]), Sn[b], with_obj=True)
         assert np.array_equal(sc[b].cpu().numpy(), sr)
@@ -474,8 +477,12 @@ def test_grouped_hessian_with_empty_group(orc):
 # ------------------------------------------------------------------ Local-Hessian search
 
 def _lh_check(orc, w, S, H):
-    sc, obj = nvfp4.scale_search_local_hessian(w.to(DEV), dev_S(S), H, return_obj=True)
-    sr, orf = orc.scales_local_hessian(f32(w), S, H.cpu().numpy(), with_obj=True)
+    """H: fp32 numpy [cols/16, 16, 16], made by the oracle or in closed form; both sides
+    search with it."""
+    H = np.ascontiguousarray(H, dtype=np.float32)
+    sc, obj = nvfp4.scale_search_local_hessian(w.to(DEV), dev_S(S), torch.from_numpy(H).to(DEV),
+                                               return_obj=True)
+    sr, orf = orc.scales_local_hessian(f32(w), S, H, with_obj=True)
     g = sc.cpu().numpy()
     assert np.array_equal(g, sr), f"{np.sum(g != sr)} bytes differ"
     assert np.array_equal(obj.cpu().numpy(), orf)
@@ -484,18 +491,16 @@ def _lh_check(orc, w, S, H):
 
 def test_local_hessian_tiny(orc, tiny):
     w, x = tiny
-    case("local hessian tiny fp32 (H from GPU)")
+    case("local hessian tiny fp32")
     S = orc.tensor_scale(w.numpy())
-    H = nvfp4.block_hessian(x.to(DEV))
-    _lh_check(orc, w, S, H)
+    _lh_check(orc, w, S, orc.block_hessian(f32(x)))
 
 
 def test_local_hessian_bf16_projection(orc):
     case("local hessian bf16 96x512, H from 4096 t4 tokens")
     w, x = synth.projection(7, rows=96, cols=512, tokens=4096)
     S = orc.tensor_scale(f32(w))
-    H = nvfp4.block_hessian(x.to(DEV))
-    _lh_check(orc, w, S, H)
+    _lh_check(orc, w, S, orc.block_hessian(f32(x)))
 
 
 def test_local_hessian_special_hessians(orc):
@@ -503,7 +508,7 @@ def test_local_hessian_special_hessians(orc):
     w = synth.mlp_weight(8, 64, 128)
     wn = f32(w)
     S = orc.tensor_scale(wn)
-    eye = torch.eye(16, device=DEV).expand(8, 16, 16).contiguous()
+    eye = np.repeat(np.eye(16, dtype=np.float32)[None], 8, axis=0)
     eye[2] = 0.0
     g = _lh_check(orc, w, S, eye)
     mse = orc.scales_mse(wn, S)
@@ -511,29 +516,28 @@ def test_local_hessian_special_hessians(orc):
     assert np.mean(g == mse) > 0.99
     case("local hessian with a rank-1 H (one token)")
     x1 = torch.randn(1, 128, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
-    H1 = nvfp4.block_hessian(x1.to(DEV))
-    _lh_check(orc, w, S, H1)
+    _lh_check(orc, w, S, orc.block_hessian(f32(x1)))
 
 
-def _dominant_h(delta: float) -> torch.Tensor:
+def _dominant_h(delta: float) -> np.ndarray:
     """(16 + delta) I - 11^T: PSD, g_i = delta, kappa ~ 30 / delta."""
-    return (16.0 + delta) * torch.eye(16) - torch.ones(16, 16)
+    return ((16.0 + delta) * np.eye(16) - np.ones((16, 16))).astype(np.float32)
 
 
 def test_local_hessian_magnitude_regimes(orc):
     w0, x = synth.projection(11, rows=64, cols=256, tokens=2048)
-    H0 = nvfp4.block_hessian(x.to(DEV))
+    H0 = orc.block_hessian(f32(x)).astype(np.float32)
     nb = H0.shape[0]
     regimes = [
         ("large weights (x1e4)", 1e4, H0),
         ("tiny weights (x1e-15)", 1e-15, H0),
-        ("H in the fp32 denormal range (x1e-44)", 1.0, H0 * 1e-44),
-        ("huge H (x1e30): fp32 screen would overflow", 1.0, H0 * 1e30),
-        ("large weights and large H (x1e3, x1e20)", 1e3, H0 * 1e20),
+        ("H in the fp32 denormal range (x1e-44)", 1.0, H0 * np.float32(1e-44)),
+        ("huge H (x1e30): fp32 screen would overflow", 1.0, H0 * np.float32(1e30)),
+        ("large weights and large H (x1e3, x1e20)", 1e3, H0 * np.float32(1e20)),
         ("diagonally dominant H, kappa ~3e4 (absolute screen bound)", 1.0,
-         _dominant_h(1e-3).to(DEV).expand(nb, 16, 16).contiguous()),
+         np.repeat(_dominant_h(1e-3)[None], nb, axis=0)),
         ("nearly singular H, kappa ~3e9 (no pruning)", 1.0,
-         _dominant_h(1e-8).to(DEV).expand(nb, 16, 16).contiguous()),
+         np.repeat(_dominant_h(1e-8)[None], nb, axis=0)),
     ]
     for name, ws, H in regimes:
         case(f"local hessian, {name}")
@@ -545,20 +549,31 @@ def test_local_hessian_magnitude_regimes(orc):
 def test_local_hessian_batched_experts(orc):
     case("local hessian batch of 4 experts with per-expert S and H")
     w, x, ids = synth.moe(9, experts=4, rows=40, cols=128, tokens=600, topk=2)
+    off_ref, tok_ref = orc.route_groups(ids.numpy(), 4)
+    Href = np.stack([orc.block_hessian(f32(x), tok_ref[off_ref[e]:off_ref[e + 1]])
+                     for e in range(4)]).astype(np.float32)
+    Sn = np.array([orc.tensor_scale(f32(w[e])) for e in range(4)], np.float32)
+    # the GPU's routing, grouped Hessian and scales against the oracle's
     off, tok = nvfp4.route_groups(ids.to(DEV), 4)
+    assert np.array_equal(off.cpu().numpy(), off_ref)
     H = nvfp4.block_hessian(x.to(DEV), group_offsets=off, token_ids=tok)
-    wd = w.to(DEV)
-    S = nvfp4.global_scale(wd)
-    sc, obj = nvfp4.scale_search_local_hessian(wd, S, H, return_obj=True)
-    Sn, Hn = S.cpu().numpy(), H.cpu().numpy()
     for e in range(4):
-        sr, orf = orc.scales_local_hessian(f32(w[e]), Sn[e], Hn[e], with_obj=True)
+        assert rel_frob(H[e].cpu().numpy(), Href[e].astype(np.float64)) <= 1e-4
+    wd = w.to(DEV)
+    assert np.array_equal(nvfp4.global_scale(wd).cpu().numpy(), Sn)
+    # the batched search, both sides on the oracle's S and H
+    S = torch.from_numpy(Sn).to(DEV)
+    sc, obj = nvfp4.scale_search_local_hessian(wd, S, torch.from_numpy(Href).to(DEV), return_obj=True)
+    srs = []
+    for e in range(4):
+        sr, orf = orc.scales_local_hessian(f32(w[e]), Sn[e], Href[e], with_obj=True)
         assert np.array_equal(sc[e].cpu().numpy(), sr)
         assert np.array_equal(obj[e].cpu().numpy(), orf)
-    # final quantisation with the chosen bytes
-    codes, _ = nvfp4.quantize(wd, S, sc)
+        srs.append(sr)
+    # final quantisation with the chosen bytes (the oracle's, equal to the GPU's)
+    codes, _ = nvfp4.quantize(wd, S, torch.from_numpy(np.stack(srs)).to(DEV))
     for e in range(4):
-        assert np.array_equal(codes[e].cpu().numpy(), orc.quantize(f32(w[e]), Sn[e], sc[e].cpu().numpy()))
+        assert np.array_equal(codes[e].cpu().numpy(), orc.quantize(f32(w[e]), Sn[e], srs[e]))
 
 
 # ------------------------------------------------------------------ debug input checks
