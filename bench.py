@@ -357,21 +357,38 @@ def main():
     if not args.no_cpu_baseline:
         from oracle import oracle
         nthr = oracle.num_threads()
+        # inputs made by the oracle itself (untimed): scales, and Hessians from a subset of
+        # the tokens (search times depend on H's structure, not on how many tokens built it)
         xa = a2.float().cpu().numpy()
-        s2 = float(S2.item())
+        s2 = oracle.tensor_scale(xa)
+        rows_lh = 4096
+        wl = w4[:rows_lh].float().cpu().numpy()
+        s4 = oracle.tensor_scale(w4.float().cpu().numpy())
+        x4s = x4[:8192].float().cpu().numpy()
+        Hn = oracle.block_hessian(x4s).astype(np.float32)
+        rows_mse = 8192
+        w3n = w3.float().cpu().numpy()
+        s3 = oracle.tensor_scale(w3n)
+        wm = w3n[:rows_mse]
+        n_exp = 16
+        We = w5[:n_exp].float().cpu().numpy()
+        Se = [oracle.tensor_scale(We[e]) for e in range(n_exp)]
+        off_r, tok_r = oracle.route_groups(ids5.cpu().numpy(), E)
+        x5n = x5.float().cpu().numpy()
+        He = [oracle.block_hessian(x5n, tok_r[off_r[e]:min(off_r[e + 1], off_r[e] + 512)]).astype(np.float32)
+              for e in range(n_exp)]
+        n_g, rows_g = 1024, 64
+        Hg = oracle.full_hessian_blas(x4s[:, :n_g])
+        wg = w4[:rows_g, :n_g].float().cpu().numpy()
+        sg = oracle.tensor_scale(wg)
+        scg = oracle.scales_max(wg, sg)
+        # timed
         t = time.perf_counter()
         oracle.fakequant(xa, s2)
         dt_fq = time.perf_counter() - t
-        rows_lh = 4096
-        wl = w4[:rows_lh].float().cpu().numpy()
-        Hn = H4.cpu().numpy()
-        s4 = float(S4.item())
         t = time.perf_counter()
         oracle.scales_local_hessian(wl, s4, Hn)
         dt_lh = time.perf_counter() - t
-        rows_mse = 8192
-        wm = w3[:rows_mse].float().cpu().numpy()
-        s3 = float(S3.item())
         t = time.perf_counter()
         oracle.scales_mse(wm, s3)
         dt_mse = time.perf_counter() - t
@@ -381,14 +398,16 @@ def main():
         t = time.perf_counter()
         oracle.calib_scale(oracle.calib_histogram(xa.ravel()), CALIB_FRACTION)
         dt_cal = time.perf_counter() - t
-        n_exp = 16
-        We = w5[:n_exp].float().cpu().numpy()
-        He = H5[:n_exp].cpu().numpy()
-        Se = S5[:n_exp].cpu().numpy()
         t = time.perf_counter()
         for e in range(n_exp):
             oracle.scales_local_hessian(We[e], Se[e], He[e])
         dt_lh5 = time.perf_counter() - t
+        t = time.perf_counter()
+        Ug = oracle.gptq_factor(Hg, GPTQ_DAMP)
+        dt_gf = time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.gptq(wg, sg, scg, U=Ug)
+        dt_gr = time.perf_counter() - t
         out["cpu_baseline"] = {
             "value": round(xa.size * FQ_BYTES_PER_ELEM / dt_fq / 1e9, 4),
             "unit": "GB/s",
@@ -399,13 +418,17 @@ def main():
                       f"calibration histogram of the activation; "
                       f"MSE and Four Over Six on {rows_mse} rows ({rows_mse * (c3 // 16)} "
                       f"blocks) of the 12288x4096 weight; Local-Hessian on {n_exp} of the 128 "
-                      f"experts",
+                      f"experts; GPTQ factor at n = {n_g} and GPTQ rounding of {rows_g} rows x "
+                      f"{n_g}",
             "local_hessian_blocks_per_s": round(rows_lh * (c4 // 16) / dt_lh, 1),
             "mse_blocks_per_s": round(rows_mse * (c3 // 16) / dt_mse, 1),
             "four_over_six_blocks_per_s": round(rows_mse * (c3 // 16) / dt_fos, 1),
             "calibration_gbs": round(xa.size * 2 / dt_cal / 1e9, 3),
             "local_hessian_moe_blocks_per_s": round(n_exp * r5 * (c5 // 16) / dt_lh5, 1),
-            "seconds": round(dt_fq + dt_lh + dt_mse + dt_fos + dt_cal + dt_lh5, 2),
+            "gptq_factor_n1024_s": round(dt_gf, 3),
+            "gptq_rows_tflops": round(rows_g * n_g * n_g / dt_gr / 1e12, 5),
+            "gptq_factor_tflops": round((4 * n_g ** 3 / 3) / dt_gf / 1e12, 5),
+            "seconds": round(dt_fq + dt_lh + dt_mse + dt_fos + dt_cal + dt_lh5 + dt_gf + dt_gr, 2),
         }
         out["gpu_over_cpu"] = {
             "fakequant": round(out["value"] / out["cpu_baseline"]["value"], 1),
