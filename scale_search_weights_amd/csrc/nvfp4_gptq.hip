@@ -35,6 +35,7 @@ constexpr int DB = 64;       // block edge
 constexpr int DP = DB + 1;   // LDS pitch of a K-major tile (doubles)
 
 static inline int64_t pad64(int64_t n) { return (n + DB - 1) / DB * DB; }
+static inline int64_t pad128(int64_t n) { return (n + 127) / 128 * 128; }
 
 size_t gptq_factor_workspace_size(int64_t n) {
   const int64_t np = pad64(n);
@@ -44,7 +45,7 @@ size_t gptq_factor_workspace_size(int64_t n) {
 constexpr int OB = 4 * DB;    // outer column block of the two-level lazy update
 
 size_t gptq_rows_workspace_size(int64_t rows, int64_t n) {
-  const int64_t rp = pad64(rows), np = pad64(n);
+  const int64_t rp = pad128(rows), np = pad128(n);  // the working copy, in 128 x 128 tiles
   return sizeof(double) * ((size_t)rp * (size_t)np + (size_t)rp * OB);
 }
 
@@ -129,6 +130,150 @@ __device__ __forceinline__ void dacc_each(const DAcc &acc, F f) {
         f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 32 + j * 16 + (lane & 15), acc.c[i][j][r]);
 }
 
+// Wide tiles: a workgroup of 4 waves owns a 128 x 128 output tile (each wave 64 x 64, as
+// 4 x 4 MFMA tiles), K in chunks of 32 staged through LDS (the next chunk's global loads
+// are in flight while the current one is multiplied). Four times the work of a 64 x 64
+// tile per byte loaded.
+constexpr int T2 = 128;     // wide tile edge
+constexpr int KC = 32;      // K chunk
+constexpr int P2 = T2 + 1;  // LDS pitch (doubles)
+
+struct DAcc2 {
+  gq_v4d c[4][4];
+};
+
+struct DStage {
+  double2 a[8], b[8];
+};
+
+__device__ __forceinline__ void d2_zero(DAcc2 &a) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a.c[i][j] = (gq_v4d){0.0, 0.0, 0.0, 0.0};
+}
+
+// A chunk: element (m, k) at A[m * lda + k], m < 128, k < 32; zero outside m < mlim, k < klim
+__device__ __forceinline__ void d2_load_a(DStage &st, const double *A, int64_t lda, int mlim, int klim) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
+    st.a[s] = (m < mlim && k < klim) ? *reinterpret_cast<const double2 *>(A + (int64_t)m * lda + k)
+                                     : make_double2(0.0, 0.0);
+  }
+}
+
+__device__ __forceinline__ void d2_store_a(const DStage &st, double *LA) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
+    LA[k * P2 + m] = st.a[s].x;
+    LA[(k + 1) * P2 + m] = st.a[s].y;
+  }
+}
+
+// B chunk, element (k, n): at B[k * ldb + n] when KN, else at B[n * ldb + k]
+template <bool KN>
+__device__ __forceinline__ void d2_load_b(DStage &st, const double *B, int64_t ldb, int klim, int nlim) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + threadIdx.x;
+    if (KN) {
+      const int k = idx >> 6, n = (idx & 63) * 2;
+      st.b[s] = (k < klim && n < nlim) ? *reinterpret_cast<const double2 *>(B + (int64_t)k * ldb + n)
+                                       : make_double2(0.0, 0.0);
+    } else {
+      const int n = idx >> 4, k = (idx & 15) * 2;
+      st.b[s] = (n < nlim && k < klim) ? *reinterpret_cast<const double2 *>(B + (int64_t)n * ldb + k)
+                                       : make_double2(0.0, 0.0);
+    }
+  }
+}
+
+template <bool KN>
+__device__ __forceinline__ void d2_store_b(const DStage &st, double *LB) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + threadIdx.x;
+    if (KN) {
+      const int k = idx >> 6, n = (idx & 63) * 2;
+      LB[k * P2 + n] = st.b[s].x;
+      LB[k * P2 + n + 1] = st.b[s].y;
+    } else {
+      const int n = idx >> 4, k = (idx & 15) * 2;
+      LB[k * P2 + n] = st.b[s].x;
+      LB[(k + 1) * P2 + n] = st.b[s].y;
+    }
+  }
+}
+
+__device__ __forceinline__ void d2_mma(DAcc2 &acc, const double *LA, const double *LB) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll 2
+  for (int kk = 0; kk < KC / 4; ++kk) {
+    const int kr = kk * 4 + (lane >> 4);
+    double a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = LA[kr * P2 + wr * 64 + i * 16 + (lane & 15)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = LB[kr * P2 + wc * 64 + j * 16 + (lane & 15)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc.c[i][j], 0, 0, 0);
+  }
+}
+
+// acc += A[0:128, 0:K] B[0:K, 0:128] (A as in d2_load_a; B as in d2_load_b), k < klim and
+// the row / column limits zero-filled. L: one (A, B) chunk buffer, 2 * KC * P2 doubles
+// (66 KiB, so two workgroups share a CU); the next chunk waits in registers.
+template <bool KN>
+__device__ __forceinline__ void d2_gemm(DAcc2 &acc, const double *A, int64_t lda, int mlim,
+                                        const double *B, int64_t ldb, int nlim, int64_t K,
+                                        int64_t klim, double *L) {
+  const int nch = (int)((K + KC - 1) / KC);
+  if (nch <= 0) return;
+  DStage st;
+  auto bofs = [&](int64_t kb) { return KN ? kb * ldb : kb; };
+  auto kl = [&](int64_t kb) { return (int)(klim - kb < KC ? (klim - kb > 0 ? klim - kb : 0) : KC); };
+  d2_load_a(st, A, lda, mlim, kl(0));
+  d2_load_b<KN>(st, B, ldb, kl(0), nlim);
+  d2_store_a(st, L);
+  d2_store_b<KN>(st, L + KC * P2);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    if (more) {
+      const int64_t kb = (int64_t)(c + 1) * KC;
+      d2_load_a(st, A + kb, lda, mlim, kl(kb));
+      d2_load_b<KN>(st, B + bofs(kb), ldb, kl(kb), nlim);
+    }
+    d2_mma(acc, L, L + KC * P2);
+    if (more) {
+      __syncthreads();
+      d2_store_a(st, L);
+      d2_store_b<KN>(st, L + KC * P2);
+      __syncthreads();
+    }
+  }
+}
+
+// visit the tile elements a thread owns: f(row, col, value)
+template <class F>
+__device__ __forceinline__ void d2_each(const DAcc2 &acc, F f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        f(wr * 64 + i * 16 + (lane >> 4) + 4 * r, wc * 64 + j * 16 + (lane & 15), acc.c[i][j][r]);
+}
+
 // ------------------------------------------------------------------ factor
 // hdr[0] = lambda, hdr[1] = 1 if diag(H) sums to zero (then H + lambda I := I)
 __global__ void __launch_bounds__(256)
@@ -154,7 +299,7 @@ __global__ void __launch_bounds__(256)
 // A (np x np) = J (H + lambda I) J, lower triangle from H's lower triangle, identity padding
 __global__ void __launch_bounds__(256)
     k_gptq_load_h(const float *__restrict__ H, int64_t n, int64_t np,
-                  const double *__restrict__ hdr, double *__restrict__ A) {
+                  const double *__restrict__ hdr, double *__restrict__ A, double *__restrict__ X) {
   const double lam = hdr[0];
   const bool ident = hdr[1] != 0.0;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < np * np;
@@ -170,6 +315,7 @@ __global__ void __launch_bounds__(256)
       }
     }
     A[e] = v;
+    X[e] = 0.0;  // the inverse's upper triangle must read as zero
   }
 }
 
@@ -315,10 +461,11 @@ __global__ void __launch_bounds__(64)
 }
 
 // One level of the recursive inverse. Groups of 2s rows: A-range [a0, a0 + s), C-range
-// [c0, c0 + sc). phase 0: T = L[C][A] X[A][A], stored transposed in X's unused upper part
-// (X[A rows][C cols]); phase 1: X[C][A] = -X[C][C] T.
+// [c0, c0 + sc). phase 0: T = L[C][A] X[A][A], stored transposed in the Cholesky factor's
+// upper triangle (A[A rows][C cols], which nothing reads as L); phase 1: X[C][A] =
+// -X[C][C] T. X's own upper triangle stays zero.
 __global__ void __launch_bounds__(256)
-    k_trtri_level(const double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
+    k_trtri_level(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
                   int phase) {
   __shared__ double LA[DB * DP], LB[DB * DP];
   const int64_t a0 = (int64_t)blockIdx.x * 2 * s, c0 = a0 + s;
@@ -339,18 +486,51 @@ __global__ void __launch_bounds__(256)
       __syncthreads();
       dmma(acc, LA, LB);
     }
-    dacc_each(acc, [&](int r, int c, double v) { X[(q0 + c) * np + r0 + r] = v; });
+    dacc_each(acc, [&](int r, int c, double v) { A[(q0 + c) * np + r0 + r] = v; });
   } else {
-    // sum over C-range blocks kb <= ib: X[r0][kb] T[kb][q0], T[kb][q0] stored at X[q0][kb]
+    // sum over C-range blocks kb <= ib: X[r0][kb] T[kb][q0], T[kb][q0] stored at A[q0][kb]
     for (int64_t kb = 0; kb <= ib; ++kb) {
       const int64_t k0 = c0 + kb * DB;
       __syncthreads();
       dload_mk(LA, X + r0 * np + k0, np, DB, DB);
-      dload_mk(LB, X + q0 * np + k0, np, DB, DB);
+      dload_mk(LB, A + q0 * np + k0, np, DB, DB);
       __syncthreads();
       dmma(acc, LA, LB);
     }
     dacc_each(acc, [&](int r, int c, double v) { X[(r0 + r) * np + q0 + c] = -v; });
+  }
+}
+
+// The same level with 128 x 128 output tiles (levels s >= 128). Whole tiles of X[A][A] and
+// X[C][C] are read, so X's upper triangle must be zero (it is).
+__global__ void __launch_bounds__(256)
+    k_trtri_level2(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
+                   int phase) {
+  __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
+  const int64_t a0 = (int64_t)blockIdx.x * 2 * s, c0 = a0 + s;
+  const int64_t sc = np - c0 < s ? np - c0 : s;
+  const int64_t nbs = s / T2;
+  const int64_t ib = blockIdx.y / nbs, jb = blockIdx.y % nbs;
+  if (ib * T2 >= sc) return;
+  const int mlim = (int)(sc - ib * T2 < T2 ? sc - ib * T2 : T2);
+  const int64_t r0 = c0 + ib * T2, q0 = a0 + jb * T2;
+  DAcc2 acc;
+  d2_zero(acc);
+  if (phase == 0) {
+    // T = L[C rows][A] X[A][q0 cols]; X_AA is lower, so k runs from q0 - a0
+    const int64_t k0 = jb * T2;
+    d2_gemm<true>(acc, A + r0 * np + a0 + k0, np, mlim, X + (a0 + k0) * np + q0, np, T2, s - k0,
+                  s - k0, L2);
+    d2_each(acc, [&](int r, int c, double v) {
+      if (r < mlim) A[(q0 + c) * np + r0 + r] = v;
+    });
+  } else {
+    // X[C][A] = -X[C][C] T, X_CC lower: k up to the tile's last row
+    const int64_t kend = ib * T2 + mlim;
+    d2_gemm<false>(acc, X + r0 * np + c0, np, mlim, A + q0 * np + c0, np, T2, kend, kend, L2);
+    d2_each(acc, [&](int r, int c, double v) {
+      if (r < mlim) X[(r0 + r) * np + q0 + c] = -v;
+    });
   }
 }
 
@@ -378,7 +558,7 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   double *A = reinterpret_cast<double *>(static_cast<char *>(workspace) + 256);
   double *X = A + np * np;
   hipLaunchKernelGGL(k_gptq_lambda, dim3(1), dim3(256), 0, st, H, n, damp, hdr, stat);
-  hipLaunchKernelGGL(k_gptq_load_h, dim3(grid_for(np * np)), dim3(256), 0, st, H, n, np, hdr, A);
+  hipLaunchKernelGGL(k_gptq_load_h, dim3(grid_for(np * np)), dim3(256), 0, st, H, n, np, hdr, A, X);
   for (int64_t k = 0; k < nb; ++k) {
     const int64_t T = nb - k - 1;
     hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(256), 0, st, A, np, k, stat);
@@ -392,10 +572,17 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
     int64_t g = groups;
     if (groups * 2 * s - s >= np) --g;  // the last group has no C range
     if (g <= 0) continue;
-    const int64_t nbs = s / DB;
-    const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
-    hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 0);
-    hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 1);
+    if (s >= T2) {
+      const int64_t nbs = s / T2;
+      const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
+      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(256), 0, st, A, X, np, s, 0);
+      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(256), 0, st, A, X, np, s, 1);
+    } else {
+      const int64_t nbs = s / DB;
+      const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
+      hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 0);
+      hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 1);
+    }
   }
   hipLaunchKernelGGL(k_gptq_store_u, dim3(grid_for(n * n)), dim3(256), 0, st, X, n, np, U);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
@@ -540,10 +727,26 @@ __global__ void __launch_bounds__(256)
   dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
 }
 
+// V[:, 128-column tiles from c_start] -= E[:, 0 .. kc) U[k0 .. k0 + kc, those columns], with
+// rows of U at or beyond n counting as zero (the outer update: kc = 256)
+__global__ void __launch_bounds__(256)
+    k_gptq_update2(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
+                   const double *__restrict__ E, int64_t k0, int kc, int64_t c_start) {
+  __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
+  const int64_t r0 = (int64_t)blockIdx.x * T2, c0 = c_start + (int64_t)blockIdx.y * T2;
+  const int nlim = (int)(n - c0 < T2 ? n - c0 : T2);
+  const int64_t klim = n - k0 < kc ? n - k0 : kc;
+  DAcc2 acc;
+  d2_zero(acc);
+  d2_gemm<true>(acc, E + r0 * OB, OB, T2, U + k0 * n + c0, n, nlim, kc, klim, L2);
+  double *C = V + r0 * np + c0;
+  d2_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
+}
+
 int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const float *S,
                      const uint8_t *scales, const double *U, uint8_t *codes, void *workspace,
                      hipStream_t st) {
-  const int64_t rp = pad64(rows), np = pad64(n), nbc = np / DB;
+  const int64_t rp = pad128(rows), np = pad128(n), nbc = pad64(n) / DB;
   double *V = static_cast<double *>(workspace);
   double *E = V + rp * np;
   if (dtype == NVFP4_DTYPE_BF16)
@@ -563,8 +766,8 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
       hipLaunchKernelGGL(k_gptq_update, dim3(rgrid, (unsigned)(ob_end - b - 1)), dim3(256), 0, st,
                          V, np, n, U, E, (int64_t)(b % 4) * DB, b * DB, DB, b + 1);
     if (b + 1 == ob_end && ob_end < nbc)
-      hipLaunchKernelGGL(k_gptq_update, dim3(rgrid, (unsigned)(nbc - ob_end)), dim3(256), 0, st,
-                         V, np, n, U, E, (int64_t)0, (b / 4) * OB, OB, ob_end);
+      hipLaunchKernelGGL(k_gptq_update2, dim3((unsigned)(rp / T2), (unsigned)((np - ob_end * DB) / T2)),
+                         dim3(256), 0, st, V, np, n, U, E, (b / 4) * OB, OB, ob_end * DB);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
