@@ -263,6 +263,31 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = 2 * (1 << 30) / (min(a.elapsed_time(b) for a, b in ce) * 1e-3) / 1e9
 
+    # peak rates this device sustains: loops of independent MFMA / VALU instructions (a
+    # separate probe library), two workgroups of four waves per CU
+    probe_rates = {}
+    if not args.no_copy:
+        pl = ctypes.CDLL(os.path.join(os.path.dirname(nvfp4.__file__), "libnvfp4_probe.so"))
+        pl.nvfp4_probe_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        blocks = 2 * cus
+        pbuf = torch.empty(blocks * 256, dtype=torch.float64, device=dev)
+        # kind: (name, work per wave instruction, iterations); 8 instructions per iteration
+        for kind, (name, per_inst, iters) in enumerate((("mfma_f64_tflops", 2048, 2000),
+                                                         ("mfma_bf16_tflops", 32768, 4000),
+                                                         ("mfma_f32_tflops", 2048, 4000),
+                                                         ("valu_lane_tops", 64, 40000))):
+            ok(pl.nvfp4_probe_run(kind, blocks, iters, P(pbuf), sptr), "probe")
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            ok(pl.nvfp4_probe_run(kind, blocks, iters, P(pbuf), sptr), "probe")
+            e1.record(st)
+            torch.cuda.synchronize()
+            work = per_inst * 8.0 * iters * blocks * 4
+            probe_rates[name] = round(work / (e0.elapsed_time(e1) * 1e-3) / 1e12, 2)
+
     # ---------------------------------------------------------------- figures
     fq_bytes = r2 * c2 * FQ_BYTES_PER_ELEM
     fq_gbs = fq_bytes / (ms["fakequant_act"] * 1e-3) / 1e9
@@ -313,6 +338,19 @@ def main():
                        "TFLOP/s"),
     }
 
+    def measured_peak(r):
+        if r["bound"] == "hbm":
+            return copy_gbs
+        if r["bound"] == "alu":
+            return probe_rates.get("valu_lane_tops")
+        return {BF16_MFMA_TFLOPS: probe_rates.get("mfma_bf16_tflops"),
+                FP32_MFMA_TFLOPS: probe_rates.get("mfma_f32_tflops"),
+                FP64_TFLOPS: probe_rates.get("mfma_f64_tflops")}.get(r["peak"])
+
+    for r in rooflines.values():
+        mp = measured_peak(r)
+        r["frac_of_measured"] = None if not mp else round(r["achieved"] / mp, 4)
+
     out = {
         "metric": "NVFP4 fake-quant GB/s + Local-Hessian blocks/s, % of MI355X roofline",
         "value": round(fq_gbs, 2),
@@ -347,9 +385,10 @@ def main():
         "copy_1GiB_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "measured_peaks": None if copy_gbs is None else {
             "hbm_copy_gbs": round(copy_gbs, 1),
-            "fakequant_frac_of_copy": round(fq_gbs / copy_gbs, 4),
-            "note": "a plain 1 GiB device copy after the step, same process; VALU and MFMA "
-                    "peaks are the datasheet figures"},
+            **probe_rates,
+            "note": "measured after the step in the same process: a plain 1 GiB device copy, "
+                    "and loops of independent MFMA / non-packed VALU instructions (two "
+                    "4-wave workgroups per CU); rooflines[*].frac_of_measured divides by these"},
         "setup_s": round(t_setup, 1),
     }
 

@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libnvfp4.so")
+PROBE_OUT = os.path.join(PKG, "libnvfp4_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["nvfp4_api.hip", "nvfp4_quant.hip", "nvfp4_search.hip", "nvfp4_hessian.hip",
            "nvfp4_calib.hip", "nvfp4_ste.hip", "nvfp4_gram.hip", "nvfp4_gptq.hip", "nvfp4_debug.hip"]
@@ -35,6 +36,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    os.makedirs(os.path.dirname(obj), exist_ok=True)
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -54,6 +56,15 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, OUT)
     if verbose:
         print("built", OUT)
+    # peak-rate probes used by the benchmark only (a separate library, not the C ABI)
+    pobj = _compile(os.path.join("probe", "nvfp4_probe.hip"))
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", pobj, "-o", PROBE_OUT + ".tmp"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_OUT + ".tmp", PROBE_OUT)
+    if verbose:
+        print("built", PROBE_OUT)
     return OUT
 
 
