@@ -130,25 +130,27 @@ __device__ __forceinline__ void dacc_each(const DAcc &acc, F f) {
         f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 32 + j * 16 + (lane & 15), acc.c[i][j][r]);
 }
 
-// Wide tiles: a workgroup of 4 waves owns a 128 x 128 output tile (each wave 64 x 64, as
-// 4 x 4 MFMA tiles), K in chunks of 32 staged through LDS (the next chunk's global loads
+// Wide tiles: a workgroup of 8 waves owns a 128 x 128 output tile (each wave 32 x 64, as
+// 2 x 4 MFMA tiles), K in chunks of 32 staged through LDS (the next chunk's global loads
 // are in flight while the current one is multiplied). Four times the work of a 64 x 64
-// tile per byte loaded.
+// tile per byte loaded; small enough per wave (registers, 66 KiB of LDS per workgroup) for
+// two workgroups per CU.
 constexpr int T2 = 128;     // wide tile edge
 constexpr int KC = 32;      // K chunk
 constexpr int P2 = T2 + 1;  // LDS pitch (doubles)
+constexpr int W2T = 512;    // threads of a wide-tile workgroup
 
 struct DAcc2 {
-  gq_v4d c[4][4];
+  gq_v4d c[2][4];
 };
 
 struct DStage {
-  double2 a[8], b[8];
+  double2 a[4], b[4];
 };
 
 __device__ __forceinline__ void d2_zero(DAcc2 &a) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) a.c[i][j] = (gq_v4d){0.0, 0.0, 0.0, 0.0};
 }
@@ -156,8 +158,8 @@ __device__ __forceinline__ void d2_zero(DAcc2 &a) {
 // A chunk: element (m, k) at A[m * lda + k], m < 128, k < 32; zero outside m < mlim, k < klim
 __device__ __forceinline__ void d2_load_a(DStage &st, const double *A, int64_t lda, int mlim, int klim) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = s * 256 + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
+  for (int s = 0; s < 4; ++s) {
+    const int idx = s * W2T + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
     st.a[s] = (m < mlim && k < klim) ? *reinterpret_cast<const double2 *>(A + (int64_t)m * lda + k)
                                      : make_double2(0.0, 0.0);
   }
@@ -165,8 +167,8 @@ __device__ __forceinline__ void d2_load_a(DStage &st, const double *A, int64_t l
 
 __device__ __forceinline__ void d2_store_a(const DStage &st, double *LA) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = s * 256 + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
+  for (int s = 0; s < 4; ++s) {
+    const int idx = s * W2T + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
     LA[k * P2 + m] = st.a[s].x;
     LA[(k + 1) * P2 + m] = st.a[s].y;
   }
@@ -176,8 +178,8 @@ __device__ __forceinline__ void d2_store_a(const DStage &st, double *LA) {
 template <bool KN>
 __device__ __forceinline__ void d2_load_b(DStage &st, const double *B, int64_t ldb, int klim, int nlim) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = s * 256 + threadIdx.x;
+  for (int s = 0; s < 4; ++s) {
+    const int idx = s * W2T + threadIdx.x;
     if (KN) {
       const int k = idx >> 6, n = (idx & 63) * 2;
       st.b[s] = (k < klim && n < nlim) ? *reinterpret_cast<const double2 *>(B + (int64_t)k * ldb + n)
@@ -193,8 +195,8 @@ __device__ __forceinline__ void d2_load_b(DStage &st, const double *B, int64_t l
 template <bool KN>
 __device__ __forceinline__ void d2_store_b(const DStage &st, double *LB) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = s * 256 + threadIdx.x;
+  for (int s = 0; s < 4; ++s) {
+    const int idx = s * W2T + threadIdx.x;
     if (KN) {
       const int k = idx >> 6, n = (idx & 63) * 2;
       LB[k * P2 + n] = st.b[s].x;
@@ -209,17 +211,17 @@ __device__ __forceinline__ void d2_store_b(const DStage &st, double *LB) {
 
 __device__ __forceinline__ void d2_mma(DAcc2 &acc, const double *LA, const double *LB) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 1, wc = wave & 1;  // 32 rows x 64 columns per wave
 #pragma unroll 2
   for (int kk = 0; kk < KC / 4; ++kk) {
     const int kr = kk * 4 + (lane >> 4);
-    double a[4], b[4];
+    double a[2], b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = LA[kr * P2 + wr * 64 + i * 16 + (lane & 15)];
+    for (int i = 0; i < 2; ++i) a[i] = LA[kr * P2 + wr * 32 + i * 16 + (lane & 15)];
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = LB[kr * P2 + wc * 64 + j * 16 + (lane & 15)];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc.c[i][j], 0, 0, 0);
@@ -266,12 +268,12 @@ __device__ __forceinline__ void d2_each(const DAcc2 &acc, F f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        f(wr * 64 + i * 16 + (lane >> 4) + 4 * r, wc * 64 + j * 16 + (lane & 15), acc.c[i][j][r]);
+        f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 64 + j * 16 + (lane & 15), acc.c[i][j][r]);
 }
 
 // ------------------------------------------------------------------ factor
@@ -503,7 +505,7 @@ __global__ void __launch_bounds__(256)
 
 // The same level with 128 x 128 output tiles (levels s >= 128). Whole tiles of X[A][A] and
 // X[C][C] are read, so X's upper triangle must be zero (it is).
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(W2T)
     k_trtri_level2(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
                    int phase) {
   __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
@@ -575,8 +577,8 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
     if (s >= T2) {
       const int64_t nbs = s / T2;
       const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
-      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(256), 0, st, A, X, np, s, 0);
-      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(256), 0, st, A, X, np, s, 1);
+      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(W2T), 0, st, A, X, np, s, 0);
+      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(W2T), 0, st, A, X, np, s, 1);
     } else {
       const int64_t nbs = s / DB;
       const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
@@ -729,7 +731,7 @@ __global__ void __launch_bounds__(256)
 
 // V[:, 128-column tiles from c_start] -= E[:, 0 .. kc) U[k0 .. k0 + kc, those columns], with
 // rows of U at or beyond n counting as zero (the outer update: kc = 256)
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(W2T)
     k_gptq_update2(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
                    const double *__restrict__ E, int64_t k0, int kc, int64_t c_start) {
   __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
@@ -767,7 +769,7 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
                          V, np, n, U, E, (int64_t)(b % 4) * DB, b * DB, DB, b + 1);
     if (b + 1 == ob_end && ob_end < nbc)
       hipLaunchKernelGGL(k_gptq_update2, dim3((unsigned)(rp / T2), (unsigned)((np - ob_end * DB) / T2)),
-                         dim3(256), 0, st, V, np, n, U, E, (b / 4) * OB, OB, ob_end * DB);
+                         dim3(W2T), 0, st, V, np, n, U, E, (b / 4) * OB, OB, ob_end * DB);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
