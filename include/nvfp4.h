@@ -272,10 +272,12 @@ NVFP4_API int nvfp4_gptq(const void *w, int dtype, int64_t rows, int64_t cols, c
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Input checks for debugging. Inputs must be finite; NaN or infinite inputs give
- * unspecified (but memory-safe) results. With the environment variable NVFP4_DEBUG_CHECKS=1,
- * every entry point that reads floating-point tensors (x, w, grad, H) first scans them on
- * its stream and raises a device-side flag if any value is NaN or infinite.
+ * Input checks for debugging. Inputs must be finite and tensor scales S positive and
+ * finite; other inputs give unspecified (but memory-safe) results. S lives in device memory,
+ * so host-side validation cannot see it. With the environment variable NVFP4_DEBUG_CHECKS=1,
+ * every entry point that reads floating-point tensors (x, w, grad, H) or S first scans them
+ * on its stream and raises a device-side flag if any value is NaN or infinite, or any S is
+ * not a positive finite number.
  * nvfp4_debug_nonfinite synchronises `stream`, writes the flag (0 or 1) to *flag_out (host
  * memory) and clears it; it returns NVFP4_ERR_ARG when NVFP4_DEBUG_CHECKS is not 1. The
  * flag is shared by all callers in the process.

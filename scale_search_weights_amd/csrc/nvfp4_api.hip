@@ -74,6 +74,7 @@ int nvfp4_scale_search_max(const void *w, int dtype, int64_t batch, int64_t rows
   if (!w || !S || !scales) return NVFP4_ERR_NULL;
   if (!aligned(w, 16) || !aligned(S, 4)) return NVFP4_ERR_ALIGN;
   debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
+  debug_check_scale(S, batch, as_stream(stream));
   return launch_quant(w, dtype, batch, rows, cols, S, nullptr, nullptr, scales, nullptr,
                       as_stream(stream));
 }
@@ -87,6 +88,7 @@ int nvfp4_scale_search_mse(const void *w, int dtype, int64_t batch, int64_t rows
   if (!aligned(w, 16) || !aligned(S, 4) || !aligned(obj, 4)) return NVFP4_ERR_ALIGN;
   if (rows * (cols / 16) / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
   debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
+  debug_check_scale(S, batch, as_stream(stream));
   return launch_mse(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
 }
 
@@ -100,6 +102,7 @@ int nvfp4_scale_search_four_over_six(const void *w, int dtype, int64_t batch, in
   if (!aligned(w, 16) || !aligned(S, 4) || !aligned(obj, 4)) return NVFP4_ERR_ALIGN;
   if (rows * (cols / 16) / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
   debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
+  debug_check_scale(S, batch, as_stream(stream));
   return launch_four_over_six(w, dtype, batch, rows, cols, S, scales, obj, as_stream(stream));
 }
 
@@ -190,6 +193,7 @@ int nvfp4_scale_search_local_hessian(const void *w, int dtype, int64_t batch, in
   if (cols / 16 > kMaxGridY || rows / 256 + 1 > (int64_t)UINT_MAX) return NVFP4_ERR_SHAPE;
   debug_check_finite(w, dtype, batch * rows * cols, as_stream(stream));
   debug_check_finite(H, NVFP4_DTYPE_F32, batch * (cols / 16) * 256, as_stream(stream));
+  debug_check_scale(S, batch, as_stream(stream));
   return launch_local_hessian(w, dtype, batch, rows, cols, S, H, scales, obj, as_stream(stream));
 }
 
@@ -202,6 +206,7 @@ int nvfp4_quantize(const void *x, int dtype, int64_t batch, int64_t rows, int64_
   if (!x || !S || !codes) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(S, 4) || !aligned(codes, 8)) return NVFP4_ERR_ALIGN;
   debug_check_finite(x, dtype, batch * rows * cols, as_stream(stream));
+  debug_check_scale(S, batch, as_stream(stream));
   return launch_quant(x, dtype, batch, rows, cols, S, scales_in, codes,
                       scales_in ? nullptr : scales_out, nullptr, as_stream(stream));
 }
@@ -213,6 +218,7 @@ int nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *S
   if (rc != NVFP4_OK || empty) return rc;
   if (!codes || !scales || !S || !y) return NVFP4_ERR_NULL;
   if (!aligned(codes, 8) || !aligned(S, 4) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  debug_check_scale(S, batch, as_stream(stream));
   return launch_dequant(codes, scales, S, batch, rows, cols, y, out_dtype, as_stream(stream));
 }
 
@@ -226,6 +232,7 @@ int nvfp4_fakequant(const void *x, int dtype, int64_t batch, int64_t rows, int64
   if (!aligned(x, 16) || !aligned(S, 4) || !aligned(y, 16) || !aligned(codes_out, 8))
     return NVFP4_ERR_ALIGN;
   debug_check_finite(x, dtype, batch * rows * cols, as_stream(stream));
+  debug_check_scale(S, batch, as_stream(stream));
   return launch_quant(x, dtype, batch, rows, cols, S, scales_in, codes_out,
                       scales_in ? nullptr : scales_out, y, as_stream(stream));
 }
@@ -317,6 +324,7 @@ int nvfp4_gptq(const void *w, int dtype, int64_t rows, int64_t cols, const float
   if (!workspace || workspace_bytes < gptq_rows_workspace_size(rows, cols)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   debug_check_finite(w, dtype, rows * cols, as_stream(stream));
+  debug_check_scale(S, 1, as_stream(stream));
   return launch_gptq_rows(w, dtype, rows, cols, S, scales, U, codes, workspace, as_stream(stream));
 }
 

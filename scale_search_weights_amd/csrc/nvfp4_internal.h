@@ -38,6 +38,7 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
 
 bool debug_checks_enabled();
 void debug_check_finite(const void *x, int dtype, int64_t n, hipStream_t st);
+void debug_check_scale(const float *S, int64_t n, hipStream_t st);
 int debug_read_flag(int32_t *out, hipStream_t st);
 
 size_t gram_workspace_size(int64_t tokens, int64_t cols);

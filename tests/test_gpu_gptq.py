@@ -185,3 +185,27 @@ def test_gptq_end_to_end(orc):
     deq = lambda c: orc.dequantize(c, sc, S, rows, cols).astype(np.float64) - wn
     err = lambda c: np.einsum("ri,ij,rj->", deq(c), Href, deq(c))
     assert err(got.cpu().numpy()) < 0.95 * err(orc.quantize(wn, S, sc))
+
+
+@pytest.mark.parametrize("scale", [1e-20, 1e20])
+def test_gptq_rows_extreme_magnitudes(orc, scale):
+    """Everything stays in double: tiny and huge weights round the same way on both sides."""
+    case(f"gptq rows with weights x{scale:g}")
+    w0, x = synth.projection(18, rows=32, cols=128, tokens=500)
+    wn = (f32(w0).astype(np.float64) * scale).astype(np.float32)
+    S = orc.tensor_scale(wn)
+    H = orc.full_hessian(f32(x)).astype(np.float32)
+    sc = orc.scales_mse(wn, S)
+    Ur = orc.gptq_factor(H.astype(np.float64), 0.01)
+    want, v_ref = orc.gptq(wn, S, sc, U=Ur, return_v=True)
+    got = nvfp4.gptq(torch.from_numpy(wn).to(DEV), torch.tensor([S], device=DEV),
+                     torch.from_numpy(sc).to(DEV), torch.from_numpy(Ur).to(DEV))
+    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9)
+
+
+def test_full_hessian_smallest_shapes(orc):
+    case("full hessian: one token, 16 channels; 3 tokens, 48 channels")
+    for tokens, cols in ((1, 16), (3, 48)):
+        x = torch.from_numpy(np.random.default_rng(cols).standard_normal((tokens, cols)).astype(np.float32))
+        Hn = nvfp4.full_hessian(x.to(DEV)).cpu().numpy()
+        assert block_rel_frob(Hn, orc.full_hessian(f32(x))) <= 1e-6

@@ -600,6 +600,11 @@ def test_debug_nonfinite_flag(monkeypatch):
     xh[50, 7] = float("inf")
     nvfp4.block_hessian(xh)
     assert nvfp4.debug_nonfinite() is True
+    xq = synth.activation(32, 16, 64).to(DEV)
+    nvfp4.quantize(xq, dev_S(0.0))                    # a non-positive tensor scale
+    assert nvfp4.debug_nonfinite() is True
+    nvfp4.quantize(xq, dev_S(1e-3))
+    assert nvfp4.debug_nonfinite() is False
     monkeypatch.delenv("NVFP4_DEBUG_CHECKS")
     with pytest.raises(nvfp4.NVFP4Error):
         nvfp4.debug_nonfinite()

@@ -124,3 +124,17 @@ def test_module_running_scale(orc):
     y = mod(x.to(DEV))
     assert mod.scale.cpu().numpy().view(np.uint32)[0] == S_ref.view(np.uint32)[0]
     assert_same(y, orc.fakequant(f32(x), S_ref[0])[0], orc)
+
+
+def test_module_mse_selector(orc):
+    case("NVFP4FakeQuant with the MSE selector, eval mode on a fixed scale")
+    mod = ste.NVFP4FakeQuant(selector="mse").to(DEV)
+    w = synth.projection(3, rows=32, cols=256, tokens=16)[0]
+    wn = f32(w)
+    S = orc.tensor_scale(wn)
+    mod.scale.fill_(float(S))
+    mod.initialised.fill_(True)
+    mod.eval()
+    y = mod(w.to(DEV))
+    assert mod.scale.item() == S
+    assert_same(y, orc.fakequant(wn, S, orc.scales_mse(wn, S))[0], orc)
