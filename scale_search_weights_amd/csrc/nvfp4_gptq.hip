@@ -14,7 +14,8 @@
 //    if J (H + lambda I) J = L L^T then H + lambda I = R R^T with R = J L J upper, and
 //    U = R^-1 = J L^-1 J. Blocked right-looking Cholesky (64 x 64 blocks: per step, each
 //    workgroup factors the diagonal block in one wave's registers and solves one panel
-//    block, fp64 MFMA updates the trailing matrix), then a bottom-up recursive inverse
+//    block; steps go in pairs, and after each pair one fp64 MFMA product with K = 128
+//    updates the trailing matrix), then a bottom-up recursive inverse
 //    [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] (two fp64 MFMA products per level).
 //  * rows: the column loop in blocks of 64 columns. In a block, sixteen lanes share a row,
 //    each holding 4 of its values in registers; for every column the owning lane rounds,
@@ -130,35 +131,35 @@ __device__ __forceinline__ void dacc_each(const DAcc &acc, F f) {
         f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 32 + j * 16 + (lane & 15), acc.c[i][j][r]);
 }
 
-// Wide tiles: a workgroup of 8 waves owns a 128 x 128 output tile (each wave 32 x 64, as
-// 2 x 4 MFMA tiles), K in chunks of 32 staged through LDS (the next chunk's global loads
-// are in flight while the current one is multiplied). Four times the work of a 64 x 64
-// tile per byte loaded; small enough per wave (registers, 66 KiB of LDS per workgroup) for
-// two workgroups per CU.
+// Wide tiles: a workgroup of 16 waves owns a 128 x 128 output tile (each wave 32 x 32, as
+// 2 x 2 MFMA tiles), K in chunks of 32 staged through one 66 KiB LDS buffer (the next
+// chunk's global loads are in flight while the current one is multiplied). Four times the
+// work of a 64 x 64 tile per byte loaded; four waves per SIMD hide the loads and barriers
+// (eight waves of 32 x 64 were 5% slower, four of 64 x 64 another 15%).
 constexpr int T2 = 128;     // wide tile edge
 constexpr int KC = 32;      // K chunk
 constexpr int P2 = T2 + 1;  // LDS pitch (doubles)
-constexpr int W2T = 512;    // threads of a wide-tile workgroup
+constexpr int W2T = 1024;  // threads of a wide-tile workgroup
 
 struct DAcc2 {
-  gq_v4d c[2][4];
+  gq_v4d c[2][2];
 };
 
 struct DStage {
-  double2 a[4], b[4];
+  double2 a[2], b[2];
 };
 
 __device__ __forceinline__ void d2_zero(DAcc2 &a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a.c[i][j] = (gq_v4d){0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < 2; ++j) a.c[i][j] = (gq_v4d){0.0, 0.0, 0.0, 0.0};
 }
 
 // A chunk: element (m, k) at A[m * lda + k], m < 128, k < 32; zero outside m < mlim, k < klim
 __device__ __forceinline__ void d2_load_a(DStage &st, const double *A, int64_t lda, int mlim, int klim) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < 2; ++s) {
     const int idx = s * W2T + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
     st.a[s] = (m < mlim && k < klim) ? *reinterpret_cast<const double2 *>(A + (int64_t)m * lda + k)
                                      : make_double2(0.0, 0.0);
@@ -167,7 +168,7 @@ __device__ __forceinline__ void d2_load_a(DStage &st, const double *A, int64_t l
 
 __device__ __forceinline__ void d2_store_a(const DStage &st, double *LA) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < 2; ++s) {
     const int idx = s * W2T + threadIdx.x, m = idx >> 4, k = (idx & 15) * 2;
     LA[k * P2 + m] = st.a[s].x;
     LA[(k + 1) * P2 + m] = st.a[s].y;
@@ -178,7 +179,7 @@ __device__ __forceinline__ void d2_store_a(const DStage &st, double *LA) {
 template <bool KN>
 __device__ __forceinline__ void d2_load_b(DStage &st, const double *B, int64_t ldb, int klim, int nlim) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < 2; ++s) {
     const int idx = s * W2T + threadIdx.x;
     if (KN) {
       const int k = idx >> 6, n = (idx & 63) * 2;
@@ -195,7 +196,7 @@ __device__ __forceinline__ void d2_load_b(DStage &st, const double *B, int64_t l
 template <bool KN>
 __device__ __forceinline__ void d2_store_b(const DStage &st, double *LB) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < 2; ++s) {
     const int idx = s * W2T + threadIdx.x;
     if (KN) {
       const int k = idx >> 6, n = (idx & 63) * 2;
@@ -211,19 +212,19 @@ __device__ __forceinline__ void d2_store_b(const DStage &st, double *LB) {
 
 __device__ __forceinline__ void d2_mma(DAcc2 &acc, const double *LA, const double *LB) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;  // 32 rows x 64 columns per wave
+  const int wr = wave >> 2, wc = wave & 3;  // 32 x 32 per wave
 #pragma unroll 2
   for (int kk = 0; kk < KC / 4; ++kk) {
     const int kr = kk * 4 + (lane >> 4);
-    double a[2], b[4];
+    double a[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) a[i] = LA[kr * P2 + wr * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = LB[kr * P2 + wc * 64 + j * 16 + (lane & 15)];
+    for (int j = 0; j < 2; ++j) b[j] = LB[kr * P2 + wc * 32 + j * 16 + (lane & 15)];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc.c[i][j], 0, 0, 0);
   }
 }
@@ -266,14 +267,14 @@ __device__ __forceinline__ void d2_gemm(DAcc2 &acc, const double *A, int64_t lda
 template <class F>
 __device__ __forceinline__ void d2_each(const DAcc2 &acc, F f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 64 + j * 16 + (lane & 15), acc.c[i][j][r]);
+        f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 32 + j * 16 + (lane & 15), acc.c[i][j][r]);
 }
 
 // ------------------------------------------------------------------ factor
@@ -418,25 +419,19 @@ __global__ void __launch_bounds__(256)
   for (int j = 0; j < 16; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
 }
 
-// trailing update after step k: A[bi][bj] -= L[bi][k] L[bj][k]^T for k < bj <= bi
+// column block k + 1 only: A[bi][k+1] -= L[bi][k] L[k+1][k]^T for bi >= k + 1 (what step
+// k + 1 needs before the paired trailing update)
 __global__ void __launch_bounds__(256)
-    k_chol_update(double *__restrict__ A, int64_t np, int64_t k) {
+    k_chol_colupd(double *__restrict__ A, int64_t np, int64_t k) {
   __shared__ double LA[DB * DP], LB[DB * DP];
-  int64_t e = blockIdx.x, bi = 0;
-  while (e > bi) {  // lower-triangular enumeration: row bi holds bi + 1 blocks
-    e -= bi + 1;
-    ++bi;
-  }
-  const int64_t bj = e;
-  bi += k + 1;
-  const int64_t bjj = bj + k + 1;
+  const int64_t bi = k + 1 + blockIdx.x, bj = k + 1;
   dload_mk(LA, A + bi * DB * np + k * DB, np, DB, DB);
-  dload_mk(LB, A + bjj * DB * np + k * DB, np, DB, DB);
+  dload_mk(LB, A + bj * DB * np + k * DB, np, DB, DB);
   __syncthreads();
   DAcc acc;
   dacc_zero(acc);
   dmma(acc, LA, LB);
-  double *C = A + bi * DB * np + bjj * DB;
+  double *C = A + bi * DB * np + bj * DB;
   dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
 }
 
@@ -552,6 +547,27 @@ static unsigned grid_for(int64_t elems) {
   return (unsigned)(g > 0 ? g : 1);
 }
 
+// trailing update after a pair of steps: for the lower-triangular 128 x 128 tiles of the
+// matrix from row / column c on, A[I][J] -= L[I][k0 .. k0 + 128) L[J][k0 .. k0 + 128)^T
+__global__ void __launch_bounds__(W2T)
+    k_chol_update2(double *__restrict__ A, int64_t np, int64_t c, int64_t k0) {
+  __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
+  int64_t e = blockIdx.x, ti = 0;
+  while (e > ti) {  // lower-triangular enumeration: tile row ti holds ti + 1 tiles
+    e -= ti + 1;
+    ++ti;
+  }
+  const int64_t I = c + ti * T2, J = c + e * T2;
+  const int mlim = (int)(np - I < T2 ? np - I : T2), nlim = (int)(np - J < T2 ? np - J : T2);
+  DAcc2 acc;
+  d2_zero(acc);
+  d2_gemm<false>(acc, A + I * np + k0, np, mlim, A + J * np + k0, np, nlim, 2 * DB, 2 * DB, L2);
+  double *C = A + I * np + J;
+  d2_each(acc, [&](int r, int cc, double v) {
+    if (r < mlim && cc < nlim) C[r * np + cc] -= v;
+  });
+}
+
 int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_t *status,
                        void *workspace, hipStream_t st) {
   const int64_t np = pad64(n), nb = np / DB;
@@ -561,12 +577,19 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   double *X = A + np * np;
   hipLaunchKernelGGL(k_gptq_lambda, dim3(1), dim3(256), 0, st, H, n, damp, hdr, stat);
   hipLaunchKernelGGL(k_gptq_load_h, dim3(grid_for(np * np)), dim3(256), 0, st, H, n, np, hdr, A, X);
-  for (int64_t k = 0; k < nb; ++k) {
+  // steps in pairs: step k, column block k + 1, step k + 1, then one trailing update with
+  // K = 128 over the 128-aligned rest (128 x 128 tiles); an odd last step stands alone
+  for (int64_t k = 0; k < nb; k += 2) {
     const int64_t T = nb - k - 1;
     hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(256), 0, st, A, np, k, stat);
-    if (T > 0)
-      hipLaunchKernelGGL(k_chol_update, dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0, st, A,
-                         np, k);
+    if (T == 0) break;
+    hipLaunchKernelGGL(k_chol_colupd, dim3((unsigned)T), dim3(256), 0, st, A, np, k);
+    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)T), dim3(256), 0, st, A, np, k + 1, stat);
+    const int64_t c = (k + 2) * DB;
+    if (c >= np) break;
+    const int64_t t2 = (np - c + T2 - 1) / T2;
+    hipLaunchKernelGGL(k_chol_update2, dim3((unsigned)(t2 * (t2 + 1) / 2)), dim3(W2T), 0, st, A,
+                       np, c, k * DB);
   }
   hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, A, X, np);
   for (int64_t s = DB; s < np; s *= 2) {
