@@ -373,8 +373,12 @@ __global__ void __launch_bounds__(256)
       const int phi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j);
       const double piv = __hiloint2double(phi, plo);
       bad |= !(piv > 0.0);
-      const double ljj = sqrt(piv);
-      const double rl = 1.0 / ljj;
+      // 1 / sqrt(piv): the hardware estimate and two Newton steps (about 1 ulp), off the
+      // longer sqrt and divide sequences on this step's critical path
+      double rl = __builtin_amdgcn_rsq(piv);
+      rl = rl * __builtin_fma(-0.5 * piv * rl, rl, 1.5);
+      rl = rl * __builtin_fma(-0.5 * piv * rl, rl, 1.5);
+      const double ljj = piv * rl;
       d[j] = i == j ? ljj : d[j] * rl;      // right of the diagonal, d holds unused values
       Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
       if (i == j) rinv[j] = rl;
