@@ -382,6 +382,13 @@ def test_calib_histogram_and_scale(orc, which):
         assert S.item() == orc.calib_scale(href, frac), frac
 
 
+def test_calib_scale_empty_histogram(orc):
+    case("calibration scale of an empty histogram")
+    h = torch.zeros(nvfp4.CALIB_BINS, dtype=torch.int64, device=DEV)
+    for frac in (0.5, 1.0):
+        assert nvfp4.calib_scale(h, frac).item() == orc.calib_scale(np.zeros(nvfp4.CALIB_BINS, np.uint64), frac)
+
+
 def test_calib_accumulates_over_batches(orc):
     case("calibration histogram over three batches")
     xs = [synth.activation(s, tokens=64, hidden=1024) for s in (7, 8, 9)]
