@@ -132,8 +132,9 @@ __device__ __forceinline__ void dacc_each(const DAcc &acc, F f) {
 }
 
 // Wide tiles: a workgroup of 16 waves owns a 128 x 128 output tile (each wave 32 x 32, as
-// 2 x 2 MFMA tiles), K in chunks of 32 staged through one 66 KiB LDS buffer (the next
-// chunk's global loads are in flight while the current one is multiplied). Four times the
+// 2 x 2 MFMA tiles), K in chunks of 32 staged through two 66 KiB LDS buffers (the next
+// chunk's global loads are in flight while the current one is multiplied, one barrier per
+// chunk). Four times the
 // work of a 64 x 64 tile per byte loaded; four waves per SIMD hide the loads and barriers
 // (eight waves of 32 x 64 were 5% slower, four of 64 x 64 another 15%).
 constexpr int T2 = 128;     // wide tile edge
@@ -230,8 +231,8 @@ __device__ __forceinline__ void d2_mma(DAcc2 &acc, const double *LA, const doubl
 }
 
 // acc += A[0:128, 0:K] B[0:K, 0:128] (A as in d2_load_a; B as in d2_load_b), k < klim and
-// the row / column limits zero-filled. L: one (A, B) chunk buffer, 2 * KC * P2 doubles
-// (66 KiB, so two workgroups share a CU); the next chunk waits in registers.
+// the row / column limits zero-filled. L: two (A, B) chunk buffers, 4 * KC * P2 doubles;
+// the next chunk is loaded into registers during the current one's products.
 template <bool KN>
 __device__ __forceinline__ void d2_gemm(DAcc2 &acc, const double *A, int64_t lda, int mlim,
                                         const double *B, int64_t ldb, int nlim, int64_t K,
@@ -247,19 +248,19 @@ __device__ __forceinline__ void d2_gemm(DAcc2 &acc, const double *A, int64_t lda
   d2_store_b<KN>(st, L + KC * P2);
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
+    double *cur = L + (c & 1) * 2 * KC * P2, *nxt = L + ((c + 1) & 1) * 2 * KC * P2;
     const bool more = c + 1 < nch;
     if (more) {
       const int64_t kb = (int64_t)(c + 1) * KC;
       d2_load_a(st, A + kb, lda, mlim, kl(kb));
       d2_load_b<KN>(st, B + bofs(kb), ldb, kl(kb), nlim);
     }
-    d2_mma(acc, L, L + KC * P2);
+    d2_mma(acc, cur, cur + KC * P2);
     if (more) {
-      __syncthreads();
-      d2_store_a(st, L);
-      d2_store_b<KN>(st, L + KC * P2);
-      __syncthreads();
+      d2_store_a(st, nxt);
+      d2_store_b<KN>(st, nxt + KC * P2);
     }
+    __syncthreads();
   }
 }
 
@@ -507,7 +508,7 @@ __global__ void __launch_bounds__(256)
 __global__ void __launch_bounds__(W2T)
     k_trtri_level2(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
                    int phase) {
-  __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
+  __shared__ __attribute__((aligned(16))) double L2[4 * KC * P2];  // two (A, B) chunk buffers
   const int64_t a0 = (int64_t)blockIdx.x * 2 * s, c0 = a0 + s;
   const int64_t sc = np - c0 < s ? np - c0 : s;
   const int64_t nbs = s / T2;
@@ -555,7 +556,7 @@ static unsigned grid_for(int64_t elems) {
 // matrix from row / column c on, A[I][J] -= L[I][k0 .. k0 + 128) L[J][k0 .. k0 + 128)^T
 __global__ void __launch_bounds__(W2T)
     k_chol_update2(double *__restrict__ A, int64_t np, int64_t c, int64_t k0) {
-  __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
+  __shared__ __attribute__((aligned(16))) double L2[4 * KC * P2];  // two (A, B) chunk buffers
   int64_t e = blockIdx.x, ti = 0;
   while (e > ti) {  // lower-triangular enumeration: tile row ti holds ti + 1 tiles
     e -= ti + 1;
@@ -761,7 +762,7 @@ __global__ void __launch_bounds__(256)
 __global__ void __launch_bounds__(W2T)
     k_gptq_update2(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
                    const double *__restrict__ E, int64_t k0, int kc, int64_t c_start) {
-  __shared__ __attribute__((aligned(16))) double L2[2 * KC * P2];  // one (A, B) chunk buffer
+  __shared__ __attribute__((aligned(16))) double L2[4 * KC * P2];  // two (A, B) chunk buffers
   const int64_t r0 = (int64_t)blockIdx.x * T2, c0 = c_start + (int64_t)blockIdx.y * T2;
   const int nlim = (int)(n - c0 < T2 ? n - c0 : T2);
   const int64_t klim = n - k0 < kc ? n - k0 : kc;
