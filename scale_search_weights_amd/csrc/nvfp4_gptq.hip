@@ -20,11 +20,11 @@
 //  * rows: the column loop in blocks of 64 columns. In a block, sixteen lanes share a row,
 //    each holding 4 of its values in registers; for every column the owning lane rounds,
 //    forms e and broadcasts it to its row of 16 lanes (DPP row_newbcast), and all of them
-//    update their values with the block's row of U from LDS (e uses 1 / U_jj). Errors reach later columns through
-//    fp64 MFMA products V[:, later] -= E U[done, later] (GPTQ's lazy batch updates), on two
-//    levels: a block's errors update the rest of its 256-column outer block, and each outer
-//    block updates all later columns at once, so the working copy of W is read and written
-//    once per 256 columns.
+//    update their values with the block's row of U from LDS (e uses 1 / U_jj). Errors reach
+//    later columns by GPTQ's lazy batch updates on two levels: the same kernel then applies
+//    the block's errors to the rest of its 256-column outer block, and after each outer block
+//    an fp64 MFMA product V[:, later] -= E U[done, later] updates all later columns at once,
+//    so the working copy of W is read and written once per 256 columns.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -731,30 +731,43 @@ __global__ void __launch_bounds__(256)
   double *er = E + r * OB + (b % 4) * DB + 4 * p;
   *reinterpret_cast<double2 *>(er) = make_double2(ev[0], ev[1]);
   *reinterpret_cast<double2 *>(er + 2) = make_double2(ev[2], ev[3]);
-}
 
-// V[:, column blocks cb0 + blockIdx.y] -= E[:, e0 .. e0 + kc) U[k0 .. k0 + kc, those columns]
-// (rows of U at or beyond n count as zero); one 64 x 64 tile of V per workgroup
-__global__ void __launch_bounds__(256)
-    k_gptq_update(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
-                  const double *__restrict__ E, int64_t e0, int64_t k0, int kc, int64_t cb0) {
-  __shared__ double LA[DB * DP], LB[DB * DP];
-  const int64_t r0 = (int64_t)blockIdx.x * DB, c0 = (cb0 + blockIdx.y) * DB;
-  const int nlim = (int)(n - c0 < DB ? n - c0 : DB);
-  DAcc acc;
-  dacc_zero(acc);
-  for (int kb = 0; kb < kc; kb += DB) {
-    const int64_t kr = k0 + kb;
-    if (kr >= n) break;
-    const int klim = (int)(n - kr < DB ? n - kr : DB);
-    __syncthreads();
-    dload_mk(LA, E + r0 * OB + e0 + kb, OB, DB, DB);
-    dload_kn(LB, U + kr * n + c0, n, klim, nlim);
-    __syncthreads();
-    dmma(acc, LA, LB);
+  // the rest of this 256-column outer block (at most 192 columns, 12 tiles of 16): for this
+  // workgroup's 16 rows, V[:, tile] -= E[:, block] U[block, tile] as 16 fp64 MFMA steps per
+  // tile (K = 4 each); wave w takes tiles w, w + 4, w + 8. A fragments (lane l: row l & 15 at
+  // k = l >> 4) come from LDS ([k][row]); U and V are loaded for all three tiles up front.
+  __shared__ double LE[DB * 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) LE[(4 * p + i) * 16 + (t >> 4)] = ev[i];
+  int64_t c_end = (b / 4 + 1) * OB;
+  if (c_end > n) c_end = n;
+  // n is a multiple of 16; when any tile follows, all 64 rows of U's block are below n
+  const int ntiles = c_end > c0 + DB ? (int)((c_end - c0 - DB) / 16) : 0;
+  const int lane = t & 63, w = t >> 6, lr = lane >> 4, lc = lane & 15;
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  double ub[3][16], vv[3][4];
+#pragma unroll
+  for (int qi = 0; qi < 3; ++qi) {
+    const int q = w + 4 * qi;
+    const int64_t cq = c0 + DB + 16 * q + lc;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) ub[qi][s] = q < ntiles ? U[(c0 + 4 * s + lr) * n + cq] : 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vv[qi][r] = q < ntiles ? V[(r0 + lr + 4 * r) * np + cq] : 0.0;
   }
-  double *C = V + r0 * np + c0;
-  dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
+  __syncthreads();
+#pragma unroll
+  for (int qi = 0; qi < 3; ++qi) {
+    const int q = w + 4 * qi;
+    if (q >= ntiles) break;
+    gq_v4d acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(LE[(4 * s + lr) * 16 + lc], ub[qi][s], acc, 0, 0, 0);
+    const int64_t cq = c0 + DB + 16 * q + lc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) V[(r0 + lr + 4 * r) * np + cq] = vv[qi][r] - acc[r];
+  }
 }
 
 // V[:, 128-column tiles from c_start] -= E[:, 0 .. kc) U[k0 .. k0 + kc, those columns], with
@@ -786,15 +799,12 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
     hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_F32>, dim3(grid_for(rp * np)), dim3(256), 0, st, w,
                        rows, n, rp, np, V);
   // blocks of 64 columns; inside an outer block of 256 a block's errors update only the
-  // rest of that outer block, and each outer block then updates every later column at once
-  const unsigned rgrid = (unsigned)(rp / DB);
+  // rest of that outer block (within k_gptq_block), and each outer block then updates
+  // every later column at once
   for (int64_t b = 0; b < nbc; ++b) {
     hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)(rp / 16)), dim3(256), 0, st, V, np, rows, n, S,
                        scales, U, b, E, codes);
     const int64_t ob_end = (b / 4 + 1) * 4 < nbc ? (b / 4 + 1) * 4 : nbc;  // in blocks
-    if (b + 1 < ob_end)
-      hipLaunchKernelGGL(k_gptq_update, dim3(rgrid, (unsigned)(ob_end - b - 1)), dim3(256), 0, st,
-                         V, np, n, U, E, (int64_t)(b % 4) * DB, b * DB, DB, b + 1);
     if (b + 1 == ob_end && ob_end < nbc)
       hipLaunchKernelGGL(k_gptq_update2, dim3((unsigned)(rp / T2), (unsigned)((np - ob_end * DB) / T2)),
                          dim3(W2T), 0, st, V, np, n, U, E, (b / 4) * OB, OB, ob_end * DB);
