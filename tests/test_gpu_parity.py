@@ -389,6 +389,47 @@ def test_calib_scale_empty_histogram(orc):
         assert nvfp4.calib_scale(h, frac).item() == orc.calib_scale(np.zeros(nvfp4.CALIB_BINS, np.uint64), frac)
 
 
+@pytest.mark.parametrize("layout", ["single_bins", "boundaries", "sparse_random", "dense_random", "huge_counts"])
+def test_calib_scale_synthetic_histograms(orc, layout):
+    """The clip scale from histograms built directly (seeded), with the crossing bin at the
+    first and last bin, at 64-bin row and 2048-bin group edges, and with counts above 2^32."""
+    case(f"calibration scale of synthetic histograms: {layout}")
+    rng = np.random.default_rng(97)
+    B = nvfp4.CALIB_BINS
+    hists = []
+    if layout == "single_bins":
+        for b in (0, 1, 63, 64, 2047, 2048, 16383, 30000, B - 1):
+            h = np.zeros(B, np.uint64)
+            h[b] = 5
+            hists.append(h)
+    elif layout == "boundaries":
+        for edge in (64, 2048, 4096, 30720):
+            h = np.zeros(B, np.uint64)
+            h[edge - 1] = 3
+            h[edge] = 4
+            h[edge + 1] = 1
+            hists.append(h)
+    elif layout == "sparse_random":
+        for _ in range(6):
+            h = np.zeros(B, np.uint64)
+            idx = rng.choice(B, size=40, replace=False)
+            h[idx] = rng.integers(1, 1000, size=40).astype(np.uint64)
+            hists.append(h)
+    elif layout == "dense_random":
+        for _ in range(3):
+            hists.append(rng.integers(0, 50, size=B).astype(np.uint64))
+    else:
+        h = np.zeros(B, np.uint64)
+        h[[100, 16000, 16001, 32000]] = np.array([3 << 33, 1 << 34, 7, 5 << 32], np.uint64)
+        hists.append(h)
+    for h in hists:
+        hd = torch.from_numpy(h.view(np.int64).copy()).to(DEV)
+        for frac in (1e-9, 0.25, 0.5, 0.75, 0.99, 0.9999, 1.0):
+            got, want = np.float32(nvfp4.calib_scale(hd, frac).item()), orc.calib_scale(h, frac)
+            # the top bins hold inf / NaN magnitudes: their clip scale is NaN on both sides
+            assert got == want or (np.isnan(got) and np.isnan(want)), (layout, frac, got, want)
+
+
 def test_calib_accumulates_over_batches(orc):
     case("calibration histogram over three batches")
     xs = [synth.activation(s, tokens=64, hidden=1024) for s in (7, 8, 9)]
