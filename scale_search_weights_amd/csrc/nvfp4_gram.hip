@@ -15,8 +15,10 @@
 // bf16: v_mfma_f32_32x32x16_bf16. A lane's operand is 8 consecutive tokens of one channel,
 // while a token row is contiguous in memory, so each step (64 tokens x 512 channels: the
 // tile's row and column channels) is transposed on the way into LDS: a lane loads 8 token
-// rows x 8 channels (eight 16-byte loads), transposes the 8x8 block of 16-bit values in
-// registers and writes eight 16-byte channel rows. LDS rows are 128 bytes (64 tokens); the
+// rows x 8 channels (eight 16-byte raw buffer loads from scalar descriptors, no address
+// arithmetic per load, rows past the chunk zero-filled by the range check), transposes the
+// 8x8 block of 16-bit values in registers (32 byte permutes) and writes eight 16-byte
+// channel rows. LDS rows are 128 bytes (64 tokens); the
 // 16-byte token groups are XOR-swizzled by (c ^ c >> 3) & 7 so that both the transposing
 // writes (8 lanes = 8 channels 8 apart) and the MFMA reads (8 lanes = 8 adjacent channels)
 // touch 8 distinct bank groups. Any order of tokens inside a K slice is valid as long as
@@ -29,6 +31,7 @@ namespace nvfp4 {
 
 typedef __bf16 gram_v8bf __attribute__((ext_vector_type(8)));
 typedef float gram_v16f __attribute__((ext_vector_type(16)));
+typedef unsigned gram_v4u __attribute__((ext_vector_type(4)));
 
 constexpr int GT = 256;   // output tile edge (channels)
 constexpr int GC = 2 * GT;  // channels staged per step: the tile's row and column channels
@@ -128,26 +131,40 @@ __global__ void __launch_bounds__(GTHREADS)
   // (group g of the step's 8)
   const int q = tid & 63, g = tid >> 6;
   const int64_t chg = q < 32 ? ti * GT + q * 8 : tj * GT + (q - 32) * 8;
-  const bool ch_ok = chg < cols;  // cols % 16 == 0: a group of 8 is all in or all out
+  // cols % 16 == 0: a group of 8 channels is all in or all out. Groups past the last
+  // channel load channels 0..7 instead: they only feed rows and columns of the partial
+  // tile at or beyond cols, which the reduction drops.
+  const int64_t chl = chg < cols ? chg : 0;
+  // Raw buffer loads: token row pos + s + 8 g of the step is row 8 g of a buffer that
+  // starts at token pos + s (a scalar descriptor) and holds only the rows below p1, so
+  // rows past the chunk read as zero; the lane's byte offset (below 2^23) never changes.
+  const int lo_bytes = (int)(((int64_t)(g * 8) * cols + chl) * 2);
   uint4 in[8];
   auto load = [&](int64_t pos) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int64_t tok = pos + g * 8 + s;
-      in[s] = (ch_ok && tok < p1) ? *reinterpret_cast<const uint4 *>(x + tok * cols + chg)
-                                  : make_uint4(0u, 0u, 0u, 0u);
+      int64_t rows = p1 - pos - s;
+      rows = rows < 0 ? 0 : (rows > GK ? GK : rows);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(x + (pos + s) * cols), (short)0, (int)(rows * cols * 2),
+          0x00020000);
+      const gram_v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, lo_bytes, 0, 0);
+      in[s] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
+  // 8x8 transpose of 16-bit values: output channel i of token pair (2e, 2e + 1) takes the
+  // low (even i) or high (odd i) halves of dword i / 2 of both rows (v_perm_b32 byte select)
   auto store = [&](uint16_t *buf) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
       unsigned o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint4 a4 = in[2 * e], b4 = in[2 * e + 1];
         const unsigned a = (i >> 1) == 0 ? a4.x : (i >> 1) == 1 ? a4.y : (i >> 1) == 2 ? a4.z : a4.w;
         const unsigned b = (i >> 1) == 0 ? b4.x : (i >> 1) == 1 ? b4.y : (i >> 1) == 2 ? b4.z : b4.w;
-        o[e] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+        o[e] = __builtin_amdgcn_perm(b, a, sel);  // bytes 0-3 from a, 4-7 from b
       }
       const int c = q * 8 + i;
       *reinterpret_cast<uint4 *>(buf + c * GK + ((g ^ gram_swz(c)) << 3)) =
