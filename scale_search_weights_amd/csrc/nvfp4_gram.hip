@@ -13,16 +13,12 @@
 //    fetches it about four times).
 //
 // bf16: v_mfma_f32_32x32x16_bf16. A lane's operand is 8 consecutive tokens of one channel,
-// while a token row is contiguous in memory, so each step (64 tokens x 512 channels: the
-// tile's row and column channels) is transposed on the way into LDS: a lane loads 8 token
-// rows x 8 channels (eight 16-byte raw buffer loads from scalar descriptors, no address
-// arithmetic per load, rows past the chunk zero-filled by the range check), transposes the
-// 8x8 block of 16-bit values in registers (32 byte permutes) and writes eight 16-byte
-// channel rows. LDS rows are 128 bytes (64 tokens); the
-// 16-byte token groups are XOR-swizzled by (c ^ c >> 3) & 7 so that both the transposing
-// writes (8 lanes = 8 channels 8 apart) and the MFMA reads (8 lanes = 8 adjacent channels)
-// touch 8 distinct bank groups. Any order of tokens inside a K slice is valid as long as
-// both operands use the same one, which holds because A and B come from the same rows.
+// while a token row is contiguous in memory. The token rows go into LDS as they are (raw
+// buffer loads that write LDS directly: no registers, so four 32-token stages can be in
+// flight, and rows past the chunk read as zero through the descriptor's range), and the
+// operands come out transposed through ds_read_b64_tr_b16 (gfx950), two reads of four
+// tokens per operand. Any order of tokens inside a K slice is valid as long as both
+// operands use the same one, which holds because A and B come from the same rows.
 // fp32: v_mfma_f32_32x32x2_f32 straight from a [token][channel] tile (no transpose needed).
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
@@ -31,11 +27,10 @@ namespace nvfp4 {
 
 typedef __bf16 gram_v8bf __attribute__((ext_vector_type(8)));
 typedef float gram_v16f __attribute__((ext_vector_type(16)));
-typedef unsigned gram_v4u __attribute__((ext_vector_type(4)));
 
 constexpr int GT = 256;   // output tile edge (channels)
 constexpr int GC = 2 * GT;  // channels staged per step: the tile's row and column channels
-constexpr int GK = 64;    // tokens per step, bf16
+constexpr int GK = 64;    // token granularity of the chunks (bf16)
 constexpr int GKF = 32;   // tokens per step, fp32
 constexpr int GTHREADS = 512;  // 8 waves: 4 x 2 quarters of 64 x 128
 
@@ -114,111 +109,126 @@ __device__ __forceinline__ void gram_tile(int64_t t, int64_t nt, int64_t &ti, in
   tj = i + t;
 }
 
-__device__ __forceinline__ int gram_swz(int c) { return (c ^ (c >> 3)) & 7; }
+// bf16 staging: 32-token stages in four LDS buffers, three stages in flight. A stage holds
+// its token rows as they lie in memory (the tile's 256 row channels, then its 256 column
+// channels: 1 KiB) at a pitch of GROWB bytes; the 64-byte pad puts the four token rows a
+// transposing read touches at bank offsets 0, 16, 32, 48, so the two 16-lane groups of a
+// read pass (channels 16 apart) use disjoint banks.
+constexpr int GK2 = 32;                  // tokens per stage
+constexpr int GNST = 4;                  // stages in LDS
+constexpr int GROWB = 2 * GC + 64;       // bytes per staged token row
+constexpr int GSTAGE = GK2 * GROWB;      // bytes per stage
+
+// s_waitcnt with only the vector-memory count N (expcnt and lgkmcnt left at their maxima)
+#define GRAM_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
 
 __global__ void __launch_bounds__(GTHREADS)
     k_gram_bf16(const uint16_t *__restrict__ x, int64_t tokens, int64_t cols, int64_t nt,
                 int64_t tiles, int64_t nc, int64_t tc, float *__restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][GC * GK];
+  // four separate arrays, so that each stage's reads wait only for the loads into it
+  __shared__ __attribute__((aligned(16))) char st0[GSTAGE], st1[GSTAGE], st2[GSTAGE], st3[GSTAGE];
   int64_t chunk, tile, ti, tj;
   gram_work(blockIdx.x, tiles, nc, chunk, tile);
   gram_tile(tile, nt, ti, tj);
   const int64_t p0 = chunk * tc;
   const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // staging role: 8 channels (group q of 64: 32 row-tile, 32 column-tile) x 8 tokens
-  // (group g of the step's 8)
-  const int q = tid & 63, g = tid >> 6;
-  const int64_t chg = q < 32 ? ti * GT + q * 8 : tj * GT + (q - 32) * 8;
-  // cols % 16 == 0: a group of 8 channels is all in or all out. Groups past the last
-  // channel load channels 0..7 instead: they only feed rows and columns of the partial
-  // tile at or beyond cols, which the reduction drops.
-  const int64_t chl = chg < cols ? chg : 0;
-  // Raw buffer loads: token row pos + s + 8 g of the step is row 8 g of a buffer that
-  // starts at token pos + s (a scalar descriptor) and holds only the rows below p1, so
-  // rows past the chunk read as zero; the lane's byte offset (below 2^23) never changes.
-  const int lo_bytes = (int)(((int64_t)(g * 8) * cols + chl) * 2);
-  uint4 in[8];
-  auto load = [&](int64_t pos) {
+  // Loading: wave w stages token rows w, w + 8, w + 16, w + 24 of each stage, one row per
+  // instruction (64 lanes x 16 bytes, written by the load straight into LDS at lane * 16):
+  // lanes 0-31 the row tile's channels, 32-63 the column tile's. Channel groups past cols
+  // load channels 0..7 (they only reach partial-tile rows and columns the reduction drops);
+  // token rows past p1 have an empty descriptor range and read as zero.
+  const int64_t chg = lane < 32 ? ti * GT + lane * 8 : tj * GT + (lane - 32) * 8;
+  const int ch_bytes = (int)((chg < cols ? chg : 0) * 2);
+  const int nst = (int)((p1 - p0 + GK2 - 1) / GK2);
+  auto issue = [&](int st, char *lb) {
+    const int64_t pos = p0 + (int64_t)st * GK2;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      int64_t rows = p1 - pos - s;
-      rows = rows < 0 ? 0 : (rows > GK ? GK : rows);
+    for (int i = 0; i < 4; ++i) {
+      const int t = wave + 8 * i;
+      const int nrec = pos + t < p1 ? (int)(cols * 2) : 0;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(x + (pos + s) * cols), (short)0, (int)(rows * cols * 2),
-          0x00020000);
-      const gram_v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, lo_bytes, 0, 0);
-      in[s] = make_uint4(v.x, v.y, v.z, v.w);
-    }
-  };
-  // 8x8 transpose of 16-bit values: output channel i of token pair (2e, 2e + 1) takes the
-  // low (even i) or high (odd i) halves of dword i / 2 of both rows (v_perm_b32 byte select)
-  auto store = [&](uint16_t *buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      unsigned o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint4 a4 = in[2 * e], b4 = in[2 * e + 1];
-        const unsigned a = (i >> 1) == 0 ? a4.x : (i >> 1) == 1 ? a4.y : (i >> 1) == 2 ? a4.z : a4.w;
-        const unsigned b = (i >> 1) == 0 ? b4.x : (i >> 1) == 1 ? b4.y : (i >> 1) == 2 ? b4.z : b4.w;
-        o[e] = __builtin_amdgcn_perm(b, a, sel);  // bytes 0-3 from a, 4-7 from b
-      }
-      const int c = q * 8 + i;
-      *reinterpret_cast<uint4 *>(buf + c * GK + ((g ^ gram_swz(c)) << 3)) =
-          make_uint4(o[0], o[1], o[2], o[3]);
+          const_cast<uint16_t *>(x + (pos + t) * cols), (short)0, nrec, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(lb + t * GROWB), 16, ch_bytes, 0, 0, 0);
     }
   };
 
+  // Operands: v_mfma_f32_32x32x16_bf16 wants, in lane l, tokens 8 (l >> 5) .. +7 of channel
+  // l & 31 of the fragment. ds_read_b64_tr_b16 gives lane i of a 16-lane group element
+  // i % 4 of the 8 bytes read by lanes 4k + i / 4 (k = 0..3) of the group; so lane r of
+  // group G reads token row 8 (G >> 1) + r / 4 (+ 4 for the second half) at channel
+  // 16 (G & 1) + 4 (r % 4) of the fragment, and receives 4 consecutive tokens of channel
+  // 16 (G & 1) + r.
+  const int G = lane >> 4, r = lane & 15;
+  const int lane_off = (8 * (G >> 1) + (r >> 2)) * GROWB + (16 * (G & 1) + 4 * (r & 3)) * 2;
   const int wr = wave >> 1, wc = wave & 1;  // wave's 64 x 128 part of the tile
+  typedef short gram_v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) gram_v4s lds_v4s;
+  auto frag = [&](const char *buf, int kk, int cb) {
+    const char *p = buf + lane_off + kk * 16 * GROWB + cb * 2;
+    const gram_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)p);
+    const gram_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p + 4 * GROWB));
+    const gram_v4s v[2] = {lo, hi};
+    return __builtin_bit_cast(gram_v8bf, v);
+  };
+
   gram_v16f acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
-  int cur = 0;
-  if (p0 < p1) {
-    load(p0);
-    store(lds[0]);
-  }
-  __syncthreads();
-  for (int64_t pos = p0; pos < p1; pos += GK) {
-    const bool more = pos + GK < p1;
-    if (more) load(pos + GK);
-    const uint16_t *buf = lds[cur];
+  // a stage's products: all 24 operand reads first, then the 16 products
+  auto compute = [&](const char *buf) {
+    gram_v8bf A[GK2 / 16][2], B[GK2 / 16][4];
 #pragma unroll
-    for (int s4 = 0; s4 < GK / 16; ++s4) {
-      const int gg = 2 * s4 + (lane >> 5);
-      gram_v8bf A[2], B[4];
+    for (int kk = 0; kk < GK2 / 16; ++kk) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int c = wr * 64 + a * 32 + (lane & 31);
-        A[a] = __builtin_bit_cast(gram_v8bf, *reinterpret_cast<const uint4 *>(
-                                                 buf + c * GK + ((gg ^ gram_swz(c)) << 3)));
-      }
+      for (int a = 0; a < 2; ++a) A[kk][a] = frag(buf, kk, wr * 64 + a * 32);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int c = GT + wc * 128 + b * 32 + (lane & 31);
-        B[b] = __builtin_bit_cast(gram_v8bf, *reinterpret_cast<const uint4 *>(
-                                                 buf + c * GK + ((gg ^ gram_swz(c)) << 3)));
-      }
+      for (int b = 0; b < 4; ++b) B[kk][b] = frag(buf, kk, GT + wc * 128 + b * 32);
+    }
+#pragma unroll
+    for (int kk = 0; kk < GK2 / 16; ++kk)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a], B[b], acc[a][b], 0, 0, 0);
-    }
-    if (more) store(lds[cur ^ 1]);
-    lds_barrier();
-    cur ^= 1;
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kk][a], B[kk][b], acc[a][b], 0, 0, 0);
+  };
+  // one stage: wait for this wave's loads of it (those of the next two may stay in flight),
+  // then a bare barrier (a memory fence here would also wait for the loads still in flight;
+  // the empty asm statements keep the compiler from moving memory accesses across it): every
+  // wave's rows of the stage are in LDS, and every wave's reads of the previous stage have
+  // completed, since its products consumed them. Then refill the previous stage's buffer
+  // three stages ahead and compute.
+  auto stage = [&](int st, const char *cur, char *refill) {
+    const int later = nst - 1 - st;
+    if (later >= 2) GRAM_WAIT_VM(8);
+    else if (later == 1) GRAM_WAIT_VM(4);
+    else GRAM_WAIT_VM(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + GNST - 1 < nst) issue(st + GNST - 1, refill);
+    compute(cur);
+  };
+  if (nst > 0) issue(0, st0);
+  if (nst > 1) issue(1, st1);
+  if (nst > 2) issue(2, st2);
+  for (int st = 0; st < nst; st += GNST) {
+    stage(st, st0, st3);
+    if (st + 1 < nst) stage(st + 1, st1, st0);
+    if (st + 2 < nst) stage(st + 2, st2, st1);
+    if (st + 3 < nst) stage(st + 3, st3, st2);
   }
 
-  // D layout of a 32x32 MFMA: lane l, register r -> row (r & 3) + 4 (l >> 5) + 8 (r >> 2),
+  // D layout of a 32x32 MFMA: lane l, register e -> row (e & 3) + 4 (l >> 5) + 8 (e >> 2),
   // column l & 31
   float *P = partial + (chunk * tiles + tile) * (int64_t)(GT * GT);
 #pragma unroll
@@ -226,10 +236,10 @@ __global__ void __launch_bounds__(GTHREADS)
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wr * 64 + a * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
+      for (int e = 0; e < 16; ++e) {
+        const int row = wr * 64 + a * 32 + (e & 3) + 4 * (lane >> 5) + 8 * (e >> 2);
         const int col = wc * 128 + b * 32 + (lane & 31);
-        P[row * GT + col] = acc[a][b][r];
+        P[row * GT + col] = acc[a][b][e];
       }
 }
 
