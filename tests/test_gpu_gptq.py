@@ -90,6 +90,19 @@ def test_full_hessian_long_input_per_xcd_chunks(orc):
     assert np.array_equal(Hn, Hn.T)
 
 
+@pytest.mark.parametrize("tokens,cols", [(1, 16), (33, 48), (20001, 272), (3000, 528)])
+def test_full_hessian_bf16_partial_stages(orc, tokens, cols):
+    """bf16 inputs whose last 32-token stage is partial (rows past the end must read as
+    zero), with channel counts off the 256-channel tile grid; 20001 tokens also takes the
+    per-XCD chunk layout with an empty tail chunk."""
+    case(f"full hessian bf16 {tokens} tokens x {cols}")
+    x = synth.projection(tokens % 97 + cols, rows=16, cols=cols, tokens=tokens)[1]
+    assert x.dtype == torch.bfloat16
+    Hn = nvfp4.full_hessian(x.to(DEV)).cpu().numpy()
+    assert block_rel_frob(Hn, orc.full_hessian_blas(f32(x))) <= 1e-4
+    assert np.array_equal(Hn, Hn.T)
+
+
 def test_full_hessian_accumulate_and_empty(orc):
     case("full hessian: two batches accumulated, and zero tokens")
     xs = [synth.projection(s, rows=16, cols=256, tokens=600)[1] for s in (9, 10)]
