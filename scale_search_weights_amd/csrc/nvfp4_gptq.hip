@@ -214,19 +214,31 @@ __device__ __forceinline__ void d2_store_b(const DStage &st, double *LB) {
 __device__ __forceinline__ void d2_mma(DAcc2 &acc, const double *LA, const double *LB) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 2, wc = wave & 3;  // 32 x 32 per wave
-#pragma unroll 2
+  const double *pa = LA + (lane >> 4) * P2 + wr * 32 + (lane & 15);
+  const double *pb = LB + (lane >> 4) * P2 + wc * 32 + (lane & 15);
+  // the operands of step kk + 1 are read while step kk's four products run
+  double a[2][2], b[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    a[0][i] = pa[i * 16];
+    b[0][i] = pb[i * 16];
+  }
+#pragma unroll
   for (int kk = 0; kk < KC / 4; ++kk) {
-    const int kr = kk * 4 + (lane >> 4);
-    double a[2], b[2];
+    const int cur = kk & 1;
+    if (kk + 1 < KC / 4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = LA[kr * P2 + wr * 32 + i * 16 + (lane & 15)];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = LB[kr * P2 + wc * 32 + j * 16 + (lane & 15)];
+      for (int i = 0; i < 2; ++i) {
+        a[cur ^ 1][i] = pa[(kk + 1) * 4 * P2 + i * 16];
+        b[cur ^ 1][i] = pb[(kk + 1) * 4 * P2 + i * 16];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc.c[i][j], 0, 0, 0);
+        acc.c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[cur][i], b[cur][j], acc.c[i][j], 0, 0, 0);
   }
 }
 
