@@ -71,8 +71,8 @@ def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                               "(python -m scale_search_weights_amd.build)")
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "python -m scale_search_weights_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)
