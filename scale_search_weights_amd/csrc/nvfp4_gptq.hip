@@ -364,8 +364,12 @@ __device__ __forceinline__ double quad_bcast(double x, int src) {
 // readlane and each scaled column is broadcast through LDS); workgroup 0 stores it, and
 // workgroup b >= 1 then solves the 64 rows of panel block k + b, x L_kk^T = a, by forward
 // substitution: four lanes per row, 16 columns each, x_j broadcast in the quad by DPP.
+// L_kk goes to the same place in X, not back into A: with more workgroups than fit on the
+// device at once, a late workgroup still reads A_kk itself (the triangular inverse reads
+// the diagonal blocks from X).
 __global__ void __launch_bounds__(256)
-    k_chol_step(double *__restrict__ A, int64_t np, int64_t k, int32_t *__restrict__ status) {
+    k_chol_step(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t k,
+                int32_t *__restrict__ status) {
   __shared__ __attribute__((aligned(16))) double Lt[DB * DB];  // Lt[j * 64 + m] = L_kk[m][j]
   __shared__ double rinv[DB];
   const int t = threadIdx.x;
@@ -404,9 +408,10 @@ __global__ void __launch_bounds__(256)
     }
     if (blockIdx.x == 0) {
       if (bad && i == 0) atomicCAS(status, 0, (int32_t)(1 + k));
+      double *lk = X + k * DB * np + k * DB;
 #pragma unroll
       for (int j = 0; j < DB; j += 2)
-        *reinterpret_cast<double2 *>(blk + (int64_t)i * np + j) =
+        *reinterpret_cast<double2 *>(lk + (int64_t)i * np + j) =
             make_double2(j <= i ? d[j] : 0.0, j + 1 <= i ? d[j + 1] : 0.0);
     }
   }
@@ -452,13 +457,14 @@ __global__ void __launch_bounds__(256)
   dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
 }
 
-// inverses of the diagonal blocks: column c of L_bb^-1 by forward substitution
+// inverses of the diagonal blocks, in place in X (where the steps left L_bb): column c of
+// L_bb^-1 by forward substitution, after the whole block is in LDS
 __global__ void __launch_bounds__(64)
-    k_trtri_diag(const double *__restrict__ A, double *__restrict__ X, int64_t np) {
+    k_trtri_diag(double *__restrict__ X, int64_t np) {
   __shared__ double Lb[DB * DP];
   const int64_t b = blockIdx.x;
   const int c = threadIdx.x;
-  const double *src = A + b * DB * np + b * DB;
+  const double *src = X + b * DB * np + b * DB;
   for (int e = c; e < DB * DB; e += 64) Lb[(e >> 6) * DP + (e & 63)] = src[(e >> 6) * np + (e & 63)];
   __syncthreads();
   double y[DB];
@@ -598,17 +604,17 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   // K = 128 over the 128-aligned rest (128 x 128 tiles); an odd last step stands alone
   for (int64_t k = 0; k < nb; k += 2) {
     const int64_t T = nb - k - 1;
-    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(256), 0, st, A, np, k, stat);
+    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(256), 0, st, A, X, np, k, stat);
     if (T == 0) break;
     hipLaunchKernelGGL(k_chol_colupd, dim3((unsigned)T), dim3(256), 0, st, A, np, k);
-    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)T), dim3(256), 0, st, A, np, k + 1, stat);
+    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)T), dim3(256), 0, st, A, X, np, k + 1, stat);
     const int64_t c = (k + 2) * DB;
     if (c >= np) break;
     const int64_t t2 = (np - c + T2 - 1) / T2;
     hipLaunchKernelGGL(k_chol_update2, dim3((unsigned)(t2 * (t2 + 1) / 2)), dim3(W2T), 0, st, A,
                        np, c, k * DB);
   }
-  hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, A, X, np);
+  hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, X, np);
   for (int64_t s = DB; s < np; s *= 2) {
     const int64_t groups = (np + 2 * s - 1) / (2 * s);
     int64_t g = groups;

@@ -151,6 +151,31 @@ def test_gptq_factor_degenerate(orc):
 
 # ------------------------------------------------------------------ GPTQ rows
 
+def test_gptq_factor_more_workgroups_than_fit():
+    """n = 20480: a Cholesky step launches 320 workgroups, more than run at once, so some
+    start after workgroup 0 has factored the diagonal block; they must still read A_kk.
+    Checked through U (H + lambda I) U^T z = z (U^T U = (H + lambda I)^-1), for H = G G^T + 20 I
+    (condition number about 10^3)."""
+    n, damp = 20480, 0.01
+    case(f"gptq factor n={n}: property U M U^T = I on random vectors")
+    g = torch.Generator(device="cpu").manual_seed(123)
+    G = torch.randn(n, 64, generator=g).to(DEV)
+    H = G @ G.T
+    H.diagonal().add_(20.0)
+    del G
+    U, status = nvfp4.gptq_factor(H, damp)
+    assert status == 0
+    M = H.double()
+    lam = damp * M.diagonal().sum().item() / n
+    M.diagonal().add_(lam)
+    del H
+    Z = torch.randn(n, 4, generator=g, dtype=torch.float64).to(DEV)
+    R = U @ (M @ (U.T @ Z))
+    rel = ((R - Z).norm(dim=0) / Z.norm(dim=0)).max().item()
+    assert rel <= 1e-8, rel
+    assert torch.all(torch.diagonal(U) > 0)
+
+
 @pytest.mark.parametrize("which", ["bf16_lh", "fp32_ragged", "zero_blocks", "wide"])
 def test_gptq_rows_same_factor(orc, which):
     """The oracle's own U feeds both sides: only the column loop is compared."""
