@@ -50,7 +50,7 @@ constexpr int GXCD = 8;  // XCDs; workgroups are dispatched to them round-robin
 
 // Token chunks per tile: 16 or 8 when the tokens allow chunks of at least 2048 (then each
 // XCD takes whole chunks, so its L2 streams only those rows), else as many as fill whole
-// rounds of one workgroup per CU best.
+// rounds of one workgroup per CU best; one when the tiles alone number four per CU.
 static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   GramGeom g;
   g.nt = (cols + GT - 1) / GT;
@@ -58,6 +58,9 @@ static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   const int64_t steps = (tokens + GK - 1) / GK;
   int64_t max_nc = steps / 32;
   if (max_nc > 16) max_nc = 16;
+  // with at least four tiles per CU the tiles alone fill the device: no token split (which
+  // would multiply the partial-tile workspace without adding useful parallelism)
+  if (g.tiles >= 4 * (int64_t)cus) max_nc = 1;
   if (max_nc < 1) max_nc = 1;
   const bool by_xcd = max_nc >= 8;
   int64_t best = max_nc >= 16 ? 16 : (max_nc >= 8 ? 8 : 1);

@@ -103,6 +103,18 @@ def test_full_hessian_bf16_partial_stages(orc, tokens, cols):
     assert np.array_equal(Hn, Hn.T)
 
 
+def test_full_hessian_wide_unsplit_tokens(orc):
+    """16384 channels: 2080 tiles, enough workgroups without splitting the tokens (the
+    partial-tile workspace then holds one chunk); ragged token count."""
+    case("full hessian bf16 300 tokens x 16384 (no token chunks)")
+    x = synth.projection(23, rows=16, cols=16384, tokens=300)[1]
+    ws_one = nvfp4.lib().nvfp4_full_hessian_workspace_size(300, 16384)
+    assert ws_one <= 2080 * 256 * 256 * 4
+    Hn = nvfp4.full_hessian(x.to(DEV)).cpu().numpy()
+    assert block_rel_frob(Hn, orc.full_hessian_blas(f32(x))) <= 1e-4
+    assert np.array_equal(Hn, Hn.T)
+
+
 def test_full_hessian_accumulate_and_empty(orc):
     case("full hessian: two batches accumulated, and zero tokens")
     xs = [synth.projection(s, rows=16, cols=256, tokens=600)[1] for s in (9, 10)]
