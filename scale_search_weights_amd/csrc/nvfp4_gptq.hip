@@ -488,10 +488,10 @@ __global__ void __launch_bounds__(256)
     k_trtri_level(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
                   int phase) {
   __shared__ double LA[DB * DP], LB[DB * DP];
-  const int64_t a0 = (int64_t)blockIdx.x * 2 * s, c0 = a0 + s;
+  const int64_t a0 = (int64_t)blockIdx.y * 2 * s, c0 = a0 + s;
   const int64_t sc = np - c0 < s ? np - c0 : s;
   const int64_t nbs = s / DB;
-  const int64_t ib = blockIdx.y / nbs, jb = blockIdx.y % nbs;  // output block (C row, A col)
+  const int64_t ib = blockIdx.x / nbs, jb = blockIdx.x % nbs;  // output block (C row, A col)
   if (ib * DB >= sc) return;
   const int64_t r0 = c0 + ib * DB, q0 = a0 + jb * DB;  // global row / column of the block
   DAcc acc;
@@ -527,10 +527,10 @@ __global__ void __launch_bounds__(W2T)
     k_trtri_level2(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
                    int phase) {
   __shared__ __attribute__((aligned(16))) double L2[4 * KC * P2];  // two (A, B) chunk buffers
-  const int64_t a0 = (int64_t)blockIdx.x * 2 * s, c0 = a0 + s;
+  const int64_t a0 = (int64_t)blockIdx.y * 2 * s, c0 = a0 + s;
   const int64_t sc = np - c0 < s ? np - c0 : s;
   const int64_t nbs = s / T2;
-  const int64_t ib = blockIdx.y / nbs, jb = blockIdx.y % nbs;
+  const int64_t ib = blockIdx.x / nbs, jb = blockIdx.x % nbs;
   if (ib * T2 >= sc) return;
   const int mlim = (int)(sc - ib * T2 < T2 ? sc - ib * T2 : T2);
   const int64_t r0 = c0 + ib * T2, q0 = a0 + jb * T2;
@@ -622,12 +622,12 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
     if (g <= 0) continue;
     if (s >= T2) {
       const int64_t nbs = s / T2;
-      const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
+      const dim3 grid((unsigned)(nbs * nbs), (unsigned)g);  // tiles in x: up to 65536 of them
       hipLaunchKernelGGL(k_trtri_level2, grid, dim3(W2T), 0, st, A, X, np, s, 0);
       hipLaunchKernelGGL(k_trtri_level2, grid, dim3(W2T), 0, st, A, X, np, s, 1);
     } else {
       const int64_t nbs = s / DB;
-      const dim3 grid((unsigned)g, (unsigned)(nbs * nbs));
+      const dim3 grid((unsigned)(nbs * nbs), (unsigned)g);  // tiles in x: up to 65536 of them
       hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 0);
       hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 1);
     }
