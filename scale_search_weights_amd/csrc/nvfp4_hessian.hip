@@ -134,10 +134,13 @@ __global__ void __launch_bounds__(256)
   constexpr int ROWS = 256 / SEGS;   // token rows per load instruction
   constexpr int NLD = HT / ROWS;     // 16-byte loads per lane per step (= W)
   __shared__ __attribute__((aligned(16))) uint16_t tile[HT * PITCH];
-  const int64_t it = blockIdx.y;
+  // grid x = (token item, channel chunk), chunks fastest: one dimension, so long inputs with
+  // more items than a y dimension holds still launch
+  const int64_t nch = (cols + C - 1) / C;
+  const int64_t it = (int64_t)blockIdx.x / nch;
   int64_t p0, p1;
   if (!hess_range<GROUPED>(it, tokens, groups, offsets, n_ids, item_off, tc, p0, p1)) return;
-  const int64_t ch0 = (int64_t)blockIdx.x * C;
+  const int64_t ch0 = ((int64_t)blockIdx.x % nch) * C;
   const int r = threadIdx.x / SEGS, q = threadIdx.x % SEGS;
   const int64_t ch = ch0 + q * 8;
   const bool ch_ok = ch < cols;
@@ -214,10 +217,12 @@ __global__ void __launch_bounds__(256)
                const int32_t *__restrict__ item_off, int64_t tc, float *__restrict__ partial,
                int64_t nb) {
   __shared__ __attribute__((aligned(16))) float tile[HT * PITCH32];
-  const int64_t it = blockIdx.y;
+  // grid x = (token item, channel chunk), chunks fastest
+  const int64_t nch = (cols + HC - 1) / HC;
+  const int64_t it = (int64_t)blockIdx.x / nch;
   int64_t p0, p1;
   if (!hess_range<GROUPED>(it, tokens, groups, offsets, n_ids, item_off, tc, p0, p1)) return;
-  const int64_t ch0 = (int64_t)blockIdx.x * HC;
+  const int64_t ch0 = ((int64_t)blockIdx.x % nch) * HC;
   const int r = threadIdx.x >> 3, q = threadIdx.x & 7;
   const int64_t ch = ch0 + q * 8;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -300,9 +305,9 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
     hipLaunchKernelGGL(k_hess_items, dim3(1), dim3(256), 0, st, group_offsets, groups, n_ids, tc,
                        items, item_off);
   if (items > 0) {
-    const dim3 g((unsigned)((cols + HC - 1) / HC), (unsigned)items), b(256);
+    const dim3 g((unsigned)(items * ((cols + HC - 1) / HC))), b(256);
     const int64_t cw = HC * (grouped ? HW_GROUPED : HW_DENSE);
-    const dim3 gb((unsigned)((cols + cw - 1) / cw), (unsigned)items);
+    const dim3 gb((unsigned)(items * ((cols + cw - 1) / cw)));
     if (dtype == NVFP4_DTYPE_BF16) {
       const uint16_t *xb = static_cast<const uint16_t *>(x);
       if (grouped)
