@@ -146,10 +146,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Per-tensor table of the 127 scale bytes: entry c >= 1 holds s = E4M3(c) and the bracket
-// lo < 1/(s S) < hi; entry 0 holds s = 0 and the bracket of 1/(6 S) used by the max byte.
+// Per-tensor table of the 127 scale bytes: entry c >= 1 holds s = E4M3(c), the bracket
+// lo < 1/(s S) < hi, and z = the largest fp32 <= s S / 4 (for fp32 X >= 0, X <= z exactly
+// when X rounds to code 0 at this scale: at s S / 4 itself the tie goes to the even code 0);
+// entry 0 holds s = 0 and the bracket of 1/(6 S) used by the max byte.
 struct Cand {
-  float s, rlo, rhi, pad;
+  float s, rlo, rhi, z;
 };
 
 __device__ __forceinline__ void build_cands(Cand *cand, float S) {
@@ -157,7 +159,10 @@ __device__ __forceinline__ void build_cands(Cand *cand, float S) {
     Cand e;
     e.s = c ? e4m3_value(c) : 0.0f;
     recip_bracket(c ? (double)e.s * (double)S : 6.0 * (double)S, e.rlo, e.rhi);
-    e.pad = 0.0f;
+    const double t = 0.25 * (double)e.s * (double)S;  // exact: at most 28 significant bits
+    float z = (float)t;
+    if ((double)z > t) z = __uint_as_float(__float_as_uint(z) - 1u);
+    e.z = c ? z : 0.0f;
     cand[c] = e;
   }
 }

@@ -50,6 +50,9 @@ __device__ __forceinline__ void load16(const void *__restrict__ x, int64_t blk, 
 //    falls, and the fp32 fma chain never decreases, so obj(c) >= fp32(e*e) =: LB(c), a
 //    lower bound that is non-increasing in c. Bytes below c_b are visited downwards until
 //    LB exceeds the best objective; then no smaller byte can win.
+//  * Upwards from c_b, the values that round to 0 at byte c (x <= s S / 4) contribute x^2
+//    each; the fp32 chain over just those terms is a lower bound that never decreases in c,
+//    so the upward walk stops once it exceeds the best objective.
 // Each lane owns one block and walks its own window [max(c_b,1), c_hi], then downwards;
 // per-candidate constants (s, the two bracketing reciprocals of s S) come from an LDS table.
 
@@ -116,6 +119,20 @@ __device__ __forceinline__ void mse_pruned(const float X[16], float amax, const 
   best = INFINITY;
   best_c = 0;
   for (int c = c_lo; c <= c_hi; ++c) {
+    // upward bound: the values that round to 0 at byte c have error -x exactly, so the fp32
+    // chain over only those terms (same order, the others zero) is at most obj(c); the set
+    // only grows with c, so once this exceeds the best objective no larger byte can win.
+    // Checked at every second byte (measured fastest: one more candidate at most)
+    if (c > c_lo && ((c - c_lo) & 1) == 0) {
+      const float z = cand[c].z;
+      float lb = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float t = X[i] <= z ? X[i] : 0.0f;
+        lb = __builtin_fmaf(t, t, lb);
+      }
+      if (lb > best) break;
+    }
     const float o = mse_candidate(X, c, cand[c], S, fast_ok);
     if (o < best) {
       best = o;
