@@ -274,6 +274,23 @@ def test_mse_pruning_edges(orc, S):
     assert np.array_equal(obj.cpu().numpy().view(np.uint32), orf.view(np.uint32))
 
 
+def test_mse_optimum_far_above_max_byte(orc):
+    """Blocks whose MSE byte lies 4 or more above the max-scaling byte (normal and Laplace
+    values): the upward walk must reach them before its zero-term bound stops it."""
+    case("mse: optimum at least 4 bytes above the max-scaling byte")
+    rng = np.random.default_rng(77)
+    pool = np.concatenate([rng.standard_normal((6000, 16)), rng.laplace(size=(6000, 16))])
+    pool = pool.astype(np.float32)
+    S = orc.tensor_scale(pool)
+    up = orc.scales_mse(pool, S).astype(int).ravel() - orc.scales_max(pool, S).astype(int).ravel()
+    x = np.ascontiguousarray(pool[up >= 4])
+    assert len(x) >= 100, len(x)
+    sc, obj = nvfp4.scale_search_mse(torch.from_numpy(x).to(DEV), dev_S(S), return_obj=True)
+    sr, orf = orc.scales_mse(x, S, with_obj=True)
+    assert np.array_equal(sc.cpu().numpy(), sr)
+    assert np.array_equal(obj.cpu().numpy().view(np.uint32), orf.view(np.uint32))
+
+
 def test_mse_batched_and_zero_blocks(orc):
     case("mse batch 4 x 32 x 128 with zero blocks")
     w = synth.moe(3, experts=4, rows=32, cols=128, tokens=8, topk=1)[0]
