@@ -234,8 +234,10 @@ NVFP4_API int nvfp4_route_groups(const int32_t *expert_ids, int64_t tokens, int6
  * x: [tokens][cols] bf16 or fp32 (bf16 products are exact, accumulation is fp32);
  * cols % 16 == 0. H: [cols][cols] fp32 (out), exactly symmetric; accumulate != 0 adds to
  * the existing H (streaming over calibration batches). Partial sums per token chunk are
- * added in a fixed order, so results are bitwise reproducible.
- * workspace_bytes must be >= nvfp4_full_hessian_workspace_size().
+ * added in a fixed order, so results are bitwise reproducible on a given device model (the
+ * chunking follows its compute-unit count).
+ * workspace_bytes must be >= nvfp4_full_hessian_workspace_size(), queried with the device
+ * that runs the call current (the size depends on its compute-unit count).
  */
 NVFP4_API size_t nvfp4_full_hessian_workspace_size(int64_t tokens, int64_t cols);
 NVFP4_API int nvfp4_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, float *H,
