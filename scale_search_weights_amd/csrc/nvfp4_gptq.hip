@@ -276,6 +276,57 @@ __device__ __forceinline__ void d2_gemm(DAcc2 &acc, const double *A, int64_t lda
   }
 }
 
+// C[0:mlim, 0:nlim] -= A[:, 0:K] B[0:K, :] with K = NCH * KC (k < klim; operands as in
+// d2_gemm), the tile of C in global memory. The tile's old values are read into registers
+// a share per chunk, beside that chunk's products, rather than after the last of them: with
+// one workgroup per compute unit, reading and writing the 128 KiB tile at the end left the
+// matrix cores idle for a third of a short-K update.
+template <bool KN, int NCH>
+__device__ __forceinline__ void d2_gemm_sub(double *C, int64_t ldc, int mlim, int nlim,
+                                            const double *A, int64_t lda, const double *B,
+                                            int64_t ldb, int64_t klim, double *L) {
+  static_assert(16 % NCH == 0, "the tile's 16 values per thread split evenly over the chunks");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 2, wc = wave & 3;
+  auto kl = [&](int64_t kb) { return (int)(klim - kb < KC ? (klim - kb > 0 ? klim - kb : 0) : KC); };
+  DAcc2 acc;
+  d2_zero(acc);
+  DStage st;
+  d2_load_a(st, A, lda, mlim, kl(0));
+  d2_load_b<KN>(st, B, ldb, kl(0), nlim);
+  d2_store_a(st, L);
+  d2_store_b<KN>(st, L + KC * P2);
+  __syncthreads();
+  double cv[16];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    double *cur = L + (c & 1) * 2 * KC * P2, *nxt = L + ((c + 1) & 1) * 2 * KC * P2;
+    if (c + 1 < NCH) {
+      const int64_t kb = (int64_t)(c + 1) * KC;
+      d2_load_a(st, A + kb, lda, mlim, kl(kb));
+      d2_load_b<KN>(st, B + (KN ? kb * ldb : kb), ldb, kl(kb), nlim);
+    }
+#pragma unroll
+    for (int q = c * (16 / NCH); q < (c + 1) * (16 / NCH); ++q) {
+      const int i = q >> 3, j = (q >> 2) & 1, r = q & 3;
+      const int row = wr * 32 + i * 16 + (lane >> 4) + 4 * r, col = wc * 32 + j * 16 + (lane & 15);
+      cv[q] = row < mlim && col < nlim ? C[(int64_t)row * ldc + col] : 0.0;
+    }
+    d2_mma(acc, cur, cur + KC * P2);
+    if (c + 1 < NCH) {
+      d2_store_a(st, nxt);
+      d2_store_b<KN>(st, nxt + KC * P2);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 3, j = (q >> 2) & 1, r = q & 3;
+    const int row = wr * 32 + i * 16 + (lane >> 4) + 4 * r, col = wc * 32 + j * 16 + (lane & 15);
+    if (row < mlim && col < nlim) C[(int64_t)row * ldc + col] = cv[q] - acc.c[i][j][r];
+  }
+}
+
 // visit the tile elements a thread owns: f(row, col, value)
 template <class F>
 __device__ __forceinline__ void d2_each(const DAcc2 &acc, F f) {
@@ -582,13 +633,8 @@ __global__ void __launch_bounds__(W2T)
   }
   const int64_t I = c + ti * T2, J = c + e * T2;
   const int mlim = (int)(np - I < T2 ? np - I : T2), nlim = (int)(np - J < T2 ? np - J : T2);
-  DAcc2 acc;
-  d2_zero(acc);
-  d2_gemm<false>(acc, A + I * np + k0, np, mlim, A + J * np + k0, np, nlim, 2 * DB, 2 * DB, L2);
-  double *C = A + I * np + J;
-  d2_each(acc, [&](int r, int cc, double v) {
-    if (r < mlim && cc < nlim) C[r * np + cc] -= v;
-  });
+  d2_gemm_sub<false, 2 * DB / KC>(A + I * np + J, np, mlim, nlim, A + I * np + k0, np,
+                                  A + J * np + k0, np, 2 * DB, L2);
 }
 
 int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_t *status,
@@ -685,24 +731,71 @@ __global__ void __launch_bounds__(256)
   __shared__ double RU[DB];                                    // 1 / U_jj
   const int t = threadIdx.x;
   const int64_t c0 = b * DB;
-  for (int e = t; e < DB * DB; e += 256) {
-    const int j = e >> 6, k = e & 63;
-    const int64_t gj = c0 + j, gk = c0 + k;
-    double u = 0.0;
-    if (gj < n && gk < n) u = U[gj * n + gk];
-    else if (gj == gk) u = 1.0;  // padding columns
-    LU[e] = u;
-  }
-  if (t < DB) RU[t] = 1.0 / (c0 + t < n ? U[(c0 + t) * n + c0 + t] : 1.0);
-  __syncthreads();
+  // every global read is issued before the first wait: one workgroup per compute unit has
+  // no other work to hide their latency behind
   const int p = t & 15;
   const int64_t r = (int64_t)blockIdx.x * 16 + (t >> 4);
   const int64_t cb = c0 + 4 * p;  // first of this lane's 4 columns
   const bool live = r < rows && cb < n;
   const double2 v01 = *reinterpret_cast<const double2 *>(V + r * np + cb);
   const double2 v23 = *reinterpret_cast<const double2 *>(V + r * np + cb + 2);
-  double v[4] = {v01.x, v01.y, v23.x, v23.y};
   const int byte = live ? scales[r * (n / 16) + cb / 16] : 0;
+  // the rest of this 256-column outer block (at most 192 columns, 12 tiles of 16), updated
+  // after the column loop: wave w takes tiles w, w + 4, w + 8, whose rows of U and values of
+  // V are read here (n is a multiple of 16; when any tile follows, all 64 rows of U's block
+  // are below n)
+  int64_t c_end = (b / 4 + 1) * OB;
+  if (c_end > n) c_end = n;
+  const int ntiles = c_end > c0 + DB ? (int)((c_end - c0 - DB) / 16) : 0;
+  const int lane = t & 63, w = t >> 6, lr = lane >> 4, lc = lane & 15;
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  double ub[3][16], vv[3][4];
+#pragma unroll
+  for (int qi = 0; qi < 3; ++qi) {
+    const int q = w + 4 * qi;
+    const int64_t cq = c0 + DB + 16 * q + lc;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) ub[qi][s] = q < ntiles ? U[(c0 + 4 * s + lr) * n + cq] : 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[qi][i] = q < ntiles ? V[(r0 + lr + 4 * i) * np + cq] : 0.0;
+  }
+  // U's block: thread t stages rows t / 16 + 16 s, columns 4 (t % 16) .. + 3 (past n: the
+  // identity, for the padding columns)
+  {
+    const int k4 = 4 * (t & 15);
+    double2 u[4][2];
+    if (c0 + DB <= n) {  // the whole block lies inside U
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const double *src = U + (c0 + (t >> 4) + 16 * s) * n + c0 + k4;
+        u[s][0] = *reinterpret_cast<const double2 *>(src);
+        u[s][1] = *reinterpret_cast<const double2 *>(src + 2);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int j = (t >> 4) + 16 * s;
+        double e4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t gj = c0 + j, gk = c0 + k4 + i;
+          e4[i] = gj < n && gk < n ? U[gj * n + gk] : (gj == gk ? 1.0 : 0.0);
+        }
+        u[s][0] = make_double2(e4[0], e4[1]);
+        u[s][1] = make_double2(e4[2], e4[3]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      double *dst = LU + ((t >> 4) + 16 * s) * DB + k4;
+      *reinterpret_cast<double2 *>(dst) = u[s][0];
+      *reinterpret_cast<double2 *>(dst + 2) = u[s][1];
+    }
+  }
+  __syncthreads();
+  if (t < DB) RU[t] = 1.0 / LU[t * DB + t];
+  __syncthreads();
+  double v[4] = {v01.x, v01.y, v23.x, v23.y};
   // s * S (exact in double) and the midpoints between grid values at that scale; a zero
   // byte gives infinite midpoints, so every value rounds to code 0
   double sS = 0.0;
@@ -750,29 +843,12 @@ __global__ void __launch_bounds__(256)
   *reinterpret_cast<double2 *>(er) = make_double2(ev[0], ev[1]);
   *reinterpret_cast<double2 *>(er + 2) = make_double2(ev[2], ev[3]);
 
-  // the rest of this 256-column outer block (at most 192 columns, 12 tiles of 16): for this
-  // workgroup's 16 rows, V[:, tile] -= E[:, block] U[block, tile] as 16 fp64 MFMA steps per
-  // tile (K = 4 each); wave w takes tiles w, w + 4, w + 8. A fragments (lane l: row l & 15 at
-  // k = l >> 4) come from LDS ([k][row]); U and V are loaded for all three tiles up front.
+  // the rest of the outer block: V[:, tile] -= E[:, block] U[block, tile] for this
+  // workgroup's 16 rows, as 16 fp64 MFMA steps per tile (K = 4 each); A fragments (lane l:
+  // row l & 15 at k = l >> 4) come from LDS ([k][row])
   __shared__ double LE[DB * 16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) LE[(4 * p + i) * 16 + (t >> 4)] = ev[i];
-  int64_t c_end = (b / 4 + 1) * OB;
-  if (c_end > n) c_end = n;
-  // n is a multiple of 16; when any tile follows, all 64 rows of U's block are below n
-  const int ntiles = c_end > c0 + DB ? (int)((c_end - c0 - DB) / 16) : 0;
-  const int lane = t & 63, w = t >> 6, lr = lane >> 4, lc = lane & 15;
-  const int64_t r0 = (int64_t)blockIdx.x * 16;
-  double ub[3][16], vv[3][4];
-#pragma unroll
-  for (int qi = 0; qi < 3; ++qi) {
-    const int q = w + 4 * qi;
-    const int64_t cq = c0 + DB + 16 * q + lc;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) ub[qi][s] = q < ntiles ? U[(c0 + 4 * s + lr) * n + cq] : 0.0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vv[qi][r] = q < ntiles ? V[(r0 + lr + 4 * r) * np + cq] : 0.0;
-  }
   __syncthreads();
 #pragma unroll
   for (int qi = 0; qi < 3; ++qi) {
@@ -784,24 +860,22 @@ __global__ void __launch_bounds__(256)
       acc = __builtin_amdgcn_mfma_f64_16x16x4f64(LE[(4 * s + lr) * 16 + lc], ub[qi][s], acc, 0, 0, 0);
     const int64_t cq = c0 + DB + 16 * q + lc;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) V[(r0 + lr + 4 * r) * np + cq] = vv[qi][r] - acc[r];
+    for (int i = 0; i < 4; ++i) V[(r0 + lr + 4 * i) * np + cq] = vv[qi][i] - acc[i];
   }
 }
 
-// V[:, 128-column tiles from c_start] -= E[:, 0 .. kc) U[k0 .. k0 + kc, those columns], with
-// rows of U at or beyond n counting as zero (the outer update: kc = 256)
+// the outer update: V[:, 128-column tiles from c_start] -= E[:, 0 .. 256) U[k0 .. k0 + 256,
+// those columns], with rows of U at or beyond n counting as zero
 __global__ void __launch_bounds__(W2T)
     k_gptq_update2(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
-                   const double *__restrict__ E, int64_t k0, int kc, int64_t c_start) {
+                   const double *__restrict__ E, int64_t k0, int64_t c_start) {
   __shared__ __attribute__((aligned(16))) double L2[4 * KC * P2];  // two (A, B) chunk buffers
   const int64_t r0 = (int64_t)blockIdx.x * T2, c0 = c_start + (int64_t)blockIdx.y * T2;
   const int nlim = (int)(n - c0 < T2 ? n - c0 : T2);
-  const int64_t klim = n - k0 < kc ? n - k0 : kc;
-  DAcc2 acc;
-  d2_zero(acc);
-  d2_gemm<true>(acc, E + r0 * OB, OB, T2, U + k0 * n + c0, n, nlim, kc, klim, L2);
-  double *C = V + r0 * np + c0;
-  d2_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
+  const int64_t klim = n - k0 < OB ? n - k0 : OB;
+  // padding columns of V (n and beyond) are left alone: only their own errors reach them
+  d2_gemm_sub<true, OB / KC>(V + r0 * np + c0, np, T2, nlim, E + r0 * OB, OB, U + k0 * n + c0, n,
+                             klim, L2);
 }
 
 int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const float *S,
@@ -825,7 +899,7 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
     const int64_t ob_end = (b / 4 + 1) * 4 < nbc ? (b / 4 + 1) * 4 : nbc;  // in blocks
     if (b + 1 == ob_end && ob_end < nbc)
       hipLaunchKernelGGL(k_gptq_update2, dim3((unsigned)(rp / T2), (unsigned)((np - ob_end * DB) / T2)),
-                         dim3(W2T), 0, st, V, np, n, U, E, (b / 4) * OB, OB, ob_end * DB);
+                         dim3(W2T), 0, st, V, np, n, U, E, (b / 4) * OB, ob_end * DB);
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
