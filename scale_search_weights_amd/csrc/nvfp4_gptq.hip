@@ -350,10 +350,19 @@ __global__ void __launch_bounds__(256)
   double tr = 0.0;
   for (int64_t base = 0; base < n; base += 4096) {
     const int64_t m = n - base < 4096 ? n - base : 4096;
-    for (int64_t i = threadIdx.x; i < m; i += 256) dg[i] = (double)H[(base + i) * n + base + i];
+    float h[16];  // this thread's diagonal entries of the chunk, all reads in flight at once
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int64_t i = s * 256 + threadIdx.x;
+      h[s] = i < m ? H[(base + i) * n + base + i] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) dg[s * 256 + threadIdx.x] = (double)h[s];
     __syncthreads();
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
+#pragma unroll 16
       for (int64_t i = 0; i < m; ++i) tr += dg[i];  // index order
+    }
     __syncthreads();
   }
   if (threadIdx.x == 0) {
@@ -363,26 +372,53 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// A (np x np) = J (H + lambda I) J, lower triangle from H's lower triangle, identity padding
+// A (np x np) = J (H + lambda I) J, lower triangle from H's lower triangle, identity padding,
+// zero above the diagonal; X zero in its blocks above the diagonal (the inverse reads them as
+// zero; the factorisation and the inverse write every other block of X before reading it).
+// One 64 x 64 tile per workgroup: A[i][j] = H[n-1-j][n-1-i] reverses and transposes, so the
+// tile of H is read along its rows into LDS and written along A's rows from there.
 __global__ void __launch_bounds__(256)
     k_gptq_load_h(const float *__restrict__ H, int64_t n, int64_t np,
                   const double *__restrict__ hdr, double *__restrict__ A, double *__restrict__ X) {
+  __shared__ float T[DB][DB + 1];  // T[k][m] = H[n-1-(j0+k)][n-1-(i0+m)]
+  const int64_t nbt = np / DB;
+  const int64_t ti = blockIdx.x / nbt, tj = blockIdx.x % nbt;
+  const int64_t i0 = ti * DB, j0 = tj * DB;
+  const int t = threadIdx.x;
+  if (tj > ti) {  // above the diagonal: zero in A and in X
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int e = s * 256 + t, r = e >> 5, c = (e & 31) * 2;
+      *reinterpret_cast<double2 *>(A + (i0 + r) * np + j0 + c) = make_double2(0.0, 0.0);
+      *reinterpret_cast<double2 *>(X + (i0 + r) * np + j0 + c) = make_double2(0.0, 0.0);
+    }
+    return;
+  }
   const double lam = hdr[0];
   const bool ident = hdr[1] != 0.0;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < np * np;
-       e += (int64_t)gridDim.x * 256) {
-    const int64_t i = e / np, j = e % np;
+  {
+    // thread t reads H row n-1-(j0+k) at columns n-1-(i0+63) + (t & 63) upward (m = 63 - (t & 63))
+    float h[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int k = s * 4 + (t >> 6), m = DB - 1 - (t & 63);
+      const int64_t b = n - 1 - (j0 + k), a = n - 1 - (i0 + m);
+      h[s] = (j0 + k < n && i0 + m < n) ? H[b * n + a] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) T[s * 4 + (t >> 6)][DB - 1 - (t & 63)] = h[s];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int m = s * 4 + (t >> 6), k = t & 63;  // A row i0 + m, column j0 + k
+    const int64_t i = i0 + m, j = j0 + k;
     double v = 0.0;
     if (j <= i) {
-      if (i >= n) {
-        v = i == j ? 1.0 : 0.0;
-      } else {
-        const int64_t a = n - 1 - i, b = n - 1 - j;  // a <= b: H[b][a] is in H's lower part
-        v = ident ? (i == j ? 1.0 : 0.0) : (double)H[b * n + a] + (i == j ? lam : 0.0);
-      }
+      if (i >= n) v = i == j ? 1.0 : 0.0;
+      else v = ident ? (i == j ? 1.0 : 0.0) : (double)T[k][m] + (i == j ? lam : 0.0);
     }
-    A[e] = v;
-    X[e] = 0.0;  // the inverse's upper triangle must read as zero
+    A[i * np + j] = v;
   }
 }
 
@@ -516,7 +552,13 @@ __global__ void __launch_bounds__(64)
   const int64_t b = blockIdx.x;
   const int c = threadIdx.x;
   const double *src = X + b * DB * np + b * DB;
-  for (int e = c; e < DB * DB; e += 64) Lb[(e >> 6) * DP + (e & 63)] = src[(e >> 6) * np + (e & 63)];
+  {
+    double l[DB];  // column c of the block: all 64 reads in flight before the first wait
+#pragma unroll
+    for (int i = 0; i < DB; ++i) l[i] = src[i * np + c];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) Lb[i * DP + c] = l[i];
+  }
   __syncthreads();
   double y[DB];
 #pragma unroll
@@ -645,7 +687,7 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   double *A = reinterpret_cast<double *>(static_cast<char *>(workspace) + 256);
   double *X = A + np * np;
   hipLaunchKernelGGL(k_gptq_lambda, dim3(1), dim3(256), 0, st, H, n, damp, hdr, stat);
-  hipLaunchKernelGGL(k_gptq_load_h, dim3(grid_for(np * np)), dim3(256), 0, st, H, n, np, hdr, A, X);
+  hipLaunchKernelGGL(k_gptq_load_h, dim3((unsigned)(nb * nb)), dim3(256), 0, st, H, n, np, hdr, A, X);
   // steps in pairs: step k, column block k + 1, step k + 1, then one trailing update with
   // K = 128 over the 128-aligned rest (128 x 128 tiles); an odd last step stands alone
   for (int64_t k = 0; k < nb; k += 2) {

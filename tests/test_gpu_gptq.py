@@ -161,6 +161,22 @@ def test_gptq_factor_degenerate(orc):
     assert status.item() != 0
 
 
+@pytest.mark.parametrize("n", [208, 1040])
+def test_gptq_factor_workspace_contents_unread(orc, n):
+    """The factor writes every part of its workspace that it reads (the inverse's blocks
+    below the diagonal are written before use, those above are zeroed): a workspace filled
+    with NaN gives the same U, bit for bit, as a zeroed one."""
+    case(f"gptq factor n={n}: NaN-filled workspace")
+    H = torch.from_numpy(_h_problem(orc, 7, n)).to(DEV)
+    need = int(nvfp4.lib().nvfp4_gptq_factor_workspace_size(n))
+    ws0 = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    wsn = torch.full((need // 8,), float("nan"), dtype=torch.float64, device=DEV).view(torch.uint8)
+    U0, s0 = nvfp4.gptq_factor(H, 0.01, workspace=ws0)
+    Un, sn = nvfp4.gptq_factor(H, 0.01, workspace=wsn)
+    assert s0.item() == 0 and sn.item() == 0
+    assert torch.equal(U0, Un)
+
+
 # ------------------------------------------------------------------ GPTQ rows
 
 def test_gptq_factor_more_workgroups_than_fit():
