@@ -131,6 +131,54 @@ __device__ __forceinline__ void dacc_each(const DAcc &acc, F f) {
         f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 32 + j * 16 + (lane & 15), acc.c[i][j][r]);
 }
 
+// C[0:64, 0:nlim] -= A B over K = 64 * NCH (k < klim): A (m, k) at A[m * lda + k]; B (k, n)
+// at B[k * ldb + n] when KN, else at B[n * ldb + k]; zero outside the limits. The 64 x 64
+// form of the trailing updates, for launches with fewer 128 x 128 tiles than compute units:
+// four times the workgroups, each a quarter as long, two per compute unit. The products run
+// over k in the same order as in the wide form, so both give the same bits. C's old values
+// are read before the products and used after them.
+template <bool KN, int NCH>
+__device__ __forceinline__ void d64_sub(double *C, int64_t ldc, int nlim, const double *A,
+                                        int64_t lda, const double *B, int64_t ldb, int64_t klim,
+                                        double *LA, double *LB) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  double cv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 3, j = (q >> 2) & 1, r = q & 3;
+    const int row = wr * 32 + i * 16 + (lane >> 4) + 4 * r, col = wc * 32 + j * 16 + (lane & 15);
+    cv[q] = col < nlim ? C[(int64_t)row * ldc + col] : 0.0;
+  }
+  DAcc acc;
+  dacc_zero(acc);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int64_t kb = (int64_t)c * DB;
+    const int kl = (int)(klim - kb < DB ? (klim - kb > 0 ? klim - kb : 0) : DB);
+    if (c) __syncthreads();
+    dload_mk(LA, A + kb, lda, DB, kl);
+    if (KN) dload_kn(LB, B + kb * ldb, ldb, kl, nlim);
+    else dload_mk(LB, B + kb, ldb, nlim, kl);
+    __syncthreads();
+    dmma(acc, LA, LB);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 3, j = (q >> 2) & 1, r = q & 3;
+    const int row = wr * 32 + i * 16 + (lane >> 4) + 4 * r, col = wc * 32 + j * 16 + (lane & 15);
+    if (col < nlim) C[(int64_t)row * ldc + col] = cv[q] - acc.c[i][j][r];
+  }
+}
+
+static int gptq_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
 // Wide tiles: a workgroup of 16 waves owns a 128 x 128 output tile (each wave 32 x 32, as
 // 2 x 2 MFMA tiles), K in chunks of 32 staged through two 66 KiB LDS buffers (the next
 // chunk's global loads are in flight while the current one is multiplied, one barrier per
@@ -679,6 +727,20 @@ __global__ void __launch_bounds__(W2T)
                                   A + J * np + k0, np, 2 * DB, L2);
 }
 
+// the same update with 64 x 64 tiles (the lower-triangular ones from c on)
+__global__ void __launch_bounds__(256)
+    k_chol_update64(double *__restrict__ A, int64_t np, int64_t c, int64_t k0) {
+  __shared__ double LA[DB * DP], LB[DB * DP];
+  int64_t e = blockIdx.x, ti = 0;
+  while (e > ti) {
+    e -= ti + 1;
+    ++ti;
+  }
+  const int64_t I = c + ti * DB, J = c + e * DB;
+  d64_sub<false, 2>(A + I * np + J, np, DB, A + I * np + k0, np, A + J * np + k0, np, 2 * DB,
+                    LA, LB);
+}
+
 int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_t *status,
                        void *workspace, hipStream_t st) {
   const int64_t np = pad64(n), nb = np / DB;
@@ -686,6 +748,7 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   int32_t *stat = status ? status : reinterpret_cast<int32_t *>(hdr + 2);
   double *A = reinterpret_cast<double *>(static_cast<char *>(workspace) + 256);
   double *X = A + np * np;
+  const int64_t cus = gptq_cus();
   hipLaunchKernelGGL(k_gptq_lambda, dim3(1), dim3(256), 0, st, H, n, damp, hdr, stat);
   hipLaunchKernelGGL(k_gptq_load_h, dim3((unsigned)(nb * nb)), dim3(256), 0, st, H, n, np, hdr, A, X);
   // steps in pairs: step k, column block k + 1, step k + 1, then one trailing update with
@@ -699,8 +762,14 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
     const int64_t c = (k + 2) * DB;
     if (c >= np) break;
     const int64_t t2 = (np - c + T2 - 1) / T2;
-    hipLaunchKernelGGL(k_chol_update2, dim3((unsigned)(t2 * (t2 + 1) / 2)), dim3(W2T), 0, st, A,
-                       np, c, k * DB);
+    if (t2 * (t2 + 1) / 2 >= cus) {
+      hipLaunchKernelGGL(k_chol_update2, dim3((unsigned)(t2 * (t2 + 1) / 2)), dim3(W2T), 0, st, A,
+                         np, c, k * DB);
+    } else {  // too few wide tiles to fill the device
+      const int64_t t1 = (np - c) / DB;
+      hipLaunchKernelGGL(k_chol_update64, dim3((unsigned)(t1 * (t1 + 1) / 2)), dim3(256), 0, st, A,
+                         np, c, k * DB);
+    }
   }
   hipLaunchKernelGGL(k_trtri_diag, dim3((unsigned)nb), dim3(64), 0, st, X, np);
   for (int64_t s = DB; s < np; s *= 2) {
@@ -920,12 +989,26 @@ __global__ void __launch_bounds__(W2T)
                              klim, L2);
 }
 
+// the same update with 64 x 64 tiles of V (columns at or beyond n are skipped)
+__global__ void __launch_bounds__(256)
+    k_gptq_update64(double *__restrict__ V, int64_t np, int64_t n, const double *__restrict__ U,
+                    const double *__restrict__ E, int64_t k0, int64_t c_start) {
+  __shared__ double LA[DB * DP], LB[DB * DP];
+  const int64_t r0 = (int64_t)blockIdx.x * DB, c0 = c_start + (int64_t)blockIdx.y * DB;
+  if (c0 >= n) return;
+  const int nlim = (int)(n - c0 < DB ? n - c0 : DB);
+  const int64_t klim = n - k0 < OB ? n - k0 : OB;
+  d64_sub<true, OB / DB>(V + r0 * np + c0, np, nlim, E + r0 * OB, OB, U + k0 * n + c0, n, klim,
+                         LA, LB);
+}
+
 int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const float *S,
                      const uint8_t *scales, const double *U, uint8_t *codes, void *workspace,
                      hipStream_t st) {
   const int64_t rp = pad128(rows), np = pad128(n), nbc = pad64(n) / DB;
   double *V = static_cast<double *>(workspace);
   double *E = V + rp * np;
+  const int64_t cus = gptq_cus();
   if (dtype == NVFP4_DTYPE_BF16)
     hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_BF16>, dim3(grid_for(rp * np)), dim3(256), 0, st, w,
                        rows, n, rp, np, V);
@@ -939,9 +1022,15 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
     hipLaunchKernelGGL(k_gptq_block, dim3((unsigned)(rp / 16)), dim3(256), 0, st, V, np, rows, n, S,
                        scales, U, b, E, codes);
     const int64_t ob_end = (b / 4 + 1) * 4 < nbc ? (b / 4 + 1) * 4 : nbc;  // in blocks
-    if (b + 1 == ob_end && ob_end < nbc)
-      hipLaunchKernelGGL(k_gptq_update2, dim3((unsigned)(rp / T2), (unsigned)((np - ob_end * DB) / T2)),
-                         dim3(W2T), 0, st, V, np, n, U, E, (b / 4) * OB, ob_end * DB);
+    if (b + 1 == ob_end && ob_end < nbc) {
+      const int64_t c_start = ob_end * DB;
+      if ((rp / T2) * ((np - c_start) / T2) >= cus)
+        hipLaunchKernelGGL(k_gptq_update2, dim3((unsigned)(rp / T2), (unsigned)((np - c_start) / T2)),
+                           dim3(W2T), 0, st, V, np, n, U, E, (b / 4) * OB, c_start);
+      else  // too few wide tiles to fill the device
+        hipLaunchKernelGGL(k_gptq_update64, dim3((unsigned)(rp / DB), (unsigned)((np - c_start) / DB)),
+                           dim3(256), 0, st, V, np, n, U, E, (b / 4) * OB, c_start);
+    }
   }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
