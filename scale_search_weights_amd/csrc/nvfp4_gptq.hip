@@ -16,7 +16,9 @@
 //    workgroup factors the diagonal block in one wave's registers and solves one panel
 //    block; steps go in pairs, and after each pair one fp64 MFMA product with K = 128
 //    updates the trailing matrix), then a bottom-up recursive inverse
-//    [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] (two fp64 MFMA products per level).
+//    [[A, 0], [B, C]]^-1 = [[A^-1, 0], [-C^-1 B A^-1, C^-1]] (two fp64 MFMA products per level,
+//    in 64 x 64 tiles whose K differs by up to a factor nbs: launched longest first, so the
+//    device balances them, where one 128 x 128 tile per compute unit waited on the longest).
 //  * rows: the column loop in blocks of 64 columns. In a block, sixteen lanes share a row,
 //    each holding 4 of its values in registers; for every column the owning lane rounds,
 //    forms e and broadcasts it to its row of 16 lanes (DPP row_newbcast), and all of them
@@ -182,9 +184,8 @@ static int gptq_cus() {
 // Wide tiles: a workgroup of 16 waves owns a 128 x 128 output tile (each wave 32 x 32, as
 // 2 x 2 MFMA tiles), K in chunks of 32 staged through two 66 KiB LDS buffers (the next
 // chunk's global loads are in flight while the current one is multiplied, one barrier per
-// chunk). Four times the
-// work of a 64 x 64 tile per byte loaded; four waves per SIMD hide the loads and barriers
-// (eight waves of 32 x 64 were 5% slower, four of 64 x 64 another 15%).
+// chunk). Four times the work of a 64 x 64 tile per byte loaded; four waves per SIMD hide the
+// loads and barriers (eight waves of 32 x 64 were 5% slower, four of 64 x 64 another 15%).
 constexpr int T2 = 128;     // wide tile edge
 constexpr int KC = 32;      // K chunk
 constexpr int P2 = T2 + 1;  // LDS pitch (doubles)
@@ -290,42 +291,8 @@ __device__ __forceinline__ void d2_mma(DAcc2 &acc, const double *LA, const doubl
   }
 }
 
-// acc += A[0:128, 0:K] B[0:K, 0:128] (A as in d2_load_a; B as in d2_load_b), k < klim and
-// the row / column limits zero-filled. L: two (A, B) chunk buffers, 4 * KC * P2 doubles;
-// the next chunk is loaded into registers during the current one's products.
-template <bool KN>
-__device__ __forceinline__ void d2_gemm(DAcc2 &acc, const double *A, int64_t lda, int mlim,
-                                        const double *B, int64_t ldb, int nlim, int64_t K,
-                                        int64_t klim, double *L) {
-  const int nch = (int)((K + KC - 1) / KC);
-  if (nch <= 0) return;
-  DStage st;
-  auto bofs = [&](int64_t kb) { return KN ? kb * ldb : kb; };
-  auto kl = [&](int64_t kb) { return (int)(klim - kb < KC ? (klim - kb > 0 ? klim - kb : 0) : KC); };
-  d2_load_a(st, A, lda, mlim, kl(0));
-  d2_load_b<KN>(st, B, ldb, kl(0), nlim);
-  d2_store_a(st, L);
-  d2_store_b<KN>(st, L + KC * P2);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    double *cur = L + (c & 1) * 2 * KC * P2, *nxt = L + ((c + 1) & 1) * 2 * KC * P2;
-    const bool more = c + 1 < nch;
-    if (more) {
-      const int64_t kb = (int64_t)(c + 1) * KC;
-      d2_load_a(st, A + kb, lda, mlim, kl(kb));
-      d2_load_b<KN>(st, B + bofs(kb), ldb, kl(kb), nlim);
-    }
-    d2_mma(acc, cur, cur + KC * P2);
-    if (more) {
-      d2_store_a(st, nxt);
-      d2_store_b<KN>(st, nxt + KC * P2);
-    }
-    __syncthreads();
-  }
-}
-
-// C[0:mlim, 0:nlim] -= A[:, 0:K] B[0:K, :] with K = NCH * KC (k < klim; operands as in
-// d2_gemm), the tile of C in global memory. The tile's old values are read into registers
+// C[0:mlim, 0:nlim] -= A[:, 0:K] B[0:K, :] with K = NCH * KC (k < klim; A as in d2_load_a,
+// B as in d2_load_b), the tile of C in global memory. The tile's old values are read into registers
 // a share per chunk, beside that chunk's products, rather than after the last of them: with
 // one workgroup per compute unit, reading and writing the 128 KiB tile at the end left the
 // matrix cores idle for a third of a short-K update.
@@ -373,20 +340,6 @@ __device__ __forceinline__ void d2_gemm_sub(double *C, int64_t ldc, int mlim, in
     const int row = wr * 32 + i * 16 + (lane >> 4) + 4 * r, col = wc * 32 + j * 16 + (lane & 15);
     if (row < mlim && col < nlim) C[(int64_t)row * ldc + col] = cv[q] - acc.c[i][j][r];
   }
-}
-
-// visit the tile elements a thread owns: f(row, col, value)
-template <class F>
-__device__ __forceinline__ void d2_each(const DAcc2 &acc, F f) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 2, wc = wave & 3;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        f(wr * 32 + i * 16 + (lane >> 4) + 4 * r, wc * 32 + j * 16 + (lane & 15), acc.c[i][j][r]);
 }
 
 // ------------------------------------------------------------------ factor
@@ -627,12 +580,15 @@ __global__ void __launch_bounds__(64)
 // -X[C][C] T. X's own upper triangle stays zero.
 __global__ void __launch_bounds__(256)
     k_trtri_level(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
-                  int phase) {
+                  int64_t g, int phase) {
   __shared__ double LA[DB * DP], LB[DB * DP];
-  const int64_t a0 = (int64_t)blockIdx.y * 2 * s, c0 = a0 + s;
+  // workgroups in order of decreasing work across all groups (phase 0's tiles take s - 64 jb
+  // of K, phase 1's 64 (ib + 1)), so the longest start first and the short ones fill in
+  const int64_t nbs = s / DB, per = nbs * g;
+  const int64_t q = blockIdx.x / per, rem = blockIdx.x % per, rr = rem % nbs;
+  const int64_t a0 = (rem / nbs) * 2 * s, c0 = a0 + s;
   const int64_t sc = np - c0 < s ? np - c0 : s;
-  const int64_t nbs = s / DB;
-  const int64_t ib = blockIdx.x / nbs, jb = blockIdx.x % nbs;  // output block (C row, A col)
+  const int64_t jb = phase == 0 ? q : rr, ib = phase == 0 ? rr : nbs - 1 - q;  // C row, A col
   if (ib * DB >= sc) return;
   const int64_t r0 = c0 + ib * DB, q0 = a0 + jb * DB;  // global row / column of the block
   DAcc acc;
@@ -659,39 +615,6 @@ __global__ void __launch_bounds__(256)
       dmma(acc, LA, LB);
     }
     dacc_each(acc, [&](int r, int c, double v) { X[(r0 + r) * np + q0 + c] = -v; });
-  }
-}
-
-// The same level with 128 x 128 output tiles (levels s >= 128). Whole tiles of X[A][A] and
-// X[C][C] are read, so X's upper triangle must be zero (it is).
-__global__ void __launch_bounds__(W2T)
-    k_trtri_level2(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t s,
-                   int phase) {
-  __shared__ __attribute__((aligned(16))) double L2[4 * KC * P2];  // two (A, B) chunk buffers
-  const int64_t a0 = (int64_t)blockIdx.y * 2 * s, c0 = a0 + s;
-  const int64_t sc = np - c0 < s ? np - c0 : s;
-  const int64_t nbs = s / T2;
-  const int64_t ib = blockIdx.x / nbs, jb = blockIdx.x % nbs;
-  if (ib * T2 >= sc) return;
-  const int mlim = (int)(sc - ib * T2 < T2 ? sc - ib * T2 : T2);
-  const int64_t r0 = c0 + ib * T2, q0 = a0 + jb * T2;
-  DAcc2 acc;
-  d2_zero(acc);
-  if (phase == 0) {
-    // T = L[C rows][A] X[A][q0 cols]; X_AA is lower, so k runs from q0 - a0
-    const int64_t k0 = jb * T2;
-    d2_gemm<true>(acc, A + r0 * np + a0 + k0, np, mlim, X + (a0 + k0) * np + q0, np, T2, s - k0,
-                  s - k0, L2);
-    d2_each(acc, [&](int r, int c, double v) {
-      if (r < mlim) A[(q0 + c) * np + r0 + r] = v;
-    });
-  } else {
-    // X[C][A] = -X[C][C] T, X_CC lower: k up to the tile's last row
-    const int64_t kend = ib * T2 + mlim;
-    d2_gemm<false>(acc, X + r0 * np + c0, np, mlim, A + q0 * np + c0, np, T2, kend, kend, L2);
-    d2_each(acc, [&](int r, int c, double v) {
-      if (r < mlim) X[(r0 + r) * np + q0 + c] = -v;
-    });
   }
 }
 
@@ -777,17 +700,10 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
     int64_t g = groups;
     if (groups * 2 * s - s >= np) --g;  // the last group has no C range
     if (g <= 0) continue;
-    if (s >= T2) {
-      const int64_t nbs = s / T2;
-      const dim3 grid((unsigned)(nbs * nbs), (unsigned)g);  // tiles in x: up to 65536 of them
-      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(W2T), 0, st, A, X, np, s, 0);
-      hipLaunchKernelGGL(k_trtri_level2, grid, dim3(W2T), 0, st, A, X, np, s, 1);
-    } else {
-      const int64_t nbs = s / DB;
-      const dim3 grid((unsigned)(nbs * nbs), (unsigned)g);  // tiles in x: up to 65536 of them
-      hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 0);
-      hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, 1);
-    }
+    const int64_t nbs = s / DB;
+    const dim3 grid((unsigned)(nbs * nbs * g));  // (np / 64)^2 / 2 at most
+    hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, g, 0);
+    hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, g, 1);
   }
   hipLaunchKernelGGL(k_gptq_store_u, dim3(grid_for(n * n)), dim3(256), 0, st, X, n, np, U);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
