@@ -89,6 +89,57 @@ __device__ __forceinline__ void dload_kn(double *T, const double *src, int64_t l
   }
 }
 
+// The same loads in two halves: into registers (issued before the current chunk's products)
+// and from there into LDS (after them), so a chunk's global reads overlap the previous
+// chunk's products with one LDS buffer
+struct DPre {
+  double2 v[8];
+};
+
+__device__ __forceinline__ void dpre_mk(DPre &r, const double *src, int64_t ld, int mlim, int klim) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + t;
+    const int m = idx >> 5, k = (idx & 31) * 2;
+    r.v[s] = m < mlim && k < klim ? *reinterpret_cast<const double2 *>(src + (int64_t)m * ld + k)
+                                  : make_double2(0.0, 0.0);
+  }
+}
+
+__device__ __forceinline__ void dput_mk(double *T, const DPre &r) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + t;
+    const int m = idx >> 5, k = (idx & 31) * 2;
+    T[k * DP + m] = r.v[s].x;
+    T[(k + 1) * DP + m] = r.v[s].y;
+  }
+}
+
+__device__ __forceinline__ void dpre_kn(DPre &r, const double *src, int64_t ld, int klim, int nlim) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + t;
+    const int k = idx >> 5, n = (idx & 31) * 2;
+    r.v[s] = k < klim && n < nlim ? *reinterpret_cast<const double2 *>(src + (int64_t)k * ld + n)
+                                  : make_double2(0.0, 0.0);
+  }
+}
+
+__device__ __forceinline__ void dput_kn(double *T, const DPre &r) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int idx = s * 256 + t;
+    const int k = idx >> 5, n = (idx & 31) * 2;
+    T[k * DP + n] = r.v[s].x;
+    T[k * DP + n + 1] = r.v[s].y;
+  }
+}
+
 struct DAcc {
   gq_v4d c[2][2];
 };
@@ -154,15 +205,27 @@ __device__ __forceinline__ void d64_sub(double *C, int64_t ldc, int nlim, const 
   }
   DAcc acc;
   dacc_zero(acc);
+  auto kl = [&](int c) {
+    const int64_t kb = (int64_t)c * DB;
+    return (int)(klim - kb < DB ? (klim - kb > 0 ? klim - kb : 0) : DB);
+  };
+  DPre ra, rb;
+  dpre_mk(ra, A, lda, DB, kl(0));
+  if (KN) dpre_kn(rb, B, ldb, kl(0), nlim);
+  else dpre_mk(rb, B, ldb, nlim, kl(0));
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int64_t kb = (int64_t)c * DB;
-    const int kl = (int)(klim - kb < DB ? (klim - kb > 0 ? klim - kb : 0) : DB);
     if (c) __syncthreads();
-    dload_mk(LA, A + kb, lda, DB, kl);
-    if (KN) dload_kn(LB, B + kb * ldb, ldb, kl, nlim);
-    else dload_mk(LB, B + kb, ldb, nlim, kl);
+    dput_mk(LA, ra);
+    if (KN) dput_kn(LB, rb);
+    else dput_mk(LB, rb);
     __syncthreads();
+    if (c + 1 < NCH) {
+      const int64_t kb = (int64_t)(c + 1) * DB;
+      dpre_mk(ra, A + kb, lda, DB, kl(c + 1));
+      if (KN) dpre_kn(rb, B + kb * ldb, ldb, kl(c + 1), nlim);
+      else dpre_mk(rb, B + kb, ldb, nlim, kl(c + 1));
+    }
     dmma(acc, LA, LB);
   }
 #pragma unroll
@@ -595,23 +658,37 @@ __global__ void __launch_bounds__(256)
   dacc_zero(acc);
   if (phase == 0) {
     // sum over A-range blocks kb >= jb: L[r0][kb] X[kb][q0]
+    DPre ra, rb;
+    dpre_mk(ra, A + r0 * np + a0 + jb * DB, np, DB, DB);
+    dpre_kn(rb, X + (a0 + jb * DB) * np + q0, np, DB, DB);
     for (int64_t kb = jb; kb < nbs; ++kb) {
-      const int64_t k0 = a0 + kb * DB;
       __syncthreads();
-      dload_mk(LA, A + r0 * np + k0, np, DB, DB);
-      dload_kn(LB, X + k0 * np + q0, np, DB, DB);
+      dput_mk(LA, ra);
+      dput_kn(LB, rb);
       __syncthreads();
+      if (kb + 1 < nbs) {
+        const int64_t k1 = a0 + (kb + 1) * DB;
+        dpre_mk(ra, A + r0 * np + k1, np, DB, DB);
+        dpre_kn(rb, X + k1 * np + q0, np, DB, DB);
+      }
       dmma(acc, LA, LB);
     }
     dacc_each(acc, [&](int r, int c, double v) { A[(q0 + c) * np + r0 + r] = v; });
   } else {
     // sum over C-range blocks kb <= ib: X[r0][kb] T[kb][q0], T[kb][q0] stored at A[q0][kb]
+    DPre ra, rb;
+    dpre_mk(ra, X + r0 * np + c0, np, DB, DB);
+    dpre_mk(rb, A + q0 * np + c0, np, DB, DB);
     for (int64_t kb = 0; kb <= ib; ++kb) {
-      const int64_t k0 = c0 + kb * DB;
       __syncthreads();
-      dload_mk(LA, X + r0 * np + k0, np, DB, DB);
-      dload_mk(LB, A + q0 * np + k0, np, DB, DB);
+      dput_mk(LA, ra);
+      dput_mk(LB, rb);
       __syncthreads();
+      if (kb + 1 <= ib) {
+        const int64_t k1 = c0 + (kb + 1) * DB;
+        dpre_mk(ra, X + r0 * np + k1, np, DB, DB);
+        dpre_mk(rb, A + q0 * np + k1, np, DB, DB);
+      }
       dmma(acc, LA, LB);
     }
     dacc_each(acc, [&](int r, int c, double v) { X[(r0 + r) * np + q0 + c] = -v; });
