@@ -550,11 +550,18 @@ __global__ void __launch_bounds__(256)
       d[j] = i == j ? ljj : d[j] * rl;      // right of the diagonal, d holds unused values
       Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
       if (i == j) rinv[j] = rl;
+      // the next pivot's column first, with L[j+1][j] read from lane j + 1 (off the LDS
+      // round trip, which only the rest of the column waits for)
+      if (j + 1 < DB) {
+        const int slo = __builtin_amdgcn_readlane(__double2loint(d[j]), j + 1);
+        const int shi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j + 1);
+        d[j + 1] = fma(-d[j], __hiloint2double(shi, slo), d[j + 1]);
+      }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       const double *col = Lt + j * DB;
 #pragma unroll
-      for (int l = j + 1; l < DB; ++l) d[l] = fma(-d[j], col[l], d[l]);
+      for (int l = j + 2; l < DB; ++l) d[l] = fma(-d[j], col[l], d[l]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (blockIdx.x == 0) {
