@@ -232,6 +232,26 @@ def test_gptq_rows_same_factor(orc, which):
     check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9)
 
 
+def test_gptq_rows_workspace_contents_unread(orc):
+    """GPTQ rounding writes every part of its workspace that it reads (the working copy of W,
+    padding included, and each outer block's errors): a NaN-filled workspace gives the same
+    codes as a zeroed one. 100 x 1040: padded rows and columns, 4 full outer blocks + 1."""
+    case("gptq rows 100x1040: NaN-filled workspace")
+    w, x = synth.projection(17, rows=100, cols=1040, tokens=2500)
+    wn = f32(w)
+    S = orc.tensor_scale(wn)
+    sc = orc.scales_local_hessian(wn, S, orc.block_hessian(f32(x)))
+    U, status = nvfp4.gptq_factor(torch.from_numpy(orc.full_hessian(f32(x)).astype(np.float32)).to(DEV), 0.01)
+    assert status.item() == 0
+    need = int(nvfp4.lib().nvfp4_gptq_workspace_size(100, 1040))
+    ws0 = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    wsn = torch.full((need // 8,), float("nan"), dtype=torch.float64, device=DEV).view(torch.uint8)
+    args = (w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV), U)
+    c0 = nvfp4.gptq(*args, workspace=ws0)
+    cn = nvfp4.gptq(*args, workspace=wsn)
+    assert torch.equal(c0, cn)
+
+
 def test_gptq_end_to_end(orc):
     """GPU H -> GPU factor -> GPU GPTQ against the oracle's chain from the same X."""
     case("gptq end to end 128x512 bf16")
