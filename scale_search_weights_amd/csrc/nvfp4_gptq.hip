@@ -922,9 +922,21 @@ __global__ void __launch_bounds__(256)
   const double half = 0.5 * sS, twice = 2.0 * sS;
   unsigned cw = 0u;
   double ev[4] = {0.0, 0.0, 0.0, 0.0};
+  // kept in registers off the column chain: 1 / U_jj for this lane's own four columns (only
+  // the owning lane's e is used), and U's next row, read one column ahead
+  double ru[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ru[i] = RU[4 * p + i];
+  double2 un01 = *reinterpret_cast<const double2 *>(LU + 4 * p);
+  double2 un23 = *reinterpret_cast<const double2 *>(LU + 4 * p + 2);
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
     const int pj = j >> 2, jj = j & 3;
+    const double2 u01 = un01, u23 = un23;
+    if (j + 1 < DB) {
+      un01 = *reinterpret_cast<const double2 *>(LU + (j + 1) * DB + 4 * p);
+      un23 = *reinterpret_cast<const double2 *>(LU + (j + 1) * DB + 4 * p + 2);
+    }
     const double x = v[jj];
     const double a = fabs(x);
     // round half to even onto {0, .5, 1, 1.5, 2, 3, 4, 6} sS: crossing midpoint i moves up
@@ -936,13 +948,11 @@ __global__ void __launch_bounds__(256)
                       (b6 ? twice : 0.0);  // exact: small multiples of sS / 2
     const double q = x < 0.0 ? -qm : qm;
     const unsigned code = (unsigned)k | ((x < 0.0 && k > 0) ? 8u : 0u);
-    const double e_own = (x - q) * RU[j];
+    const double e_own = (x - q) * ru[jj];
     const bool mine = p == pj;
     cw |= mine ? code << (4 * jj) : 0u;
     ev[jj] = mine ? e_own : ev[jj];
     const double e = row_bcast16(e_own, pj);
-    const double2 u01 = *reinterpret_cast<const double2 *>(LU + j * DB + 4 * p);
-    const double2 u23 = *reinterpret_cast<const double2 *>(LU + j * DB + 4 * p + 2);
     v[0] = fma(-e, u01.x, v[0]);
     v[1] = fma(-e, u01.y, v[1]);
     v[2] = fma(-e, u23.x, v[2]);
