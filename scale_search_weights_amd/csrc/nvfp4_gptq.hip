@@ -525,6 +525,19 @@ __global__ void __launch_bounds__(256)
   __shared__ double rinv[DB];
   const int t = threadIdx.x;
   double *blk = A + k * DB * np + k * DB;
+  // this thread's part of the panel block, read now so that the read overlaps the diagonal
+  // block's factorisation (four lanes per row, 16 columns each)
+  const int p = t & 3;
+  double *ar = A + ((k + (blockIdx.x ? blockIdx.x : 1)) * DB + (t >> 2)) * np + k * DB + 16 * p;
+  double a[16];
+  if (blockIdx.x != 0) {
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const double2 v = *reinterpret_cast<const double2 *>(ar + j);
+      a[j] = v.x;
+      a[j + 1] = v.y;
+    }
+  }
   if (t < DB) {
     const int i = t;
     double d[DB];
@@ -575,15 +588,6 @@ __global__ void __launch_bounds__(256)
   }
   if (blockIdx.x == 0) return;
   __syncthreads();
-  const int p = t & 3;
-  double *ar = A + ((k + blockIdx.x) * DB + (t >> 2)) * np + k * DB + 16 * p;
-  double a[16];
-#pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    const double2 v = *reinterpret_cast<const double2 *>(ar + j);
-    a[j] = v.x;
-    a[j + 1] = v.y;
-  }
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
     const int pj = j >> 4, jj = j & 15;
@@ -605,14 +609,8 @@ __global__ void __launch_bounds__(256)
     k_chol_colupd(double *__restrict__ A, int64_t np, int64_t k) {
   __shared__ double LA[DB * DP], LB[DB * DP];
   const int64_t bi = k + 1 + blockIdx.x, bj = k + 1;
-  dload_mk(LA, A + bi * DB * np + k * DB, np, DB, DB);
-  dload_mk(LB, A + bj * DB * np + k * DB, np, DB, DB);
-  __syncthreads();
-  DAcc acc;
-  dacc_zero(acc);
-  dmma(acc, LA, LB);
-  double *C = A + bi * DB * np + bj * DB;
-  dacc_each(acc, [&](int r, int c, double v) { C[r * np + c] -= v; });
+  d64_sub<false, 1>(A + bi * DB * np + bj * DB, np, DB, A + bi * DB * np + k * DB, np,
+                    A + bj * DB * np + k * DB, np, DB, LA, LB);
 }
 
 // inverses of the diagonal blocks, in place in X (where the steps left L_bb): column c of
@@ -919,7 +917,7 @@ __global__ void __launch_bounds__(256)
   const double T0 = byte ? 0.25 * sS : big, T1 = byte ? 0.75 * sS : big,
                T2 = byte ? 1.25 * sS : big, T3 = byte ? 1.75 * sS : big,
                T4 = byte ? 2.5 * sS : big, T5 = byte ? 3.5 * sS : big, T6 = byte ? 5.0 * sS : big;
-  const double half = 0.5 * sS, twice = 2.0 * sS;
+  const double half = 0.5 * sS;
   unsigned cw = 0u;
   double ev[4] = {0.0, 0.0, 0.0, 0.0};
   // kept in registers off the column chain: 1 / U_jj for this lane's own four columns (only
@@ -944,8 +942,8 @@ __global__ void __launch_bounds__(256)
     const int b0 = a > T0, b1 = a >= T1, b2 = a > T2, b3 = a >= T3, b4 = a > T4, b5 = a >= T5,
               b6 = a > T6;
     const int k = b0 + b1 + b2 + b3 + b4 + b5 + b6;
-    const double qm = (double)(b0 + b1 + b2 + b3) * half + (double)(b4 + b5) * sS +
-                      (b6 ? twice : 0.0);  // exact: small multiples of sS / 2
+    // grid value in halves of sS: steps of 1/2 up to 2, then 3, 4, 6 (exact: at most 12 sS / 2)
+    const double qm = (double)(b0 + b1 + b2 + b3 + 2 * (b4 + b5) + 4 * b6) * half;
     const double q = x < 0.0 ? -qm : qm;
     const unsigned code = (unsigned)k | ((x < 0.0 && k > 0) ? 8u : 0u);
     const double e_own = (x - q) * ru[jj];
