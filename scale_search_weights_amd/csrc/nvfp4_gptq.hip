@@ -59,39 +59,10 @@ size_t gptq_rows_workspace_size(int64_t rows, int64_t n) {
 // columns; D: lane l, register r holds row (l >> 4) + 4 r of column l & 15, unlike the
 // fp32 16x16x4 form, whose rows are 4 (l >> 4) + r).
 
-// element (m, k) at src[m * ld + k] (k contiguous), zero outside m < mlim, k < klim
-__device__ __forceinline__ void dload_mk(double *T, const double *src, int64_t ld, int mlim,
-                                         int klim) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = s * 256 + t;
-    const int m = idx >> 5, k = (idx & 31) * 2;
-    double2 v = make_double2(0.0, 0.0);
-    if (m < mlim && k < klim) v = *reinterpret_cast<const double2 *>(src + (int64_t)m * ld + k);
-    T[k * DP + m] = v.x;
-    T[(k + 1) * DP + m] = v.y;
-  }
-}
-
-// element (k, n) at src[k * ld + n] (n contiguous), zero outside k < klim, n < nlim
-__device__ __forceinline__ void dload_kn(double *T, const double *src, int64_t ld, int klim,
-                                         int nlim) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int idx = s * 256 + t;
-    const int k = idx >> 5, n = (idx & 31) * 2;
-    double2 v = make_double2(0.0, 0.0);
-    if (k < klim && n < nlim) v = *reinterpret_cast<const double2 *>(src + (int64_t)k * ld + n);
-    T[k * DP + n] = v.x;
-    T[k * DP + n + 1] = v.y;
-  }
-}
-
-// The same loads in two halves: into registers (issued before the current chunk's products)
-// and from there into LDS (after them), so a chunk's global reads overlap the previous
-// chunk's products with one LDS buffer
+// Tile loads in two halves: into registers (issued before the current chunk's products) and
+// from there into LDS (after them), so a chunk's global reads overlap the previous chunk's
+// products with one LDS buffer. mk: element (m, k) at src[m * ld + k] (k contiguous); kn:
+// element (k, n) at src[k * ld + n] (n contiguous); zero outside the limits
 struct DPre {
   double2 v[8];
 };
