@@ -232,6 +232,22 @@ def test_gptq_rows_same_factor(orc, which):
     check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9)
 
 
+def test_gptq_rows_wide_and_narrow_outer_updates(orc):
+    """4096 x 1280: the first outer update has 32 x 8 = 256 tiles of 128 x 128 (the wide form,
+    which reads its output tile beside the products), the later ones fewer (the 64 x 64 form).
+    The oracle's own U and max-scaling bytes feed both sides."""
+    case("gptq rows 4096x1280 bf16: wide and 64x64 outer updates")
+    w, x = synth.projection(18, rows=4096, cols=1280, tokens=3000)
+    wn = f32(w)
+    S = orc.tensor_scale(wn)
+    sc = orc.scales_max(wn, S)
+    Ur = orc.gptq_factor(orc.full_hessian(f32(x)).astype(np.float32).astype(np.float64), 0.01)
+    want, v_ref = orc.gptq(wn, S, sc, U=Ur, return_v=True)
+    got = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV),
+                     torch.from_numpy(Ur).to(DEV))
+    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9, max_rows_frac=0.002)
+
+
 def test_gptq_rows_workspace_contents_unread(orc):
     """GPTQ rounding writes every part of its workspace that it reads (the working copy of W,
     padding included, and each outer block's errors): a NaN-filled workspace gives the same
