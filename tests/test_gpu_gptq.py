@@ -151,6 +151,23 @@ def test_gptq_factor(orc, n):
     assert not np.tril(Ug, -1).any()
 
 
+def test_gptq_factor_wide_and_narrow_updates(orc):
+    """n = 3072: the first Cholesky trailing updates have 24 * 25 / 2 = 300 tiles of 128 x 128
+    (the wide form), the later ones fewer than the compute units (the 64 x 64 form). A weakly
+    correlated H (condition number about 400) keeps the fp64 error far below the bound."""
+    n = 3072
+    case(f"gptq factor n={n}: wide and 64x64 trailing updates")
+    rng = np.random.default_rng(31)
+    X = 0.1 * rng.standard_normal((2 * n, 1)) + rng.standard_normal((2 * n, n))
+    H = (X.T @ X).astype(np.float32)  # any SPD fp32 matrix serves; a BLAS product is quick
+    U, status = nvfp4.gptq_factor(torch.from_numpy(H).to(DEV), 0.01)
+    assert status.item() == 0
+    Ug = U.cpu().numpy()
+    Ur = orc.gptq_factor(H.astype(np.float64), 0.01)
+    assert np.abs(Ug - Ur).max() <= 1e-8 * np.abs(Ur).max()
+    assert not np.tril(Ug, -1).any()
+
+
 def test_gptq_factor_degenerate(orc):
     case("gptq factor: zero H gives I; an indefinite H is reported")
     U, status = nvfp4.gptq_factor(torch.zeros(64, 64, device=DEV), 0.01)
