@@ -319,7 +319,7 @@ int nvfp4_gptq(const void *w, int dtype, int64_t rows, int64_t cols, const float
   if (rc != NVFP4_OK || empty) return rc;
   if (cols > 65536 || (rows + 63) / 64 > INT32_MAX) return NVFP4_ERR_SHAPE;
   if (!w || !S || !scales || !U || !codes) return NVFP4_ERR_NULL;
-  if (!aligned(w, 4) || !aligned(S, 4) || !aligned(U, 16) || !aligned(codes, 8))
+  if (!aligned(w, 16) || !aligned(S, 4) || !aligned(U, 16) || !aligned(codes, 8))
     return NVFP4_ERR_ALIGN;
   if (!workspace || workspace_bytes < gptq_rows_workspace_size(rows, cols)) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;

@@ -671,20 +671,20 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// U[i][j] = X[n-1-i][n-1-j] for i <= j, zero below the diagonal
+// U[i][j] = X[n-1-i][n-1-j] for i <= j, zero below the diagonal. Thread x of a row writes
+// columns 4x .. 4x + 3 (n is a multiple of 16); rows by grid-stride over y, no index division.
 __global__ void __launch_bounds__(256)
     k_gptq_store_u(const double *__restrict__ X, int64_t n, int64_t np, double *__restrict__ U) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n * n;
-       e += (int64_t)gridDim.x * 256) {
-    const int64_t i = e / n, j = e % n;
-    U[e] = i <= j ? X[(n - 1 - i) * np + (n - 1 - j)] : 0.0;
+  const int64_t j = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (j >= n) return;
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    const double *src = X + (n - 1 - i) * np + (n - 1 - j);  // column n-1-j, then leftwards
+    double u[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = i <= j + q ? src[-q] : 0.0;
+    *reinterpret_cast<double2 *>(U + i * n + j) = make_double2(u[0], u[1]);
+    *reinterpret_cast<double2 *>(U + i * n + j + 2) = make_double2(u[2], u[3]);
   }
-}
-
-static unsigned grid_for(int64_t elems) {
-  int64_t g = (elems + 255) / 256;
-  if (g > 65536) g = 65536;
-  return (unsigned)(g > 0 ? g : 1);
 }
 
 // trailing update after a pair of steps: for the lower-triangular 128 x 128 tiles of the
@@ -758,26 +758,39 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
     hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, g, 0);
     hipLaunchKernelGGL(k_trtri_level, grid, dim3(256), 0, st, A, X, np, s, g, 1);
   }
-  hipLaunchKernelGGL(k_gptq_store_u, dim3(grid_for(n * n)), dim3(256), 0, st, X, n, np, U);
+  hipLaunchKernelGGL(k_gptq_store_u, dim3((unsigned)((n / 4 + 255) / 256), (unsigned)(n < 65535 ? n : 65535)),
+                     dim3(256), 0, st, X, n, np, U);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 // ------------------------------------------------------------------ rows
+// the working copy V [rp][np] (fp64) of W [rows][n], zero in the padding. Thread x of a row
+// fills columns 4x .. 4x + 3 (n and np are multiples of 16); rows by grid-stride over y.
 template <int DT>
 __global__ void __launch_bounds__(256)
     k_gptq_init(const void *__restrict__ w, int64_t rows, int64_t n, int64_t rp, int64_t np,
                 double *__restrict__ V) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < rp * np;
-       e += (int64_t)gridDim.x * 256) {
-    const int64_t r = e / np, c = e % np;
-    double v = 0.0;
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= np) return;
+  for (int64_t r = blockIdx.y; r < rp; r += gridDim.y) {
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
     if (r < rows && c < n) {
-      if (DT == NVFP4_DTYPE_BF16)
-        v = (double)__uint_as_float((unsigned)static_cast<const uint16_t *>(w)[r * n + c] << 16);
-      else
-        v = (double)static_cast<const float *>(w)[r * n + c];
+      if (DT == NVFP4_DTYPE_BF16) {
+        const uint2 h = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(w) + r * n + c);
+        v[0] = (double)__uint_as_float(h.x << 16);
+        v[1] = (double)__uint_as_float(h.x & 0xFFFF0000u);
+        v[2] = (double)__uint_as_float(h.y << 16);
+        v[3] = (double)__uint_as_float(h.y & 0xFFFF0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(w) + r * n + c);
+        v[0] = (double)f.x;
+        v[1] = (double)f.y;
+        v[2] = (double)f.z;
+        v[3] = (double)f.w;
+      }
     }
-    V[e] = v;
+    *reinterpret_cast<double2 *>(V + r * np + c) = make_double2(v[0], v[1]);
+    *reinterpret_cast<double2 *>(V + r * np + c + 2) = make_double2(v[2], v[3]);
   }
 }
 
@@ -989,10 +1002,10 @@ int launch_gptq_rows(const void *w, int dtype, int64_t rows, int64_t n, const fl
   double *E = V + rp * np;
   const int64_t cus = gptq_cus();
   if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_BF16>, dim3(grid_for(rp * np)), dim3(256), 0, st, w,
+    hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_BF16>, dim3((unsigned)((np / 4 + 255) / 256), (unsigned)(rp < 65535 ? rp : 65535)), dim3(256), 0, st, w,
                        rows, n, rp, np, V);
   else
-    hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_F32>, dim3(grid_for(rp * np)), dim3(256), 0, st, w,
+    hipLaunchKernelGGL(k_gptq_init<NVFP4_DTYPE_F32>, dim3((unsigned)((np / 4 + 255) / 256), (unsigned)(rp < 65535 ? rp : 65535)), dim3(256), 0, st, w,
                        rows, n, rp, np, V);
   // blocks of 64 columns; inside an outer block of 256 a block's errors update only the
   // rest of that outer block (within k_gptq_block), and each outer block then updates
