@@ -209,10 +209,20 @@ int oracle_max_byte(float amax, float S)
     return oracle_byte_for_divisor(amax, S, 6.0);
 }
 
+/* A block byte as an E4M3FN magnitude: the sign bit plays no part in a scale, and 0x7F is
+ * NaN, not one of the 126 candidates; such a block (like an all-zero one, byte 0) is coded
+ * as zeros. Bytes 0x00..0x7E are returned unchanged. */
+static int given_byte(int byte)
+{
+    int m = byte & 0x7F;
+    return m == 0x7F ? 0 : m;
+}
+
 /* E2M1 code of x under block byte `byte` and tensor scale S: round half to even on the
  * exact ratio |x| / (s S), saturating at 6 ([QAD] sec. 2.1). */
 int oracle_e2m1_code(float x, int byte, float S)
 {
+    byte = given_byte(byte);
     if (byte == 0) return 0;
     double ax = fabs((double)x);
     double sS = oracle_e4m3_value(byte) * (double)S; /* exact, <= 28 bits */
@@ -230,6 +240,7 @@ int oracle_e2m1_code(float x, int byte, float S)
 float oracle_dequant_value(int code, int byte, float S)
 {
     int k = code & 7;
+    byte = given_byte(byte);
     if (byte == 0 || k == 0) return 0.0f;
     double mag = E2M1_MAG[k] * oracle_e4m3_value(byte) * (double)S; /* exact */
     float d = (float)mag;
@@ -496,6 +507,7 @@ void oracle_full_hessian(const float *X, int64_t tokens, int64_t cols, double *H
  * The products mid * s * S are exact in double, so the comparisons are exact. */
 int oracle_e2m1_code_d(double v, int byte, float S)
 {
+    byte = given_byte(byte);
     if (byte == 0) return 0;
     double av = fabs(v);
     double sS = oracle_e4m3_value(byte) * (double)S;
@@ -594,7 +606,7 @@ void oracle_gptq_rows(const float *w, int64_t rows, int64_t n, float S, const ui
         double *v = (double *)malloc(sizeof(double) * n);
         for (int64_t k = 0; k < n; ++k) v[k] = (double)w[r * n + k];
         for (int64_t j = 0; j < n; ++j) {
-            int byte = scales[r * nb + j / 16];
+            int byte = given_byte(scales[r * nb + j / 16]);
             int code = oracle_e2m1_code_d(v[j], byte, S);
             if (vout) vout[r * n + j] = v[j];
             double q = E2M1_MAG[code & 7] * oracle_e4m3_value(byte) * (double)S; /* exact */

@@ -16,9 +16,17 @@
 
 namespace nvfp4 {
 
-// Value of E4M3FN byte b in 0..126 (exponent bias 7, subnormals m * 2^-9).
+// A block byte given by the caller, read as an E4M3FN magnitude: the sign bit is ignored,
+// and 0x7F (NaN, not one of the 126 candidates) codes its block as zeros, like 0x00.
+__device__ __forceinline__ int given_byte(int b) {
+  const int m = b & 0x7F;
+  return m == 0x7F ? 0 : m;
+}
+
+// Value of E4M3FN byte b in 0..126 (exponent bias 7, subnormals m * 2^-9); the sign bit
+// of a larger byte is ignored.
 __device__ __forceinline__ float e4m3_value(int b) {
-  int e = b >> 3, m = b & 7;
+  int e = (b >> 3) & 15, m = b & 7;
   return e ? ldexpf(float(8 + m), e - 10) : ldexpf(float(m), -9);
 }
 

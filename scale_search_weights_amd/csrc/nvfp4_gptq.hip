@@ -832,7 +832,7 @@ __global__ void __launch_bounds__(256)
   const bool live = r < rows && cb < n;
   const double2 v01 = *reinterpret_cast<const double2 *>(V + r * np + cb);
   const double2 v23 = *reinterpret_cast<const double2 *>(V + r * np + cb + 2);
-  const int byte = live ? scales[r * (n / 16) + cb / 16] : 0;
+  const int byte = live ? given_byte(scales[r * (n / 16) + cb / 16]) : 0;
   // the rest of this 256-column outer block (at most 192 columns, 12 tiles of 16), updated
   // after the column loop: wave w takes tiles w, w + 4, w + 8, whose rows of U and values of
   // V are read here (n is a multiple of 16; when any tile follows, all 64 rows of U's block

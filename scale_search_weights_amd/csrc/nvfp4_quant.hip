@@ -6,9 +6,12 @@
 // on NVFP4 quality, "Why do we need a scale" and "Block scaling").
 //
 // Work mapping: two lanes own one 16-value block (16 B of bf16 each), so a wave streams
-// 1 KiB of contiguous input per load and the block max needs one lane-pair exchange. The kernel is HBM-bound. Rounding decisions use the hardware
-// FP8/FP4 converts on two bracketing products (nvfp4_device.h); a value whose bracket
-// straddles a midpoint takes the exact threshold path.
+// 1 KiB of contiguous input per load and the block max needs one lane-pair exchange. The
+// kernel is HBM-bound. Rounding decisions use the hardware FP8/FP4 converts on two
+// bracketing products (nvfp4_device.h); a value whose bracket straddles a midpoint takes
+// the exact threshold path. Outputs use non-temporal stores: with ordinary stores the
+// kernel itself finishes sooner, but the dirty lines it leaves in the caches are written
+// back during the kernels that follow, which then take longer than the time saved.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -219,29 +222,26 @@ __device__ __forceinline__ void unpack_raw8(const Raw8 &r, float v[8]) {
   }
 }
 
+// Grid: x = chunks of 256 half blocks within one tensor, y = batch entry. Every workgroup
+// belongs to one tensor, so it builds that tensor's 127-entry byte table (E4M3 value, the
+// bracket of 1/(sS), and the bracket of 1/(6S)) once in LDS and no lane runs fp64 work.
 template <int DT, int OUT_DT, int FLAGS>
 __global__ void __launch_bounds__(256)
     k_quant(const void *__restrict__ x, const float *__restrict__ S_arr,
              const uint8_t *__restrict__ scales_in, uint8_t *__restrict__ codes,
-             uint8_t *__restrict__ scales_out, void *__restrict__ y, int64_t blocks_per_batch,
-             int64_t total_blocks) {
-  const bool one_batch = blocks_per_batch == total_blocks;
-  const float S0 = S_arr[0];  // uniform: a scalar load
-  const int64_t total_half = 2 * total_blocks;
+             uint8_t *__restrict__ scales_out, void *__restrict__ y, int64_t blocks_per_batch) {
+  const float S = S_arr[blockIdx.y];  // uniform: a scalar load
+  const int64_t n_half = 2 * blocks_per_batch;
+  const int64_t off = (int64_t)blockIdx.y * n_half;  // the entry's first half block
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t hb0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t l0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   // the first load (clamped to a valid index) is in flight while the table is built
-  const Raw8 first = load_raw8<DT>(x, hb0 < total_half ? hb0 : total_half - 1);
-  // one tensor: the per-byte constants come from a table built once per workgroup
+  const Raw8 first = load_raw8<DT>(x, off + (l0 < n_half ? l0 : n_half - 1));
   __shared__ Cand tab[127];
-  if (one_batch) {
-    build_cands(tab, S0);
-    lds_barrier();
-  }
+  build_cands(tab, S);
+  lds_barrier();
   auto block = [&](int64_t hb, const Raw8 &raw) {
     const int64_t blk = hb >> 1;
-    const int h = (int)(hb & 1);
-    const float S = one_batch ? S0 : S_arr[blk / blocks_per_batch];
     float v[8];
     unpack_raw8<DT>(raw, v);
     float amax = 0.0f;
@@ -250,35 +250,16 @@ __global__ void __launch_bounds__(256)
     // the two lanes of a block are lanes 2k and 2k+1 (both active): DPP quad_perm [1,0,3,2]
     amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
                                                                    0xF, 0xF, false)));
-    int byte;
-    if (FLAGS & F_SCALES_IN) {
-      byte = scales_in[blk];
-    } else {
-      float qlo, qhi;
-      if (one_batch) {
-        qlo = tab[0].rlo;
-        qhi = tab[0].rhi;
-      } else {
-        recip_bracket(6.0 * (double)S, qlo, qhi);
-      }
-      byte = max_scale_byte_fast(amax, qlo, qhi, S);
-    }
+    const int byte = (FLAGS & F_SCALES_IN) ? given_byte(scales_in[blk])
+                                           : max_scale_byte_fast(amax, tab[0].rlo, tab[0].rhi, S);
     unsigned c = 0u;
     float s = 0.0f;
     if (byte) {
-      float rlo, rhi;
-      if (one_batch) {
-        const Cand e = tab[byte];
-        s = e.s;
-        rlo = e.rlo;
-        rhi = e.rhi;
-      } else {
-        s = e4m3_value(byte);
-        recip_bracket((double)s * (double)S, rlo, rhi);
-      }
+      const Cand e = tab[byte];
+      s = e.s;
       const double sS = (double)s * (double)S;
-      if (rlo >= 0x1p-126f && amax * rhi < 0x1p126f) {
-        c = fp4_exact_codes8(v, rlo, rhi, sS);
+      if (e.rlo >= 0x1p-126f && amax * e.rhi < 0x1p126f) {
+        c = fp4_exact_codes8(v, e.rlo, e.rhi, sS);
       } else {
         ScaleTable tb;
         make_table(byte, S, tb);
@@ -287,7 +268,7 @@ __global__ void __launch_bounds__(256)
       c = fp4_clear_neg_zero(c);
     }
     if (FLAGS & F_CODES) NVFP4_ST(reinterpret_cast<unsigned *>(codes) + hb, c);
-    if ((FLAGS & F_SCALES_OUT) && h == 0) st_out(scales_out + blk, (uint8_t)byte);
+    if ((FLAGS & F_SCALES_OUT) && (hb & 1) == 0) st_out(scales_out + blk, (uint8_t)byte);
     if (FLAGS & F_Y) {
       float dq[8];
       fp4_decode8(c, dq);
@@ -305,25 +286,24 @@ __global__ void __launch_bounds__(256)
       }
     }
   };
-  if (hb0 < total_half) block(hb0, first);
-  for (int64_t hb = hb0 + stride; hb < total_half; hb += stride) block(hb, load_raw8<DT>(x, hb));
+  if (l0 < n_half) block(off + l0, first);
+  for (int64_t l = l0 + stride; l < n_half; l += stride) block(off + l, load_raw8<DT>(x, off + l));
 }
 
-static unsigned grid_for(int64_t total_blocks) {
-  int64_t g = (total_blocks + 255) / 256;
+static unsigned grid_for(int64_t n) {
+  int64_t g = (n + 255) / 256;
   const int64_t cap = 1 << 20;
   return (unsigned)(g > cap ? cap : (g < 1 ? 1 : g));
 }
 
 template <int DT, int OUT_DT>
 static void dispatch_quant(int flags, const void *x, const float *S, const uint8_t *si,
-                           uint8_t *codes, uint8_t *so, void *y, int64_t bpb, int64_t total,
+                           uint8_t *codes, uint8_t *so, void *y, int64_t batch, int64_t bpb,
                            hipStream_t st) {
-  const dim3 b(256), g2(grid_for(2 * total));
+  const dim3 b(256), g2(grid_for(2 * bpb), (unsigned)batch);
 #define NVFP4_Q(F)                                                                              \
   case F:                                                                                       \
-    hipLaunchKernelGGL((k_quant<DT, OUT_DT, F>), g2, b, 0, st, x, S, si, codes, so, y, bpb,    \
-                       total);                                                                  \
+    hipLaunchKernelGGL((k_quant<DT, OUT_DT, F>), g2, b, 0, st, x, S, si, codes, so, y, bpb);   \
     break;
   switch (flags) {
     NVFP4_Q(F_CODES)
@@ -345,7 +325,7 @@ static void dispatch_quant(int flags, const void *x, const float *S, const uint8
 int launch_quant(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
                  const float *S, const uint8_t *scales_in, uint8_t *codes, uint8_t *scales_out,
                  void *y, hipStream_t st) {
-  const int64_t bpb = rows * (cols / 16), total = batch * bpb;
+  const int64_t bpb = rows * (cols / 16);
   int flags = 0;
   if (scales_in) flags |= F_SCALES_IN;
   if (codes) flags |= F_CODES;
@@ -353,24 +333,26 @@ int launch_quant(const void *x, int dtype, int64_t batch, int64_t rows, int64_t 
   if (y) flags |= F_Y;
   if (dtype == NVFP4_DTYPE_BF16)
     dispatch_quant<NVFP4_DTYPE_BF16, NVFP4_DTYPE_BF16>(flags, x, S, scales_in, codes, scales_out,
-                                                       y, bpb, total, st);
+                                                       y, batch, bpb, st);
   else
     dispatch_quant<NVFP4_DTYPE_F32, NVFP4_DTYPE_F32>(flags, x, S, scales_in, codes, scales_out,
-                                                     y, bpb, total, st);
+                                                     y, batch, bpb, st);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 // ------------------------------------------------------------------ dequantise
 
+// Grid: x = chunks of blocks within one tensor, y = batch entry (one S per workgroup).
 template <int OUT_DT>
 __global__ void __launch_bounds__(256)
     k_dequant(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-              const float *__restrict__ S_arr, void *__restrict__ y, int64_t blocks_per_batch,
-              int64_t total_blocks) {
-  for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < total_blocks;
-       blk += (int64_t)gridDim.x * blockDim.x) {
-    const float S = S_arr[blk / blocks_per_batch];
-    const int byte = scales[blk];
+              const float *__restrict__ S_arr, void *__restrict__ y, int64_t blocks_per_batch) {
+  const float S = S_arr[blockIdx.y];
+  const int64_t off = (int64_t)blockIdx.y * blocks_per_batch;
+  for (int64_t l = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; l < blocks_per_batch;
+       l += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t blk = off + l;
+    const int byte = given_byte(scales[blk]);
     const uint2 c = reinterpret_cast<const uint2 *>(codes)[blk];
     const float s = byte ? e4m3_value(byte) : 0.0f;
     float dq[16];
@@ -384,12 +366,12 @@ __global__ void __launch_bounds__(256)
 
 int launch_dequant(const uint8_t *codes, const uint8_t *scales, const float *S, int64_t batch,
                    int64_t rows, int64_t cols, void *y, int out_dtype, hipStream_t st) {
-  const int64_t bpb = rows * (cols / 16), total = batch * bpb;
-  const dim3 g(grid_for(total)), b(256), g2(grid_for(2 * total));
+  const int64_t bpb = rows * (cols / 16);
+  const dim3 g(grid_for(bpb), (unsigned)batch), b(256);
   if (out_dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_dequant<NVFP4_DTYPE_BF16>, g, b, 0, st, codes, scales, S, y, bpb, total);
+    hipLaunchKernelGGL(k_dequant<NVFP4_DTYPE_BF16>, g, b, 0, st, codes, scales, S, y, bpb);
   else
-    hipLaunchKernelGGL(k_dequant<NVFP4_DTYPE_F32>, g, b, 0, st, codes, scales, S, y, bpb, total);
+    hipLaunchKernelGGL(k_dequant<NVFP4_DTYPE_F32>, g, b, 0, st, codes, scales, S, y, bpb);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -127,15 +127,49 @@ def _out_shape(t: torch.Tensor, last: int):
 
 
 def _need(t: torch.Tensor, name: str):
+    """The call's main tensor: a contiguous GPU tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
+def _arg(t, name: str, like: torch.Tensor, dtype=None, numel: int | None = None,
+         min_numel: int | None = None):
+    """Another tensor argument, checked before anything is launched: a contiguous GPU
+    tensor on the main tensor's device, of the expected dtype and element count (the kernels
+    read and write exactly that many elements)."""
+    _need(t, name)
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must have at least {min_numel} elements, got {t.numel()}")
+    return t
+
+
+def _scale_arg(S, like: torch.Tensor, batch: int):
+    return _arg(S, "S", like, torch.float32, numel=batch)
+
+
+def _bytes_arg(scales, like: torch.Tensor, n: int):
+    return _arg(scales, "scales", like, torch.uint8, numel=n)
+
+
+def _elem(x: torch.Tensor, name: str):
+    """An element tensor (bf16 or fp32) as the main argument."""
+    _need(x, name)
+    _dt(x)
+
+
 def global_scale(x: torch.Tensor) -> torch.Tensor:
     """S[b] = fp32(amax(|x[b]|) / 2688) per batch entry (2-D input: one scale)."""
-    _need(x, "x")
+    _elem(x, "x")
     batch = x.shape[0] if x.dim() == 3 else 1
     n = x.numel() // max(batch, 1)
     S = torch.empty(batch, dtype=torch.float32, device=x.device)
@@ -145,8 +179,9 @@ def global_scale(x: torch.Tensor) -> torch.Tensor:
 
 
 def scale_search_max(w: torch.Tensor, S: torch.Tensor) -> torch.Tensor:
-    _need(w, "w")
+    _elem(w, "w")
     b, r, c = _shape3(w)
+    _scale_arg(S, w, b)
     sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
     _check(lib().nvfp4_scale_search_max(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(sc), _stream()),
            "nvfp4_scale_search_max")
@@ -154,8 +189,9 @@ def scale_search_max(w: torch.Tensor, S: torch.Tensor) -> torch.Tensor:
 
 
 def scale_search_mse(w: torch.Tensor, S: torch.Tensor, return_obj: bool = False):
-    _need(w, "w")
+    _elem(w, "w")
     b, r, c = _shape3(w)
+    _scale_arg(S, w, b)
     sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
     obj = torch.empty(_out_shape(w, c // 16), dtype=torch.float32, device=w.device) if return_obj else None
     _check(lib().nvfp4_scale_search_mse(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(sc), _ptr(obj),
@@ -164,8 +200,9 @@ def scale_search_mse(w: torch.Tensor, S: torch.Tensor, return_obj: bool = False)
 
 
 def scale_search_four_over_six(w: torch.Tensor, S: torch.Tensor, return_obj: bool = False):
-    _need(w, "w")
+    _elem(w, "w")
     b, r, c = _shape3(w)
+    _scale_arg(S, w, b)
     sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
     obj = torch.empty(_out_shape(w, c // 16), dtype=torch.float32, device=w.device) if return_obj else None
     _check(lib().nvfp4_scale_search_four_over_six(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(sc),
@@ -177,8 +214,11 @@ def scale_search_four_over_six(w: torch.Tensor, S: torch.Tensor, return_obj: boo
 def ste_backward(grad: torch.Tensor, clip: float = float("inf"),
                  out: torch.Tensor | None = None) -> torch.Tensor:
     """Straight-through gradient of fake-quant: grad clamped to [-clip, clip]."""
-    _need(grad, "grad")
-    out = torch.empty_like(grad) if out is None else out
+    _elem(grad, "grad")
+    if out is None:
+        out = torch.empty_like(grad)
+    else:
+        _arg(out, "out", grad, grad.dtype, numel=grad.numel())
     _check(lib().nvfp4_ste_backward(_ptr(grad), _dt(grad), grad.numel(), float(clip), _ptr(out),
                                     _stream()), "nvfp4_ste_backward")
     return out
@@ -187,7 +227,8 @@ def ste_backward(grad: torch.Tensor, clip: float = float("inf"),
 def scale_ema(S: torch.Tensor, S_batch: torch.Tensor, momentum: float) -> torch.Tensor:
     """In place: S = momentum * S + (1 - momentum) * S_batch (fixed fp32 order)."""
     _need(S, "S")
-    _need(S_batch, "S_batch")
+    _arg(S, "S", S, torch.float32)
+    _arg(S_batch, "S_batch", S, torch.float32, numel=S.numel())
     _check(lib().nvfp4_scale_ema(_ptr(S), _ptr(S_batch), S.numel(), float(momentum), _stream()),
            "nvfp4_scale_ema")
     return S
@@ -198,9 +239,11 @@ CALIB_BINS = 32768
 
 def calib_histogram(x: torch.Tensor, hist: torch.Tensor | None = None) -> torch.Tensor:
     """Add |x| to a calibration histogram ([CALIB_BINS] int64 on x's device; new if None)."""
-    _need(x, "x")
+    _elem(x, "x")
     if hist is None:
         hist = torch.zeros(CALIB_BINS, dtype=torch.int64, device=x.device)
+    else:
+        _arg(hist, "hist", x, torch.int64, numel=CALIB_BINS)
     _check(lib().nvfp4_calib_histogram(_ptr(x), _dt(x), x.numel(), _ptr(hist), _stream()),
            "nvfp4_calib_histogram")
     return hist
@@ -208,6 +251,8 @@ def calib_histogram(x: torch.Tensor, hist: torch.Tensor | None = None) -> torch.
 
 def calib_scale(hist: torch.Tensor, fraction: float) -> torch.Tensor:
     """Tensor scale S [1] from the clip value at `fraction` of the histogram's values."""
+    _need(hist, "hist")
+    _arg(hist, "hist", hist, torch.int64, numel=CALIB_BINS)
     S = torch.empty(1, dtype=torch.float32, device=hist.device)
     _check(lib().nvfp4_calib_scale(_ptr(hist), float(fraction), _ptr(S), _stream()),
            "nvfp4_calib_scale")
@@ -218,14 +263,31 @@ def block_hessian_workspace_size(tokens: int, cols: int, groups: int = 1, n_ids:
     return int(lib().nvfp4_block_hessian_workspace_size(tokens, cols, groups, n_ids))
 
 
+def _workspace(need: int, like: torch.Tensor, workspace: torch.Tensor | None) -> torch.Tensor:
+    """The caller's workspace (checked: uint8 on the main tensor's device, large enough),
+    or a new one."""
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=like.device)
+    return _arg(workspace, "workspace", like, torch.uint8, min_numel=need)
+
+
 def block_hessian(x: torch.Tensor, group_offsets: torch.Tensor | None = None,
                   token_ids: torch.Tensor | None = None, H: torch.Tensor | None = None,
                   accumulate: bool = False, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Block-diagonal Gram matrices of x [tokens, cols]: [cols/16, 16, 16] (dense) or
     [groups, cols/16, 16, 16] (grouped by group_offsets / token_ids)."""
-    _need(x, "x")
+    _elem(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, cols]")
     tokens, cols = x.shape
-    grouped = group_offsets is not None
+    grouped = group_offsets is not None or token_ids is not None
+    if grouped:
+        if group_offsets is None or token_ids is None:
+            raise ValueError("the grouped form needs both group_offsets and token_ids")
+        _arg(group_offsets, "group_offsets", x, torch.int32)
+        _arg(token_ids, "token_ids", x, torch.int32)
+        if group_offsets.numel() < 1:
+            raise ValueError("group_offsets must have groups + 1 entries")
     groups = group_offsets.numel() - 1 if grouped else 1
     n_ids = token_ids.numel() if grouped else 0
     shape = (groups, cols // 16, 16, 16) if grouped else (cols // 16, 16, 16)
@@ -233,9 +295,10 @@ def block_hessian(x: torch.Tensor, group_offsets: torch.Tensor | None = None,
         if accumulate:
             raise ValueError("accumulate needs an existing H")
         H = torch.empty(shape, dtype=torch.float32, device=x.device)
+    else:
+        _arg(H, "H", x, torch.float32, numel=groups * (cols // 16) * 256)
     need = block_hessian_workspace_size(tokens, cols, groups, n_ids)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    workspace = _workspace(need, x, workspace)
     _check(lib().nvfp4_block_hessian(_ptr(x), _dt(x), tokens, cols, groups, _ptr(group_offsets),
                                      _ptr(token_ids), n_ids, _ptr(H), int(accumulate),
                                      _ptr(workspace), workspace.numel(), _stream()),
@@ -251,23 +314,21 @@ def debug_nonfinite() -> bool:
     return bool(flag.value)
 
 
-def _workspace(need: int, device, workspace: torch.Tensor | None) -> torch.Tensor:
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    return workspace
-
-
 def full_hessian(x: torch.Tensor, H: torch.Tensor | None = None, accumulate: bool = False,
                  workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Full Gram matrix X^T X [cols, cols] (fp32) of x [tokens, cols]."""
-    _need(x, "x")
+    _elem(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, cols]")
     tokens, cols = x.shape
     if H is None:
         if accumulate:
             raise ValueError("accumulate needs an existing H")
         H = torch.empty(cols, cols, dtype=torch.float32, device=x.device)
+    else:
+        _arg(H, "H", x, torch.float32, numel=cols * cols)
     need = int(lib().nvfp4_full_hessian_workspace_size(tokens, cols))
-    workspace = _workspace(need, x.device, workspace)
+    workspace = _workspace(need, x, workspace)
     _check(lib().nvfp4_full_hessian(_ptr(x), _dt(x), tokens, cols, _ptr(H), int(accumulate),
                                     _ptr(workspace), workspace.numel(), _stream()),
            "nvfp4_full_hessian")
@@ -279,11 +340,13 @@ def gptq_factor(H: torch.Tensor, damp: float = 0.01, workspace: torch.Tensor | N
     U^T U = (H + damp * mean(diag H) I)^-1, status [1] int32: 0 when H was positive definite
     after damping)."""
     _need(H, "H")
+    if H.dim() != 2 or H.shape[0] != H.shape[1] or H.dtype != torch.float32:
+        raise ValueError("H must be a square fp32 [cols, cols] tensor")
     cols = H.shape[0]
     U = torch.empty(cols, cols, dtype=torch.float64, device=H.device)
     status = torch.empty(1, dtype=torch.int32, device=H.device)
     need = int(lib().nvfp4_gptq_factor_workspace_size(cols))
-    workspace = _workspace(need, H.device, workspace)
+    workspace = _workspace(need, H, workspace)
     _check(lib().nvfp4_gptq_factor(_ptr(H), cols, float(damp), _ptr(U), _ptr(status),
                                    _ptr(workspace), workspace.numel(), _stream()),
            "nvfp4_gptq_factor")
@@ -293,13 +356,16 @@ def gptq_factor(H: torch.Tensor, damp: float = 0.01, workspace: torch.Tensor | N
 def gptq(w: torch.Tensor, S: torch.Tensor, scales: torch.Tensor, U: torch.Tensor,
          workspace: torch.Tensor | None = None) -> torch.Tensor:
     """GPTQ codes [rows, cols/2] of w [rows, cols] at the given block bytes, S and factor U."""
-    _need(w, "w")
-    for t, name in ((S, "S"), (scales, "scales"), (U, "U")):
-        _need(t, name)
+    _elem(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [rows, cols]")
     rows, cols = w.shape
+    _scale_arg(S, w, 1)
+    _bytes_arg(scales, w, rows * (cols // 16))
+    _arg(U, "U", w, torch.float64, numel=cols * cols)
     codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=w.device)
     need = int(lib().nvfp4_gptq_workspace_size(rows, cols))
-    workspace = _workspace(need, w.device, workspace)
+    workspace = _workspace(need, w, workspace)
     _check(lib().nvfp4_gptq(_ptr(w), _dt(w), rows, cols, _ptr(S), _ptr(scales), _ptr(U),
                             _ptr(codes), _ptr(workspace), workspace.numel(), _stream()),
            "nvfp4_gptq")
@@ -308,11 +374,10 @@ def gptq(w: torch.Tensor, S: torch.Tensor, scales: torch.Tensor, U: torch.Tensor
 
 def scale_search_local_hessian(w: torch.Tensor, S: torch.Tensor, H: torch.Tensor,
                                return_obj: bool = False):
-    _need(w, "w")
-    _need(H, "H")
+    _elem(w, "w")
     b, r, c = _shape3(w)
-    if H.numel() != b * (c // 16) * 256 or H.dtype != torch.float32:
-        raise ValueError("H must be fp32 [batch, cols/16, 16, 16]")
+    _scale_arg(S, w, b)
+    _arg(H, "H", w, torch.float32, numel=b * (c // 16) * 256)
     sc = torch.empty(_out_shape(w, c // 16), dtype=torch.uint8, device=w.device)
     obj = torch.empty(_out_shape(w, c // 16), dtype=torch.float64, device=w.device) if return_obj else None
     _check(lib().nvfp4_scale_search_local_hessian(_ptr(w), _dt(w), b, r, c, _ptr(S), _ptr(H),
@@ -323,8 +388,11 @@ def scale_search_local_hessian(w: torch.Tensor, S: torch.Tensor, H: torch.Tensor
 
 def quantize(x: torch.Tensor, S: torch.Tensor, scales: torch.Tensor | None = None):
     """Returns (codes, scales): packed E2M1 codes and the block bytes used."""
-    _need(x, "x")
+    _elem(x, "x")
     b, r, c = _shape3(x)
+    _scale_arg(S, x, b)
+    if scales is not None:
+        _bytes_arg(scales, x, b * r * (c // 16))
     codes = torch.empty(_out_shape(x, c // 2), dtype=torch.uint8, device=x.device)
     so = None
     if scales is None:
@@ -337,9 +405,15 @@ def quantize(x: torch.Tensor, S: torch.Tensor, scales: torch.Tensor | None = Non
 def dequantize(codes: torch.Tensor, scales: torch.Tensor, S: torch.Tensor,
                out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     _need(codes, "codes")
-    shape = _out_shape(codes, codes.shape[-1] * 2)
-    y = torch.empty(shape, dtype=out_dtype, device=codes.device)
-    b, r, c = _shape3(y)
+    if codes.dtype != torch.uint8 or codes.dim() not in (2, 3):
+        raise ValueError("codes must be uint8 [rows, cols/2] or [batch, rows, cols/2]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported dtype {out_dtype} (bf16 or fp32)")
+    b, r, half = _shape3(codes)
+    c = 2 * half
+    _bytes_arg(scales, codes, b * r * (c // 16))
+    _scale_arg(S, codes, b)
+    y = torch.empty(_out_shape(codes, c), dtype=out_dtype, device=codes.device)
     _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(S), b, r, c, _ptr(y), _dt(y),
                                   _stream()), "nvfp4_dequantize")
     return y
@@ -348,9 +422,15 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, S: torch.Tensor,
 def fakequant(x: torch.Tensor, S: torch.Tensor, scales: torch.Tensor | None = None,
               return_codes: bool = False, out: torch.Tensor | None = None):
     """Quantise -> dequantise in one pass. Returns y (and codes, scales if asked)."""
-    _need(x, "x")
+    _elem(x, "x")
     b, r, c = _shape3(x)
-    y = torch.empty_like(x) if out is None else out
+    _scale_arg(S, x, b)
+    if scales is not None:
+        _bytes_arg(scales, x, b * r * (c // 16))
+    if out is None:
+        y = torch.empty_like(x)
+    else:
+        y = _arg(out, "out", x, x.dtype, numel=x.numel())
     codes = so = None
     if return_codes:
         codes = torch.empty(_out_shape(x, c // 2), dtype=torch.uint8, device=x.device)
@@ -366,6 +446,8 @@ def fakequant(x: torch.Tensor, S: torch.Tensor, scales: torch.Tensor | None = No
 def route_groups(expert_ids: torch.Tensor, experts: int):
     """Per-expert token lists from a [tokens, topk] routing table: (offsets, token_ids)."""
     _need(expert_ids, "expert_ids")
+    if expert_ids.dtype != torch.int32 or expert_ids.dim() != 2:
+        raise ValueError("expert_ids must be int32 [tokens, topk]")
     tokens, topk = expert_ids.shape
     offsets = torch.empty(experts + 1, dtype=torch.int32, device=expert_ids.device)
     tok = torch.empty(tokens * topk, dtype=torch.int32, device=expert_ids.device)

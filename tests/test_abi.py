@@ -157,3 +157,81 @@ def test_binding_refuses_cpu_tensors():
         nvfp4.fakequant(torch.zeros(4, 16), torch.ones(1))
     with pytest.raises(TypeError):
         nvfp4._dt(torch.zeros(1, dtype=torch.float16))
+
+
+# ---------------------------------------------------------------- binding argument checks
+# The binding checks every tensor argument before the library is called. On this CPU-only
+# host the tensors below are CPU tensors dressed up as GPU tensors (only their metadata is
+# read); the library loader is replaced so that any call through it fails the test.
+
+import torch  # noqa: E402
+
+
+class _OnGpu(torch.Tensor):
+    """A CPU tensor that reports itself as living on cuda:<index> (metadata only)."""
+    index = 0
+
+    @property
+    def is_cuda(self):
+        return True
+
+    @property
+    def device(self):
+        return torch.device("cuda", type(self).index)
+
+
+class _OnGpu1(_OnGpu):
+    index = 1
+
+
+def G(*shape, dtype=torch.float32, cls=_OnGpu):
+    return torch.zeros(*shape, dtype=dtype).as_subclass(cls)
+
+
+@pytest.fixture
+def no_launch(monkeypatch):
+    def boom():
+        raise AssertionError("the library was called before the arguments were checked")
+    monkeypatch.setattr(nvfp4, "lib", boom)
+
+
+def _bad_cases():
+    x = G(8, 32)                      # fp32 [8, 32]: 16 blocks
+    xb = G(8, 32, dtype=torch.bfloat16)
+    w3 = G(3, 8, 32)                  # batch 3
+    S1 = G(1)
+    return [
+        ("S on the host", lambda: nvfp4.fakequant(x, torch.ones(1)), ValueError),
+        ("S on another GPU", lambda: nvfp4.fakequant(x, G(1, cls=_OnGpu1)), ValueError),
+        ("S fp64", lambda: nvfp4.fakequant(x, G(1, dtype=torch.float64)), TypeError),
+        ("S with fewer entries than the batch", lambda: nvfp4.scale_search_mse(w3, S1), ValueError),
+        ("S with more entries", lambda: nvfp4.quantize(x, G(2)), ValueError),
+        ("scales too small", lambda: nvfp4.quantize(x, S1, G(15, dtype=torch.uint8)), ValueError),
+        ("scales not uint8", lambda: nvfp4.fakequant(x, S1, G(16, dtype=torch.int32)), TypeError),
+        ("out bf16 for an fp32 input", lambda: nvfp4.fakequant(x, S1, out=G(8, 32, dtype=torch.bfloat16)), TypeError),
+        ("out too small", lambda: nvfp4.fakequant(xb, S1, out=G(8, 16, dtype=torch.bfloat16)), ValueError),
+        ("out not contiguous", lambda: nvfp4.fakequant(x, S1, out=G(32, 8).t()), ValueError),
+        ("dequantize with a short S", lambda: nvfp4.dequantize(G(3, 8, 16, dtype=torch.uint8), G(3 * 16, dtype=torch.uint8), S1), ValueError),
+        ("dequantize scales too small", lambda: nvfp4.dequantize(G(8, 16, dtype=torch.uint8), G(8, dtype=torch.uint8), S1), ValueError),
+        ("Local-Hessian H too small", lambda: nvfp4.scale_search_local_hessian(x, S1, G(1, 16, 16)), ValueError),
+        ("Local-Hessian H fp64", lambda: nvfp4.scale_search_local_hessian(x, S1, G(2, 16, 16, dtype=torch.float64)), TypeError),
+        ("GPTQ U fp32", lambda: nvfp4.gptq(x, S1, G(16, dtype=torch.uint8), G(32, 32)), TypeError),
+        ("GPTQ U too small", lambda: nvfp4.gptq(x, S1, G(16, dtype=torch.uint8), G(16, 32, dtype=torch.float64)), ValueError),
+        ("GPTQ S with two entries", lambda: nvfp4.gptq(x, G(2), G(16, dtype=torch.uint8), G(32, 32, dtype=torch.float64)), ValueError),
+        ("GPTQ factor of a non-square H", lambda: nvfp4.gptq_factor(G(32, 16)), ValueError),
+        ("histogram int32", lambda: nvfp4.calib_histogram(x, G(nvfp4.CALIB_BINS, dtype=torch.int32)), TypeError),
+        ("histogram too short", lambda: nvfp4.calib_scale(G(100, dtype=torch.int64), 0.5), ValueError),
+        ("block Hessian H too small", lambda: nvfp4.block_hessian(x, H=G(1, 16, 16)), ValueError),
+        ("block Hessian ids without offsets", lambda: nvfp4.block_hessian(x, token_ids=G(4, dtype=torch.int32)), ValueError),
+        ("block Hessian offsets int64", lambda: nvfp4.block_hessian(x, G(3, dtype=torch.int64), G(4, dtype=torch.int32)), TypeError),
+        ("full Hessian H too small", lambda: nvfp4.full_hessian(x, H=G(32, 16)), ValueError),
+        ("STE out of another dtype", lambda: nvfp4.ste_backward(xb, 1.0, out=G(8, 32)), TypeError),
+        ("scale EMA with a short batch scale", lambda: nvfp4.scale_ema(G(3), G(2), 0.9), ValueError),
+        ("routing ids int64", lambda: nvfp4.route_groups(G(4, 2, dtype=torch.int64), 8), ValueError),
+    ]
+
+
+@pytest.mark.parametrize("what,call,exc", _bad_cases(), ids=[c[0] for c in _bad_cases()])
+def test_binding_rejects_bad_tensor_arguments(no_launch, what, call, exc):
+    with pytest.raises(exc):
+        call()

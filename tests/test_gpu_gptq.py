@@ -122,8 +122,8 @@ def test_full_hessian_accumulate_and_empty(orc):
     nvfp4.full_hessian(xs[1].to(DEV), H=H, accumulate=True)
     ref = orc.full_hessian(np.concatenate([f32(x) for x in xs]))
     assert block_rel_frob(H.cpu().numpy(), ref) <= 1e-4
-    e = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
-    assert not nvfp4.full_hessian(e).cpu().numpy().any()
+    assert not nvfp4.full_hessian(torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)).cpu().numpy().any()
+    e = torch.empty(0, 256, dtype=torch.bfloat16, device=DEV)
     H2 = H.clone()
     nvfp4.full_hessian(e, H=H2, accumulate=True)
     assert torch.equal(H2, H)

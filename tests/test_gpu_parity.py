@@ -132,6 +132,38 @@ def test_quantize_with_given_scales_all_bytes(orc, dtype):
     assert_bits(y, dq, orc)
 
 
+def test_given_bytes_outside_the_candidates(orc):
+    """Every byte value as a given block scale: a byte acts as its E4M3FN magnitude (sign
+    bit ignored), and 0x7F (NaN) codes its block as zeros like 0x00; quantise, fake-quant,
+    dequantise and GPTQ agree with the oracle on all 256 values."""
+    case("given block bytes 0x00..0xFF: quantize, fakequant, dequantize, gptq")
+    rng = np.random.default_rng(11)
+    rows, cols = 256, 64
+    S = np.float32(3.0e-3)
+    sc = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // 16, axis=1)
+    mag = np.array([orc.e4m3_value(b & 0x7F) if (b & 0x7F) not in (0, 0x7F) else 1.0
+                    for b in range(256)], np.float64)[:, None]
+    x = (rng.uniform(-7, 7, (rows, cols)) * mag * float(S)).astype(np.float32)
+    x[0x80:] = x[:0x80]  # bytes b and b | 0x80 see the same values
+    xd, Sd, scd = torch.from_numpy(x).to(DEV), dev_S(S), torch.from_numpy(sc).to(DEV)
+    codes, _ = nvfp4.quantize(xd, Sd, scd)
+    want = orc.quantize(x, S, sc)
+    assert np.array_equal(codes.cpu().numpy(), want)
+    # bytes b and b | 0x80 give the same codes; 0x00, 0x7F, 0x80 and 0xFF give zeros
+    assert np.array_equal(want[0x01:0x7F], want[0x81:0xFF])
+    assert not want[[0x00, 0x7F, 0x80, 0xFF]].any()
+    y = nvfp4.fakequant(xd, Sd, scd)
+    dq, _, _ = orc.fakequant(x, S, sc)
+    assert_bits(y, dq, orc)
+    yd = nvfp4.dequantize(torch.from_numpy(want).to(DEV), scd, Sd)
+    assert_bits(yd, orc.dequantize(want, sc, S, rows, cols), orc)
+    # GPTQ at the same bytes (U of a random well-conditioned H from the oracle)
+    a = rng.standard_normal((4 * cols, cols))
+    U = orc.gptq_factor(a.T @ a, 0.01)
+    g = nvfp4.gptq(xd, Sd, scd, torch.from_numpy(U).to(DEV)).cpu().numpy()
+    assert np.array_equal(g, orc.gptq(x, S, sc, U=U))
+
+
 def test_exact_ties_and_edges(orc):
     case("ties on midpoints, zero blocks, -0, saturation, denormal inputs")
     blocks = []

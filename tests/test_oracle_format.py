@@ -286,3 +286,25 @@ def test_zero_block_gets_zero_byte_and_positive_zero(orc):
     dq, codes, sc = orc.fakequant(x, 1.0)
     assert np.all(sc == 0) and np.all(codes == 0)
     assert not np.any(np.signbit(dq))
+
+
+def test_given_byte_reads_the_e4m3_magnitude(orc):
+    """A given block byte acts as its E4M3FN magnitude: torch's float8_e4m3fn decode of
+    b | 0x80 is the negative of b's value, and the oracle codes and dequantises with |value|;
+    0x7F and 0xFF decode to NaN there and, like 0x00 and 0x80 (zero), code a block as zeros."""
+    import torch
+    rng = np.random.default_rng(3)
+    S = np.float32(0.01)
+    dec = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    for b in range(1, 0x7F):
+        assert dec[b | 0x80] == -dec[b] == -orc.e4m3_value(b)
+        x = (rng.uniform(-7, 7, 16) * dec[b] * S).astype(np.float32)
+        for v in x:
+            c = orc.e2m1_code(float(v), b, S)
+            assert orc.e2m1_code(float(v), b | 0x80, S) == c
+            assert orc.dequant_value(c, b | 0x80, S) == orc.dequant_value(c, b, S)
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF]) and dec[0x80] == 0
+    for b in (0x00, 0x7F, 0x80, 0xFF):
+        for v in (0.0, 1e-3, -2.0, 5.0):
+            assert orc.e2m1_code(v, b, S) == 0
+            assert orc.dequant_value(0x7, b, S) == 0.0
