@@ -174,6 +174,24 @@ NVFP4_API int nvfp4_block_hessian(const void *x, int dtype, int64_t tokens, int6
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Allocation-free form of nvfp4_block_hessian, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight calibration or serving loops, harnesses that
+ * forbid hipMalloc). Arguments, checks and results are those of nvfp4_block_hessian without
+ * the workspace: the scratch comes from a static device array of NVFP4_STATIC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends. A call whose
+ * nvfp4_block_hessian_workspace_size() exceeds that returns NVFP4_ERR_WORKSPACE before any
+ * launch. All calls on a device share the array (it keeps the last call's contents, which
+ * no call reads): calls that overlap on one device, e.g. on two streams, race and must be
+ * ordered by the caller. Nothing is allocated or freed; NVFP4_ERR_HIP if the array's device
+ * address cannot be obtained.
+ */
+#define NVFP4_STATIC_SCRATCH_BYTES (64u << 20)
+NVFP4_API int nvfp4_block_hessian_noalloc(const void *x, int dtype, int64_t tokens, int64_t cols,
+                                          int64_t groups, const int32_t *group_offsets,
+                                          const int32_t *token_ids, int64_t n_ids, float *H,
+                                          int accumulate, void *stream);
+
+/*
  * Local-Hessian scale search ([LH] "Change the objective"): for every (row, block) of
  * every batch entry, all 126 positive E4M3 bytes are tried and the first with the
  * smallest d H_b d^T wins, with d_i = fp32(dq_i(c) - w_i) and H_b the block's 16x16

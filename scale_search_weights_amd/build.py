@@ -17,7 +17,8 @@ OUT = os.path.join(PKG, "libnvfp4.so")
 PROBE_OUT = os.path.join(PKG, "libnvfp4_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["nvfp4_api.hip", "nvfp4_quant.hip", "nvfp4_search.hip", "nvfp4_hessian.hip",
-           "nvfp4_calib.hip", "nvfp4_ste.hip", "nvfp4_gram.hip", "nvfp4_gptq.hip", "nvfp4_debug.hip"]
+           "nvfp4_calib.hip", "nvfp4_ste.hip", "nvfp4_gram.hip", "nvfp4_gptq.hip", "nvfp4_debug.hip",
+           "nvfp4_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -36,6 +36,45 @@ hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
 
+namespace nvfp4 {
+
+// Host checks shared by the block-Hessian entry points (all but the workspace): *empty is
+// set when there is nothing to launch.
+int check_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t groups,
+                        const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
+                        const float *H, bool *empty) {
+  *empty = false;
+  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+  if (tokens < 0 || cols < 0 || (cols % 16) != 0 || groups < 0 || n_ids < 0)
+    return NVFP4_ERR_SHAPE;
+  int64_t t1, t2;
+  if (!mul_ok(tokens, cols, &t1) || !mul_ok(t1, 4, &t2)) return NVFP4_ERR_SHAPE;
+  if (groups > kMaxGridY || n_ids > INT32_MAX || tokens > INT32_MAX) return NVFP4_ERR_SHAPE;
+  const bool grouped = group_offsets != nullptr || token_ids != nullptr;
+  if (grouped && (!group_offsets || !token_ids)) return NVFP4_ERR_NULL;
+  if (!grouped && groups != 1) return NVFP4_ERR_ARG;
+  if (cols == 0 || groups == 0) {
+    *empty = true;
+    return NVFP4_OK;
+  }
+  if (!H || (tokens > 0 && !x)) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(H, 4) || !aligned(group_offsets, 4) || !aligned(token_ids, 4))
+    return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+int run_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t groups,
+                      const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
+                      float *H, int accumulate, void *workspace, void *stream) {
+  const bool grouped = group_offsets != nullptr;
+  debug_check_finite(x, dtype, tokens * cols, as_stream(stream));
+  return launch_block_hessian(x, dtype, tokens, cols, groups, grouped ? group_offsets : nullptr,
+                              grouped ? token_ids : nullptr, n_ids, H, accumulate, workspace,
+                              as_stream(stream));
+}
+
+}  // namespace nvfp4
+
 extern "C" {
 
 const char *nvfp4_status_string(int status) {
@@ -159,26 +198,15 @@ int nvfp4_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, 
                         const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
                         float *H, int accumulate, void *workspace, size_t workspace_bytes,
                         void *stream) {
-  if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
-  if (tokens < 0 || cols < 0 || (cols % 16) != 0 || groups < 0 || n_ids < 0)
-    return NVFP4_ERR_SHAPE;
-  int64_t t1, t2;
-  if (!mul_ok(tokens, cols, &t1) || !mul_ok(t1, 4, &t2)) return NVFP4_ERR_SHAPE;
-  if (groups > kMaxGridY || n_ids > INT32_MAX || tokens > INT32_MAX) return NVFP4_ERR_SHAPE;
-  const bool grouped = group_offsets != nullptr || token_ids != nullptr;
-  if (grouped && (!group_offsets || !token_ids)) return NVFP4_ERR_NULL;
-  if (!grouped && groups != 1) return NVFP4_ERR_ARG;
-  if (cols == 0 || groups == 0) return NVFP4_OK;
-  if (!H || (tokens > 0 && !x)) return NVFP4_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(H, 4) || !aligned(group_offsets, 4) || !aligned(token_ids, 4))
-    return NVFP4_ERR_ALIGN;
+  bool empty = false;
+  const int rc = check_block_hessian(x, dtype, tokens, cols, groups, group_offsets, token_ids,
+                                     n_ids, H, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
   const size_t need = nvfp4_block_hessian_workspace_size(tokens, cols, groups, n_ids);
   if (!workspace || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
-  debug_check_finite(x, dtype, tokens * cols, as_stream(stream));
-  return launch_block_hessian(x, dtype, tokens, cols, groups, grouped ? group_offsets : nullptr,
-                              grouped ? token_ids : nullptr, n_ids, H, accumulate, workspace,
-                              as_stream(stream));
+  return run_block_hessian(x, dtype, tokens, cols, groups, group_offsets, token_ids, n_ids, H,
+                           accumulate, workspace, stream);
 }
 
 int nvfp4_scale_search_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows,

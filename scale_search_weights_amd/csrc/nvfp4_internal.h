@@ -36,6 +36,13 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
                          const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
                          float *H, int accumulate, void *workspace, hipStream_t st);
 
+int check_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t groups,
+                        const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
+                        const float *H, bool *empty);
+int run_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, int64_t groups,
+                      const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
+                      float *H, int accumulate, void *workspace, void *stream);
+
 bool debug_checks_enabled();
 void debug_check_finite(const void *x, int dtype, int64_t n, hipStream_t st);
 void debug_check_scale(const float *S, int64_t n, hipStream_t st);

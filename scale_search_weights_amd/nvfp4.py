@@ -23,6 +23,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "nvfp4.h")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+STATIC_SCRATCH_BYTES = 64 << 20  # NVFP4_STATIC_SCRATCH_BYTES: nvfp4_block_hessian_noalloc's scratch
 
 _lib = None
 
@@ -44,6 +45,7 @@ _SIGS = {
     "nvfp4_calib_scale": (_I, [_P, ctypes.c_double, _P, _P]),
     "nvfp4_block_hessian_workspace_size": (_SZ, [_I64, _I64, _I64, _I64]),
     "nvfp4_block_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P, _SZ, _P]),
+    "nvfp4_block_hessian_noalloc": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _I64, _P, _I, _P]),
     "nvfp4_scale_search_local_hessian": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_quantize": (_I, [_P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "nvfp4_dequantize": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),

@@ -18,7 +18,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = nvfp4.declared_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     for n in names:
         assert hasattr(L, n), n
     assert L.nvfp4_version() == 100
@@ -139,6 +139,24 @@ def test_block_hessian_workspace_and_group_checks(L):
     a = L.nvfp4_block_hessian_workspace_size(1000, 512, 8, 100)
     b = L.nvfp4_block_hessian_workspace_size(1000, 512, 8, 1000000)
     assert b > a
+
+
+def test_block_hessian_noalloc_checks(L):
+    """The allocation-free form validates like the workspace form and refuses calls whose
+    workspace would exceed its static scratch, all before touching the device."""
+    f = L.nvfp4_block_hessian_noalloc
+    assert f(P(FAKE), 1, 4096, 500, 1, None, None, 0, P(FAKE), 0, None) == ESHAPE
+    assert f(P(FAKE), 7, 4096, 512, 1, None, None, 0, P(FAKE), 0, None) == EDTYPE
+    assert f(P(FAKE), 1, 4096, 512, 2, None, None, 0, P(FAKE), 0, None) == EARG
+    assert f(P(FAKE), 1, 4096, 512, 1, None, None, 0, None, 0, None) == ENULL
+    assert f(P(FAKE + 2), 1, 4096, 512, 1, None, None, 0, P(FAKE), 0, None) == EALIGN
+    assert f(None, 1, 4096, 0, 1, None, None, 0, None, 0, None) == OK
+    big_t, big_c = 1 << 20, 16384
+    assert L.nvfp4_block_hessian_workspace_size(big_t, big_c, 1, 0) > nvfp4.STATIC_SCRATCH_BYTES
+    assert f(P(FAKE), 1, big_t, big_c, 1, None, None, 0, P(FAKE), 0, None) == EWS
+    # the two projection-sized and MoE-sized calibration calls fit
+    assert L.nvfp4_block_hessian_workspace_size(131072, 4096, 1, 0) <= nvfp4.STATIC_SCRATCH_BYTES
+    assert L.nvfp4_block_hessian_workspace_size(65536, 2048, 128, 524288) <= nvfp4.STATIC_SCRATCH_BYTES
 
 
 def test_route_groups_checks(L):
