@@ -304,6 +304,43 @@ NVFP4_API int nvfp4_gptq(const void *w, int dtype, int64_t rows, int64_t cols, c
  */
 NVFP4_API int nvfp4_debug_nonfinite(int32_t *flag_out, void *stream);
 
+/*
+ * Search statistics (diagnostics; not part of the method). While switched on with
+ * nvfp4_search_stats_enable(1), the MSE and Local-Hessian searches (and the MSE fallback of
+ * Local-Hessian blocks whose H_b is zero) add to process-wide device counters the work they
+ * do and the path each (row, block) takes; nvfp4_search_stats_enable(0) switches counting
+ * off (the default: counting adds atomics to the searches). nvfp4_search_stats_read
+ * synchronises `stream`, copies the NVFP4_STATS_N counters to out[] (host memory) and
+ * clears them. Counters are shared by every caller in the process; concurrent searches add
+ * to the same totals. Indices:
+ *  NVFP4_STAT_MSE_BLOCKS     non-zero blocks searched by the MSE search
+ *  NVFP4_STAT_MSE_EVALS      MSE candidate objectives evaluated (of 126 per block)
+ *  NVFP4_STAT_LH_PAIRS       (row, block) pairs with a non-zero block and H_b searched
+ *  NVFP4_STAT_LH_ZERO_H      non-zero blocks whose H_b is zero (the MSE choice)
+ *  NVFP4_STAT_LH_REL         pairs screened with the error bound relative to the objective
+ *  NVFP4_STAT_LH_ABS         pairs screened with the absolute error bound
+ *  NVFP4_STAT_LH_NOPRUNE     pairs whose H_b rules out the pruning below the max byte
+ *  NVFP4_STAT_LH_RESCAN      pairs rescanned exactly (three or more screen survivors, or
+ *                            values outside the screen's range)
+ *  NVFP4_STAT_LH_TWO         pairs with two screen survivors (two exact evaluations)
+ *  NVFP4_STAT_LH_SCREENED    (pair, candidate) objectives evaluated on the fp32 screen
+ *  NVFP4_STAT_LH_EXACT       (pair, candidate) objectives evaluated exactly in fp64
+ */
+#define NVFP4_STATS_N 16
+#define NVFP4_STAT_MSE_BLOCKS 0
+#define NVFP4_STAT_MSE_EVALS 1
+#define NVFP4_STAT_LH_PAIRS 2
+#define NVFP4_STAT_LH_ZERO_H 3
+#define NVFP4_STAT_LH_REL 4
+#define NVFP4_STAT_LH_ABS 5
+#define NVFP4_STAT_LH_NOPRUNE 6
+#define NVFP4_STAT_LH_RESCAN 7
+#define NVFP4_STAT_LH_TWO 8
+#define NVFP4_STAT_LH_SCREENED 9
+#define NVFP4_STAT_LH_EXACT 10
+NVFP4_API int nvfp4_search_stats_enable(int on);
+NVFP4_API int nvfp4_search_stats_read(int64_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

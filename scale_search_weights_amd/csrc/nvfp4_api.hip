@@ -288,6 +288,16 @@ int nvfp4_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk, 
                              as_stream(stream));
 }
 
+int nvfp4_search_stats_enable(int on) {
+  search_stats_enable(on != 0);
+  return NVFP4_OK;
+}
+
+int nvfp4_search_stats_read(int64_t *out, void *stream) {
+  if (!out) return NVFP4_ERR_NULL;
+  return search_stats_read(out, as_stream(stream));
+}
+
 int nvfp4_debug_nonfinite(int32_t *flag_out, void *stream) {
   if (!flag_out) return NVFP4_ERR_NULL;
   if (!debug_checks_enabled()) return NVFP4_ERR_ARG;

@@ -43,6 +43,9 @@ int run_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, in
                       const int32_t *group_offsets, const int32_t *token_ids, int64_t n_ids,
                       float *H, int accumulate, void *workspace, void *stream);
 
+void search_stats_enable(bool on);
+int search_stats_read(int64_t *out, hipStream_t st);
+
 bool debug_checks_enabled();
 void debug_check_finite(const void *x, int dtype, int64_t n, hipStream_t st);
 void debug_check_scale(const float *S, int64_t n, hipStream_t st);

@@ -15,6 +15,20 @@
 
 namespace nvfp4 {
 
+// ------------------------------------------------------------------ search statistics
+//
+// Process-wide device counters of the work the searches do (NVFP4_STAT_* indices), filled
+// only by the STATS instantiations, which the launchers pick while counting is switched on.
+__device__ unsigned long long g_search_stats[NVFP4_STATS_N];
+static bool g_stats_on = false;
+
+// sum of v over the wave, added to counter i by lane 0
+__device__ __forceinline__ void stat_add(int i, unsigned v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += (unsigned)__shfl_xor((int)v, off, 64);
+  if ((threadIdx.x & 63) == 0 && v) atomicAdd(&g_search_stats[i], (unsigned long long)v);
+}
+
 template <int DT>
 __device__ __forceinline__ void load16(const void *__restrict__ x, int64_t blk, float v[16]) {
   if (DT == NVFP4_DTYPE_BF16) {
@@ -110,7 +124,7 @@ __device__ __forceinline__ bool fast_path_ok(float amax, const Cand *cand) {
 
 // Pruned MSE search over |x| (see above); amax > 0.
 __device__ __forceinline__ void mse_pruned(const float X[16], float amax, const Cand *cand,
-                                           float S, int &best_c, float &best) {
+                                           float S, int &best_c, float &best, unsigned &n_eval) {
   int cz, cb;
   window_bounds(amax, cand, S, cz, cb);
   const int c_hi = cz <= 126 ? cz : 126;
@@ -134,6 +148,7 @@ __device__ __forceinline__ void mse_pruned(const float X[16], float amax, const 
       if (lb > best) break;
     }
     const float o = mse_candidate(X, c, cand[c], S, fast_ok);
+    ++n_eval;
     if (o < best) {
       best = o;
       best_c = c;
@@ -143,6 +158,7 @@ __device__ __forceinline__ void mse_pruned(const float X[16], float amax, const 
     const float e7 = (6.0f * cand[c].s) * S - amax;
     if (e7 * e7 > best) break;  // LB(c) > best, and LB only grows below
     const float o = mse_candidate(X, c, cand[c], S, fast_ok);
+    ++n_eval;
     if (o <= best) {  // ties: the smaller byte wins
       best = o;
       best_c = c;
@@ -150,7 +166,7 @@ __device__ __forceinline__ void mse_pruned(const float X[16], float amax, const 
   }
 }
 
-template <int DT>
+template <int DT, bool STATS>
 __global__ void __launch_bounds__(256)
     k_mse(const void *__restrict__ w, const float *__restrict__ S_arr, uint8_t *__restrict__ scales,
           float *__restrict__ obj, int64_t blocks_per_batch) {
@@ -164,28 +180,39 @@ __global__ void __launch_bounds__(256)
   load16<DT>(w, blk, v);  // in flight while the table is built
   build_cands(cand, S);
   lds_barrier();
-  if (!active) return;
+  if (!STATS && !active) return;
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     X[i] = fabsf(v[i]);
     amax = fmaxf(amax, X[i]);
   }
+  if (!active) amax = 0.0f;  // (STATS: every lane reaches the wave sums below)
   int best_c = 0;
   float best = 0.0f;
-  if (amax != 0.0f) mse_pruned(X, amax, cand, S, best_c, best);
-  scales[blk] = (uint8_t)best_c;
-  if (obj) obj[blk] = best;
+  unsigned n_eval = 0;
+  if (amax != 0.0f) mse_pruned(X, amax, cand, S, best_c, best, n_eval);
+  if (active) {
+    scales[blk] = (uint8_t)best_c;
+    if (obj) obj[blk] = best;
+  }
+  if (STATS) {
+    stat_add(NVFP4_STAT_MSE_BLOCKS, amax != 0.0f ? 1u : 0u);
+    stat_add(NVFP4_STAT_MSE_EVALS, n_eval);
+  }
 }
 
 int launch_mse(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
                const float *S, uint8_t *scales, float *obj, hipStream_t st) {
   const int64_t bpb = rows * (cols / 16);
   const dim3 g((unsigned)((bpb + 255) / 256), (unsigned)batch), b(256);
-  if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_mse<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, scales, obj, bpb);
-  else
-    hipLaunchKernelGGL(k_mse<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, scales, obj, bpb);
+  if (dtype == NVFP4_DTYPE_BF16) {
+    if (g_stats_on) hipLaunchKernelGGL((k_mse<NVFP4_DTYPE_BF16, true>), g, b, 0, st, w, S, scales, obj, bpb);
+    else hipLaunchKernelGGL((k_mse<NVFP4_DTYPE_BF16, false>), g, b, 0, st, w, S, scales, obj, bpb);
+  } else {
+    if (g_stats_on) hipLaunchKernelGGL((k_mse<NVFP4_DTYPE_F32, true>), g, b, 0, st, w, S, scales, obj, bpb);
+    else hipLaunchKernelGGL((k_mse<NVFP4_DTYPE_F32, false>), g, b, 0, st, w, S, scales, obj, bpb);
+  }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
@@ -416,7 +443,7 @@ __device__ __forceinline__ void screen_merge(Screen &z) {
   z = r;
 }
 
-template <int DT>
+template <int DT, bool STATS>
 __global__ void __launch_bounds__(256)
     k_lh_mfma(const void *__restrict__ w, const float *__restrict__ S_arr,
               const float *__restrict__ H, uint8_t *__restrict__ scales, double *__restrict__ obj,
@@ -471,6 +498,7 @@ __global__ void __launch_bounds__(256)
 
   if (!h_nonzero) {  // every candidate has objective 0: the MSE choice, one lane per row
     const int64_t row_end = min(tile1 * 64, rows);
+    unsigned n_zero = 0, n_eval = 0;
     for (int64_t row = tile0 * 64 + threadIdx.x; row < row_end; row += blockDim.x) {
       {
         const int64_t blk = (batch * rows + row) * nb + b;
@@ -484,10 +512,15 @@ __global__ void __launch_bounds__(256)
         }
         int bc = 0;
         float bm = 0.0f;
-        if (amax != 0.0f) mse_pruned(X, amax, cand, S, bc, bm);
+        if (amax != 0.0f) mse_pruned(X, amax, cand, S, bc, bm, n_eval);
+        n_zero += amax != 0.0f ? 1u : 0u;
         scales[blk] = (uint8_t)bc;
         if (obj) obj[blk] = 0.0;
       }
+    }
+    if (STATS) {
+      stat_add(NVFP4_STAT_LH_ZERO_H, n_zero);
+      stat_add(NVFP4_STAT_MSE_EVALS, n_eval);
     }
     return;
   }
@@ -499,6 +532,10 @@ __global__ void __launch_bounds__(256)
     ha[t] = (float)hb[p * 16 + 4 * q + t];
     ab[t] = aw[4 * q + t];
   }
+  // statistics (STATS only): pair-path counts kept by lane group 0 of each pair, screened
+  // candidates by the lane group that scores them
+  unsigned st_pairs = 0, st_rel = 0, st_abs = 0, st_noprune = 0, st_rescan = 0, st_two = 0;
+  unsigned st_screened = 0, st_exact = 0;
   for (int64_t tile = tile0; tile < tile1; ++tile) {
   const int64_t row = tile * 64 + (threadIdx.x >> 6) * 16 + p;
   const bool valid = row < rows;
@@ -587,6 +624,7 @@ __global__ void __launch_bounds__(256)
     const int cq = q == 0 ? cs[0] : (q == 1 ? cs[1] : (q == 2 ? cs[2] : cs[3]));
     const bool aq = q == 0 ? acts[0] : (q == 1 ? acts[1] : (q == 2 ? acts[2] : acts[3]));
     if (aq) screen_add(z, o - er, o + er, cq);
+    if (STATS) st_screened += aq ? 1u : 0u;
   };
   for (int j = 0;; j += 4) {
     int cs[4];
@@ -669,6 +707,7 @@ __global__ void __launch_bounds__(256)
       float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (act) lh_delta4(v, c, cand[c], S, fast_ok, d);
       const double o = lh_exact_split(d, q, hb);
+      if (STATS && q == 0) st_exact += act ? 1u : 0u;
       if (act && o < bo) {
         bo = o;
         bcx = c;
@@ -686,6 +725,7 @@ __global__ void __launch_bounds__(256)
       float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (act) lh_delta4(v, c, cand[c], S, fast_ok, d);
       const double o = lh_exact_split(d, q, hb);
+      if (STATS && q == 0) st_exact += act ? 1u : 0u;
       if (act && o <= bo) {
         bo = o;
         bcx = c;
@@ -700,7 +740,26 @@ __global__ void __launch_bounds__(256)
     scales[blk] = (uint8_t)best_c;
     if (obj) obj[blk] = best_c ? best_o : 0.0;
   }
+  if (STATS && q == 0 && live) {
+    st_pairs += 1;
+    st_rel += (screen && rel) ? 1u : 0u;
+    st_abs += (screen && !rel) ? 1u : 0u;
+    st_noprune += prune ? 0u : 1u;
+    st_rescan += slow ? 1u : 0u;
+    st_two += two ? 1u : 0u;
+    st_exact += (need ? 1u : 0u) + (two ? 1u : 0u);
+  }
   }  // tiles
+  if (STATS) {
+    stat_add(NVFP4_STAT_LH_PAIRS, st_pairs);
+    stat_add(NVFP4_STAT_LH_REL, st_rel);
+    stat_add(NVFP4_STAT_LH_ABS, st_abs);
+    stat_add(NVFP4_STAT_LH_NOPRUNE, st_noprune);
+    stat_add(NVFP4_STAT_LH_RESCAN, st_rescan);
+    stat_add(NVFP4_STAT_LH_TWO, st_two);
+    stat_add(NVFP4_STAT_LH_SCREENED, st_screened);
+    stat_add(NVFP4_STAT_LH_EXACT, st_exact);
+  }
 }
 
 constexpr int64_t LH_TILES = 8;
@@ -716,13 +775,33 @@ int launch_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows, 
   int64_t tpw = LH_TILES;
   while (tpw > 1 && cols_batch * ((n_tiles + tpw - 1) / tpw) < 8192) tpw >>= 1;
   const dim3 g((unsigned)((n_tiles + tpw - 1) / tpw), (unsigned)nb, (unsigned)batch), b(256);
-  if (dtype == NVFP4_DTYPE_BF16)
-    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_BF16>, g, b, 0, st, w, S, H, scales, obj, rows, nb,
-                       tpw);
-  else
-    hipLaunchKernelGGL(k_lh_mfma<NVFP4_DTYPE_F32>, g, b, 0, st, w, S, H, scales, obj, rows, nb,
-                       tpw);
+#define NVFP4_LH(D, ST) \
+  hipLaunchKernelGGL((k_lh_mfma<D, ST>), g, b, 0, st, w, S, H, scales, obj, rows, nb, tpw)
+  if (dtype == NVFP4_DTYPE_BF16) {
+    if (g_stats_on) NVFP4_LH(NVFP4_DTYPE_BF16, true);
+    else NVFP4_LH(NVFP4_DTYPE_BF16, false);
+  } else {
+    if (g_stats_on) NVFP4_LH(NVFP4_DTYPE_F32, true);
+    else NVFP4_LH(NVFP4_DTYPE_F32, false);
+  }
+#undef NVFP4_LH
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+void search_stats_enable(bool on) { g_stats_on = on; }
+
+int search_stats_read(int64_t *out, hipStream_t st) {
+  if (hipStreamSynchronize(st) != hipSuccess) return NVFP4_ERR_HIP;
+  unsigned long long v[NVFP4_STATS_N];
+  if (hipMemcpyFromSymbol(v, HIP_SYMBOL(g_search_stats), sizeof(v), 0, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return NVFP4_ERR_HIP;
+  const unsigned long long zero[NVFP4_STATS_N] = {};
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_search_stats), zero, sizeof(zero), 0,
+                        hipMemcpyHostToDevice) != hipSuccess)
+    return NVFP4_ERR_HIP;
+  for (int i = 0; i < NVFP4_STATS_N; ++i) out[i] = (int64_t)v[i];
+  return NVFP4_OK;
 }
 
 }  // namespace nvfp4

@@ -57,6 +57,8 @@ _SIGS = {
     "nvfp4_gptq_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_gptq": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_debug_nonfinite": (_I, [_P, _P]),
+    "nvfp4_search_stats_enable": (_I, [_I]),
+    "nvfp4_search_stats_read": (_I, [_P, _P]),
     "nvfp4_route_groups_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_route_groups": (_I, [_P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P]),
 }
@@ -314,6 +316,24 @@ def debug_nonfinite() -> bool:
     flag = ctypes.c_int32(0)
     _check(lib().nvfp4_debug_nonfinite(ctypes.byref(flag), _stream()), "nvfp4_debug_nonfinite")
     return bool(flag.value)
+
+
+STATS_NAMES = ("mse_blocks", "mse_evals", "lh_pairs", "lh_zero_h", "lh_rel", "lh_abs",
+               "lh_noprune", "lh_rescan", "lh_two", "lh_screened", "lh_exact")
+STATS_N = 16
+
+
+def search_stats_enable(on: bool) -> None:
+    """Switch the searches' work counters on or off (process-wide; off by default)."""
+    _check(lib().nvfp4_search_stats_enable(int(bool(on))), "nvfp4_search_stats_enable")
+
+
+def search_stats_read() -> dict:
+    """The searches' work counters since the last read, by name (synchronises the current
+    stream; clears them)."""
+    out = (ctypes.c_int64 * STATS_N)()
+    _check(lib().nvfp4_search_stats_read(out, _stream()), "nvfp4_search_stats_read")
+    return {n: int(out[i]) for i, n in enumerate(STATS_NAMES)}
 
 
 def full_hessian(x: torch.Tensor, H: torch.Tensor | None = None, accumulate: bool = False,

@@ -18,7 +18,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = nvfp4.declared_symbols()
-    assert len(names) == 26
+    assert len(names) == 28
     for n in names:
         assert hasattr(L, n), n
     assert L.nvfp4_version() == 100

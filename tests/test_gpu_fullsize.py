@@ -1,6 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark uses.
-The oracle recomputes sampled rows / block columns / experts (each is independent of the
-rest once S and H are fixed), bit-exact except the Hessian (1e-4 relative Frobenius)."""
+The oracle recomputes sampled rows / experts, or all of them where it takes seconds (each is
+independent of the rest once S and H are fixed), bit-exact except the Hessian (1e-4 relative
+Frobenius). The Local-Hessian searches run on the oracle's Hessians built from every
+calibration token, the same data the benchmark's Hessians come from."""
 import numpy as np
 import pytest
 import torch
@@ -102,30 +104,53 @@ def test_mlp_weight_four_over_six_12288x4096(orc):
     assert torch.all(obj.view(-1) <= e_max * (1 + 1e-5) + 1e-30)
 
 
+def _search_three_ways(wd, S, Hd):
+    """Local-Hessian bytes as the benchmark runs the search (no objectives, no counters),
+    bytes and objectives, and the counters of a third, counting run."""
+    sc_bench = nvfp4.scale_search_local_hessian(wd, S, Hd)
+    sc, obj = nvfp4.scale_search_local_hessian(wd, S, Hd, return_obj=True)
+    nvfp4.search_stats_read()  # clear
+    nvfp4.search_stats_enable(True)
+    try:
+        sc_st = nvfp4.scale_search_local_hessian(wd, S, Hd)
+        stats = nvfp4.search_stats_read()
+    finally:
+        nvfp4.search_stats_enable(False)
+    assert torch.equal(sc_bench, sc) and torch.equal(sc_st, sc)
+    return sc.cpu().numpy(), obj.cpu().numpy(), stats
+
+
+def _report(stats, n_blocks):
+    print("[info] Local-Hessian paths: " + ", ".join(f"{k} {v}" for k, v in stats.items()
+                                                      if k.startswith("lh_")), flush=True)
+    assert stats["lh_pairs"] + stats["lh_zero_h"] == n_blocks
+    assert stats["lh_rel"] + stats["lh_abs"] <= stats["lh_pairs"]
+    assert stats["lh_rescan"] <= stats["lh_pairs"]
+
+
 def test_projection_hessian_and_local_hessian_full(orc):
-    case("block Hessian of 131072x4096 bf16 t4 tokens + Local-Hessian on 4096x4096")
+    case("block Hessian of 131072x4096 bf16 t4 tokens + Local-Hessian on 4096x4096, "
+         "both sides on the oracle's H from all 131072 tokens, every row")
     w, x = synth.projection(0)
     xd, wd = x.to(DEV), w.to(DEV)
     H = nvfp4.block_hessian(xd)
     torch.cuda.synchronize()
     Hn = H.cpu().numpy()
-    for b in (0, 77, 200, 255):
-        xb = np.ascontiguousarray(f32(x[:, 16 * b:16 * b + 16]))
-        assert rel_frob(Hn[b], orc.block_hessian(xb)[0]) <= 1e-4, b
     del xd, H
-    # the search at full size, both sides on the oracle's S and on an oracle H (from the
-    # first 8192 tokens: any H of the right shape exercises the search)
+    Href = orc.block_hessian(f32(x))  # fp64, all tokens
+    assert rel_frob(Hn, Href) <= 1e-4
+    del Hn
+    Href = Href.astype(np.float32)
     wn = f32(w)
     S_ref = orc.tensor_scale(wn)
     S = nvfp4.global_scale(wd)
     assert S.item() == S_ref
-    Href = orc.block_hessian(f32(x[:8192])).astype(np.float32)
-    sc, obj = nvfp4.scale_search_local_hessian(wd, torch.tensor([S_ref], device=DEV),
-                                               torch.from_numpy(Href).to(DEV), return_obj=True)
-    rows = np.random.default_rng(2).choice(w.shape[0], 6, replace=False)
-    sr, orf = orc.scales_local_hessian(wn[rows], S_ref, Href, with_obj=True)
-    assert np.array_equal(sc.cpu().numpy()[rows], sr)
-    assert np.array_equal(obj.cpu().numpy()[rows], orf)
+    sc, obj, stats = _search_three_ways(wd, torch.tensor([S_ref], device=DEV),
+                                        torch.from_numpy(Href).to(DEV))
+    sr, orf = orc.scales_local_hessian(wn, S_ref, Href, with_obj=True)
+    assert np.array_equal(sc, sr)
+    assert np.array_equal(obj, orf)
+    _report(stats, int((np.abs(wn).reshape(-1, 16).max(1) > 0).sum()))
 
 
 def test_projection_full_hessian_and_gptq(orc):
@@ -171,7 +196,8 @@ def test_projection_full_hessian_and_gptq(orc):
 
 
 def test_moe_routing_hessian_local_hessian_full(orc):
-    case("MoE: 128 experts 512x2048, 65536 tokens top-8 Zipf(1.1)")
+    case("MoE: 128 experts 512x2048, 65536 tokens top-8 Zipf(1.1); both searches on the "
+         "oracle's H from every routed token; every row of 16 experts")
     w, x, ids = synth.moe(0)
     off, tok = nvfp4.route_groups(ids.to(DEV), 128)
     off_ref, tok_ref = orc.route_groups(ids.numpy(), 128)
@@ -182,27 +208,22 @@ def test_moe_routing_hessian_local_hessian_full(orc):
           flush=True)
     H = nvfp4.block_hessian(x.to(DEV), group_offsets=off, token_ids=tok)
     Hn = H.cpu().numpy()
+    del H
     xn = f32(x)
-    picks = [int(np.argmax(counts)), int(np.argsort(counts)[64]), int(np.argmin(counts))]
-    for e in picks:
-        sel = tok_ref[off_ref[e]:off_ref[e + 1]]
-        for b in (0, 127):
-            xb = np.ascontiguousarray(xn[:, 16 * b:16 * b + 16])
-            assert rel_frob(Hn[e, b], orc.block_hessian(xb, sel)[0]) <= 1e-4, (e, b)
-    del H, Hn
-    # the batched search at full size, both sides on the oracle's S and on oracle H (from up
-    # to 512 of each expert's routed tokens)
+    Href = np.stack([orc.block_hessian(xn, tok_ref[off_ref[e]:off_ref[e + 1]]) for e in range(128)])
+    assert rel_frob(Hn, Href) <= 1e-4  # every expert, every block
+    del Hn
+    Href = Href.astype(np.float32)
     wd = w.to(DEV)
     wn = f32(w)
     Sn = np.array([orc.tensor_scale(wn[e]) for e in range(128)], np.float32)
     assert np.array_equal(nvfp4.global_scale(wd).cpu().numpy(), Sn)
-    Href = np.stack([orc.block_hessian(xn, tok_ref[off_ref[e]:min(off_ref[e + 1], off_ref[e] + 512)])
-                     for e in range(128)]).astype(np.float32)
-    sc, obj = nvfp4.scale_search_local_hessian(wd, torch.from_numpy(Sn).to(DEV),
-                                               torch.from_numpy(Href).to(DEV), return_obj=True)
-    for e in picks:
-        we = wn[e]
-        rows = np.random.default_rng(e).choice(512, 4, replace=False)
-        sr, orf = orc.scales_local_hessian(we[rows], Sn[e], Href[e], with_obj=True)
-        assert np.array_equal(sc[e].cpu().numpy()[rows], sr), e
-        assert np.array_equal(obj[e].cpu().numpy()[rows], orf), e
+    sc, obj, stats = _search_three_ways(wd, torch.from_numpy(Sn).to(DEV), torch.from_numpy(Href).to(DEV))
+    _report(stats, int((np.abs(wn).reshape(-1, 16).max(1) > 0).sum()))
+    order = np.argsort(counts, kind="stable")
+    picks = [int(order[-1]), int(order[64]), int(order[0])]
+    rest = [e for e in np.random.default_rng(7).permutation(128) if e not in picks]
+    for e in picks + [int(e) for e in rest[:13]]:
+        sr, orf = orc.scales_local_hessian(wn[e], Sn[e], Href[e], with_obj=True)
+        assert np.array_equal(sc[e], sr), e
+        assert np.array_equal(obj[e], orf), e

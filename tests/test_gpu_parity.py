@@ -573,16 +573,30 @@ def test_grouped_hessian_with_empty_group(orc):
 
 # ------------------------------------------------------------------ Local-Hessian search
 
-def _lh_check(orc, w, S, H):
+def _lh_check(orc, w, S, H, stats_out=None):
     """H: fp32 numpy [cols/16, 16, 16], made by the oracle or in closed form; both sides
-    search with it."""
+    search with it. The search also runs without objectives and with its counters on (a
+    separate instantiation); all give the same bytes. The counters go to stats_out."""
     H = np.ascontiguousarray(H, dtype=np.float32)
-    sc, obj = nvfp4.scale_search_local_hessian(w.to(DEV), dev_S(S), torch.from_numpy(H).to(DEV),
-                                               return_obj=True)
+    wd, Sd, Hd = w.to(DEV), dev_S(S), torch.from_numpy(H).to(DEV)
+    sc, obj = nvfp4.scale_search_local_hessian(wd, Sd, Hd, return_obj=True)
     sr, orf = orc.scales_local_hessian(f32(w), S, H, with_obj=True)
     g = sc.cpu().numpy()
     assert np.array_equal(g, sr), f"{np.sum(g != sr)} bytes differ"
     assert np.array_equal(obj.cpu().numpy(), orf)
+    assert torch.equal(nvfp4.scale_search_local_hessian(wd, Sd, Hd), sc)
+    nvfp4.search_stats_read()
+    nvfp4.search_stats_enable(True)
+    try:
+        sc_st = nvfp4.scale_search_local_hessian(wd, Sd, Hd)
+        st = nvfp4.search_stats_read()
+    finally:
+        nvfp4.search_stats_enable(False)
+    assert torch.equal(sc_st, sc)
+    nz = int((np.abs(f32(w)).reshape(-1, 16).max(1) > 0).sum())
+    assert st["lh_pairs"] + st["lh_zero_h"] == nz
+    if stats_out is not None:
+        stats_out.update(st)
     return g
 
 
@@ -607,7 +621,9 @@ def test_local_hessian_special_hessians(orc):
     S = orc.tensor_scale(wn)
     eye = np.repeat(np.eye(16, dtype=np.float32)[None], 8, axis=0)
     eye[2] = 0.0
-    g = _lh_check(orc, w, S, eye)
+    st = {}
+    g = _lh_check(orc, w, S, eye, st)
+    assert st["lh_zero_h"] == 64  # block column 2's 64 rows took the MSE choice
     mse = orc.scales_mse(wn, S)
     assert np.array_equal(g[:, 2], mse[:, 2])
     assert np.mean(g == mse) > 0.99
@@ -636,11 +652,21 @@ def test_local_hessian_magnitude_regimes(orc):
         ("nearly singular H, kappa ~3e9 (no pruning)", 1.0,
          np.repeat(_dominant_h(1e-8)[None], nb, axis=0)),
     ]
+    seen = {}
     for name, ws, H in regimes:
         case(f"local hessian, {name}")
         w = (w0.float() * ws).to(torch.bfloat16)
         S = orc.tensor_scale(f32(w))
-        _lh_check(orc, w, S, H)
+        st = {}
+        _lh_check(orc, w, S, H, st)
+        print("[info] " + ", ".join(f"{k} {v}" for k, v in st.items() if k.startswith("lh_")), flush=True)
+        seen[name] = st
+    # each of the kernel's paths is taken, and agrees with the oracle, in some regime
+    assert seen["large weights (x1e4)"]["lh_rel"] > 0 and seen["large weights (x1e4)"]["lh_two"] > 0
+    assert seen["diagonally dominant H, kappa ~3e4 (absolute screen bound)"]["lh_abs"] > 0
+    assert seen["nearly singular H, kappa ~3e9 (no pruning)"]["lh_noprune"] > 0
+    assert seen["huge H (x1e30): fp32 screen would overflow"]["lh_rescan"] == 1024
+    assert seen["H in the fp32 denormal range (x1e-44)"]["lh_rescan"] == 1024
 
 
 def test_local_hessian_batched_experts(orc):
