@@ -88,3 +88,79 @@ def mse_ranking(xs, S: Fr, dq_round=None):
 
 def quad_form(d, H) -> Fr:
     return sum(Fr(d[i]) * Fr(H[i][j]) * Fr(d[j]) for i in range(len(d)) for j in range(len(d)))
+
+
+# ---------------------------------------------------------------- exact integer brute force
+# Every finite fp32 value, every product M_j s S of an E2M1 midpoint (a multiple of 1/4), an
+# E4M3 value (a multiple of 2^-9) and an fp32 tensor scale (a multiple of 2^-149), and every
+# stored magnitude fp32(G_k s S) is an integer multiple of 2^-K with K = 170. Scaled by 2^K
+# they become Python integers, so codes and objectives below are exact and fast enough for
+# whole tensors of the tiny configuration.
+
+K = 170
+MIDS = [Fr(1, 4), Fr(3, 4), Fr(5, 4), Fr(7, 4), Fr(5, 2), Fr(7, 2), Fr(5)]
+
+
+def to_fixed(q) -> int:
+    """q (a Fraction or float with a power-of-two denominator dividing 2^K) times 2^K."""
+    q = Fr(q)
+    den = q.denominator
+    assert (1 << K) % den == 0, "denominator is not a power of two up to 2^K"
+    return q.numerator * ((1 << K) // den)
+
+
+def candidate_tables(S, fp32_round):
+    """For each byte c in 1..126: the seven midpoint thresholds M_j s S (exact), and the
+    eight stored magnitudes fp32(G_k s S) both as integers at 2^-K and as floats.
+    fp32_round maps an exact rational to the nearest fp32 value (ties to even)."""
+    Sf = Fr(S)
+    tabs = []
+    for c in range(1, 127):
+        sS = e4m3(c) * Sf
+        thr = [to_fixed(m * sS) for m in MIDS]
+        mags = [fp32_round(g * sS) for g in GRID]
+        tabs.append((c, thr, [to_fixed(m) for m in mags], mags))
+    return tabs
+
+
+def code_index(X: int, thr) -> int:
+    """Grid index of a magnitude X (at 2^-K) under thresholds thr: the number of midpoints
+    below X, a value exactly on a midpoint going to the even index."""
+    from bisect import bisect_left, bisect_right
+    lo, hi = bisect_left(thr, X), bisect_right(thr, X)
+    return hi if (lo != hi and lo % 2 == 1) else lo
+
+
+def mse_objectives_fixed(xs, tabs):
+    """Exact sum of (dq_i - x_i)^2 at 2^-2K for every candidate in tabs; dq is the stored
+    fp32 magnitude with the sign of x (so each error is its magnitude minus |x|)."""
+    X = [abs(to_fixed(float(v))) for v in xs]
+    out = []
+    for c, thr, magf, _ in tabs:
+        acc = 0
+        for Xi in X:
+            e = magf[code_index(Xi, thr)] - Xi
+            acc += e * e
+        out.append(acc)
+    return out
+
+
+def candidate_weight_errors(ws, tabs):
+    """d[c][i] = fp32(dq_i(c) - w_i) for every candidate in tabs, as float32 [126, 16]: the
+    codes decided exactly, dq the stored fp32 magnitude carrying the sign of w, and the
+    difference rounded once to fp32 (numpy float32 subtraction is IEEE single precision)."""
+    import numpy as np
+    W = np.asarray(ws, dtype=np.float32)
+    X = [abs(to_fixed(float(v))) for v in W]
+    D = np.empty((len(tabs), len(W)), dtype=np.float32)
+    for ci, (c, thr, magf, mags) in enumerate(tabs):
+        dq = np.array([mags[code_index(Xi, thr)] for Xi in X], dtype=np.float32)
+        D[ci] = np.where(W < 0, -dq, dq) - W
+    return D
+
+
+def quad_form_fixed(d, Hf) -> int:
+    """Exact d H d^T at 2^-3K for fp32 d and H given as integers at 2^-K (Hf[i][j])."""
+    D = [to_fixed(float(v)) for v in d]
+    n = len(D)
+    return sum(D[i] * sum(Hf[i][j] * D[j] for j in range(n)) for i in range(n))
