@@ -76,6 +76,16 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads used by the parallel loops from now on (timing runs on one thread). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Value of an OCP E4M3FN byte (bias 7, 3 mantissa bits, no infinities): bytes 0x00..0x7E
  * are 0 and the 126 positive values [LH] counts; 0x7F is NaN. Sign bit ignored. */
 double oracle_e4m3_value(int byte)

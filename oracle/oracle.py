@@ -97,6 +97,8 @@ def lib():
         L.oracle_gptq_rows.argtypes = [P, i64, i64, f32, P, P, P, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -112,6 +114,11 @@ def _f32(x) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops from now on."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def e4m3_value(byte: int) -> float:
