@@ -188,7 +188,11 @@ int nvfp4_calib_scale(const uint64_t *hist, double fraction, float *S, void *str
 
 size_t nvfp4_block_hessian_workspace_size(int64_t tokens, int64_t cols, int64_t groups,
                                           int64_t n_ids) {
+  // 0 for arguments nvfp4_block_hessian rejects (every size below then fits in 64 bits)
+  int64_t t1, t2;
   if (tokens < 0 || cols < 0 || groups < 0 || n_ids < 0) return 0;
+  if (!mul_ok(tokens, cols, &t1) || !mul_ok(t1, 4, &t2)) return 0;
+  if (groups > kMaxGridY || n_ids > INT32_MAX || tokens > INT32_MAX) return 0;
   const size_t dense = hessian_workspace_size(tokens, cols, groups, -1);
   const size_t grouped = hessian_workspace_size(tokens, cols, groups, n_ids);
   return dense > grouped ? dense : grouped;
@@ -266,7 +270,10 @@ int nvfp4_fakequant(const void *x, int dtype, int64_t batch, int64_t rows, int64
 }
 
 size_t nvfp4_route_groups_workspace_size(int64_t tokens, int64_t topk, int64_t experts) {
-  if (tokens < 0 || topk < 0 || experts < 0) return 0;
+  // 0 for arguments nvfp4_route_groups rejects
+  int64_t pairs;
+  if (tokens < 0 || topk < 0 || experts <= 0 || experts > 16384) return 0;
+  if (!mul_ok(tokens, topk, &pairs) || pairs > INT32_MAX) return 0;
   return route_workspace_size(tokens, topk, experts);
 }
 
@@ -345,7 +352,10 @@ int nvfp4_gptq_factor(const float *H, int64_t cols, double damp, double *U, int3
 }
 
 size_t nvfp4_gptq_workspace_size(int64_t rows, int64_t cols) {
-  if (rows < 0 || cols <= 0) return 0;
+  // 0 for arguments nvfp4_gptq rejects
+  int64_t r1, r2;
+  if (rows < 0 || cols <= 0 || cols > 65536) return 0;
+  if (!mul_ok(rows, cols, &r1) || !mul_ok(r1, 4, &r2) || (rows + 63) / 64 > INT32_MAX) return 0;
   return gptq_rows_workspace_size(rows, cols);
 }
 
