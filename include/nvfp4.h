@@ -37,6 +37,7 @@
  *  - `stream` is a hipStream_t (NULL = the null stream). Every call is asynchronous on it.
  *  - Return value: NVFP4_OK or an error code below. Calls with an empty tensor (a zero
  *    dimension) validate their shape and return NVFP4_OK without launching.
+ *  - The *_workspace_size queries return 0 for arguments their entry point rejects.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
