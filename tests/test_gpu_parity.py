@@ -571,6 +571,34 @@ def test_grouped_hessian_with_empty_group(orc):
         assert rel_frob(H[e], orc.block_hessian(f32(x), tok_ref[off_ref[e]:off_ref[e + 1]])) <= 1e-4
 
 
+@pytest.mark.parametrize("cols", [256, 208])
+def test_grouped_hessian_accumulate_multi_piece(orc, cols):
+    """Grouped bf16 Hessians accumulated over two batches. Expert 0 takes every token
+    (its list is cut into several pieces whose partial sums are reduced), the others a
+    few hundred each (one piece, written straight into H); 208 channels leave a ragged
+    last 64-channel chunk."""
+    case(f"grouped hessian accumulate, multi-piece expert 0, cols={cols}")
+    tokens, E = 9000, 5
+    x = synth.projection(11, rows=16, cols=cols, tokens=tokens)[1]
+    rng = np.random.default_rng(12)
+    second = rng.integers(1, E, size=tokens)
+    ids = np.stack([np.zeros(tokens, np.int64), second], 1).astype(np.int32)
+    xn = f32(x)
+    halves = (slice(0, 4000), slice(4000, tokens))
+    H = None
+    for sl in halves:
+        xb = x[sl].contiguous()
+        off, tok = nvfp4.route_groups(torch.from_numpy(ids[sl].copy()).to(DEV), E)
+        H = nvfp4.block_hessian(xb.to(DEV), group_offsets=off, token_ids=tok, H=H,
+                                accumulate=H is not None)
+    off_ref, tok_ref = orc.route_groups(ids, E)
+    assert int(off_ref[1]) == tokens  # expert 0: every token
+    Hn = H.cpu().numpy()
+    for e in range(E):
+        Href = orc.block_hessian(xn, tok_ref[off_ref[e]:off_ref[e + 1]])
+        assert rel_frob(Hn[e], Href) <= 1e-4, e
+
+
 # ------------------------------------------------------------------ Local-Hessian search
 
 def _lh_check(orc, w, S, H, stats_out=None):
