@@ -308,7 +308,7 @@ int launch_four_over_six(const void *w, int dtype, int64_t batch, int64_t rows, 
 
 // the four fp32 weight errors of this lane's elements under candidate c
 __device__ __forceinline__ void lh_delta4(const float v[4], int c, const Cand &e, float S,
-                                          bool fast_ok, float d[4]) {
+                                          bool fast_ok, float d[4], bool act = true) {
   unsigned code;
   if (fast_ok) {
     unsigned a = 0u, b = 0u;
@@ -318,7 +318,7 @@ __device__ __forceinline__ void lh_delta4(const float v[4], int c, const Cand &e
     b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, v[2] * e.rhi, v[3] * e.rhi, 1.0f, 1);
     a &= 0xFFFFu;
     b &= 0xFFFFu;
-    if (a != b) {
+    if (a != b && act) {
       float v8[8] = {v[0], v[1], v[2], v[3], 0.0f, 0.0f, 0.0f, 0.0f};
       a = fp4_resolve8(v8, a, b, (double)e.s * (double)S);
     }
@@ -395,15 +395,16 @@ struct Screen {
   int c1, c2;
 };
 
+// (selects, no branches: L1 <= L2 <= L3, so L < L1 implies L < L2 < ... ; L = +inf changes
+// nothing)
 __device__ __forceinline__ void screen_add(Screen &z, float L, float U, int c) {
   z.theta = fminf(z.theta, U);
-  if (L < z.L1) {
-    z.L3 = z.L2; z.L2 = z.L1; z.c2 = z.c1; z.L1 = L; z.c1 = c;
-  } else if (L < z.L2) {
-    z.L3 = z.L2; z.L2 = L; z.c2 = c;
-  } else if (L < z.L3) {
-    z.L3 = L;
-  }
+  const bool b1 = L < z.L1, b2 = L < z.L2, b3 = L < z.L3;
+  z.L3 = b2 ? z.L2 : (b3 ? L : z.L3);
+  z.L2 = b1 ? z.L1 : (b2 ? L : z.L2);
+  z.c2 = b1 ? z.c1 : (b2 ? c : z.c2);
+  z.L1 = b1 ? L : z.L1;
+  z.c1 = b1 ? c : z.c1;
 }
 
 // merge with the lane 16 (OFF = 16) or 32 (OFF = 32) positions away (both lanes end with
@@ -443,6 +444,9 @@ __device__ __forceinline__ void screen_merge(Screen &z) {
   z = r;
 }
 
+constexpr int LH_TILES = 8;                // tiles of 64 rows per workgroup, at most
+constexpr int LH_ROWS_MAX = 64 * LH_TILES;
+
 template <int DT, bool STATS>
 __global__ void __launch_bounds__(256)
     k_lh_mfma(const void *__restrict__ w, const float *__restrict__ S_arr,
@@ -453,6 +457,8 @@ __global__ void __launch_bounds__(256)
   __shared__ double gw[16];
   __shared__ double kap[16];
   __shared__ float aw[16];
+  __shared__ int32_t ord[LH_ROWS_MAX];  // this workgroup's rows (offsets), in key order
+  __shared__ uint32_t bins[128];
   // Workgroups go to the eight XCDs round-robin by linear id; renumber them so that each XCD
   // takes one contiguous range (neighbouring block columns share 128-byte lines of W and of
   // the scale bytes, and each XCD has its own L2).
@@ -525,6 +531,49 @@ __global__ void __launch_bounds__(256)
     return;
   }
 
+  // Sort this workgroup's rows by the byte nearest amax/(6S) (a counting sort in LDS), so
+  // that the 16 pairs of a wave, which step through their candidate windows together, have
+  // windows of about the same length. The key is only an ordering: every pair's result is
+  // independent of where it is processed.
+  const int64_t r0 = tile0 * 64;
+  const int nr = (int)(min(tile1 * 64, rows) - r0);  // <= LH_ROWS_MAX
+  if (threadIdx.x < 128) bins[threadIdx.x] = 0u;
+  __syncthreads();
+  int key[LH_ROWS_MAX / 256], pos[LH_ROWS_MAX / 256];
+#pragma unroll
+  for (int k = 0; k < LH_ROWS_MAX / 256; ++k) {
+    const int i = (int)threadIdx.x + 256 * k;
+    key[k] = -1;
+    if (i < nr) {
+      float vv[16];
+      load16<DT>(w, (batch * rows + r0 + i) * nb + b, vv);
+      float am = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(vv[j]));
+      const float qb = fminf(am * cand[1].rlo * 0x1p-9f * (1.0f / 6.0f), 448.0f);
+      key[k] = (int)(__builtin_amdgcn_cvt_pk_fp8_f32(qb, qb, 0, false) & 0x7F);
+      pos[k] = (int)atomicAdd(&bins[key[k]], 1u);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {  // exclusive scan of the 128 bin counts, two per lane
+    const int l = threadIdx.x;
+    const uint32_t b0 = bins[2 * l], b1 = bins[2 * l + 1];
+    uint32_t inc = b0 + b1;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(inc, d, 64);
+      inc += l >= d ? o : 0u;
+    }
+    bins[2 * l] = inc - b0 - b1;
+    bins[2 * l + 1] = inc - b1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < LH_ROWS_MAX / 256; ++k)
+    if (key[k] >= 0) ord[bins[key[k]] + pos[k]] = (int)threadIdx.x + 256 * k;
+  __syncthreads();
+
   const int lane = threadIdx.x & 63, p = lane & 15, q = lane >> 4;
   float ha[4], ab[4];
 #pragma unroll
@@ -537,8 +586,9 @@ __global__ void __launch_bounds__(256)
   unsigned st_pairs = 0, st_rel = 0, st_abs = 0, st_noprune = 0, st_rescan = 0, st_two = 0;
   unsigned st_screened = 0, st_exact = 0;
   for (int64_t tile = tile0; tile < tile1; ++tile) {
-  const int64_t row = tile * 64 + (threadIdx.x >> 6) * 16 + p;
-  const bool valid = row < rows;
+  const int idx = (int)(tile - tile0) * 64 + (int)(threadIdx.x >> 6) * 16 + p;
+  const bool valid = idx < nr;
+  const int64_t row = r0 + (valid ? ord[idx] : 0);
   const int64_t blk = (batch * rows + (valid ? row : 0)) * nb + b;
   float v[4];
   if (DT == NVFP4_DTYPE_BF16) {
@@ -584,8 +634,14 @@ __global__ void __launch_bounds__(256)
     float P[4], B[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float d[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (acts[k]) lh_delta4(v, cs[k], cand[cs[k]], S, true, d);
+      P[k] = 0.0f;
+      B[k] = 0.0f;
+      if (!__any(acts[k])) continue;  // a slot no pair of the wave uses
+      // every lane forms d (an inactive lane with byte 1: finite, since fast_ok holds for
+      // every byte); column p of the product depends only on pair p's d, and an inactive
+      // pair's objective is not used
+      float d[4];
+      lh_delta4(v, cs[k], cand[cs[k]], S, true, d, acts[k]);
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[t], d[t], acc, 0, 0, 0);
@@ -593,7 +649,6 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int r = 1; r < 4; ++r) op = __builtin_fmaf(d[r], acc[r], op);
       P[k] = op;
-      B[k] = 0.0f;
       if (!rel) {
         float bp = fabsf(d[0]) * ab[0];
 #pragma unroll
@@ -621,9 +676,11 @@ __global__ void __launch_bounds__(256)
       const float bb = t.r0 + t.r1;
       er = 1e-5f * bb * bb + tiny;
     }
-    const int cq = q == 0 ? cs[0] : (q == 1 ? cs[1] : (q == 2 ? cs[2] : cs[3]));
-    const bool aq = q == 0 ? acts[0] : (q == 1 ? acts[1] : (q == 2 ? acts[2] : acts[3]));
-    if (aq) screen_add(z, o - er, o + er, cq);
+    const int c01 = (q & 1) ? cs[1] : cs[0], c23 = (q & 1) ? cs[3] : cs[2];
+    const bool a01 = (q & 1) ? acts[1] : acts[0], a23 = (q & 1) ? acts[3] : acts[2];
+    const int cq = (q & 2) ? c23 : c01;
+    const bool aq = (q & 2) ? a23 : a01;
+    screen_add(z, aq ? o - er : INFINITY, aq ? o + er : INFINITY, cq);
     if (STATS) st_screened += aq ? 1u : 0u;
   };
   for (int j = 0;; j += 4) {
@@ -761,8 +818,6 @@ __global__ void __launch_bounds__(256)
     stat_add(NVFP4_STAT_LH_EXACT, st_exact);
   }
 }
-
-constexpr int64_t LH_TILES = 8;
 
 int launch_local_hessian(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,
                          const float *S, const float *H, uint8_t *scales, double *obj,
