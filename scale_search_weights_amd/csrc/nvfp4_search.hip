@@ -407,43 +407,6 @@ __device__ __forceinline__ void screen_add(Screen &z, float L, float U, int c) {
   z.c1 = b1 ? c : z.c1;
 }
 
-// merge with the lane 16 (OFF = 16) or 32 (OFF = 32) positions away (both lanes end with
-// the union's state)
-template <int OFF>
-__device__ __forceinline__ void screen_merge(Screen &z) {
-  auto other = [](auto x) { return OFF == 16 ? xor16(x) : xor32(x); };
-  Screen o;
-  o.theta = other(z.theta);
-  o.L1 = other(z.L1);
-  o.L2 = other(z.L2);
-  o.L3 = other(z.L3);
-  o.c1 = other(z.c1);
-  o.c2 = other(z.c2);
-  // order the two lists' entries deterministically (by L, then byte) so both lanes agree
-  auto less = [](float La, int ca, float Lb, int cb) { return La < Lb || (La == Lb && ca < cb); };
-  Screen r;
-  r.theta = fminf(z.theta, o.theta);
-  float A[3] = {z.L1, z.L2, z.L3}, B[3] = {o.L1, o.L2, o.L3};
-  int Ac[3] = {z.c1, z.c2, 0}, Bc[3] = {o.c1, o.c2, 0};
-  float M[3];
-  int Mc[3];
-  int ia = 0, ib = 0;
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    float La = ia == 0 ? A[0] : (ia == 1 ? A[1] : A[2]);
-    int ca = ia == 0 ? Ac[0] : (ia == 1 ? Ac[1] : Ac[2]);
-    float Lb = ib == 0 ? B[0] : (ib == 1 ? B[1] : B[2]);
-    int cb = ib == 0 ? Bc[0] : (ib == 1 ? Bc[1] : Bc[2]);
-    const bool ta = less(La, ca, Lb, cb);
-    M[k] = ta ? La : Lb;
-    Mc[k] = ta ? ca : cb;
-    ia += ta ? 1 : 0;
-    ib += ta ? 0 : 1;
-  }
-  r.L1 = M[0]; r.c1 = Mc[0]; r.L2 = M[1]; r.c2 = Mc[1]; r.L3 = M[2];
-  z = r;
-}
-
 constexpr int LH_TILES = 8;                // tiles of 64 rows per workgroup, at most
 constexpr int LH_ROWS_MAX = 64 * LH_TILES;
 
@@ -459,6 +422,12 @@ __global__ void __launch_bounds__(256)
   __shared__ float aw[16];
   __shared__ int32_t ord[LH_ROWS_MAX];  // this workgroup's rows (offsets), in key order
   __shared__ uint32_t bins[128];
+  // per row of the workgroup: its block as stored, the block max, and c_lo | c_hi << 8 |
+  // (first index of the max) << 16
+  constexpr int VB = DT == NVFP4_DTYPE_BF16 ? 32 : 64;
+  __shared__ __attribute__((aligned(16))) unsigned char wv[LH_ROWS_MAX * VB];
+  __shared__ float amx[LH_ROWS_MAX];
+  __shared__ int32_t meta[LH_ROWS_MAX];
   // Workgroups go to the eight XCDs round-robin by linear id; renumber them so that each XCD
   // takes one contiguous range (neighbouring block columns share 128-byte lines of W and of
   // the scale bytes, and each XCD has its own L2).
@@ -531,10 +500,11 @@ __global__ void __launch_bounds__(256)
     return;
   }
 
-  // Sort this workgroup's rows by the byte nearest amax/(6S) (a counting sort in LDS), so
-  // that the 16 pairs of a wave, which step through their candidate windows together, have
-  // windows of about the same length. The key is only an ordering: every pair's result is
-  // independent of where it is processed.
+  // Per row of this workgroup (one thread per row): the block, kept in LDS, its max, the first
+  // index of the max and the candidate window [c_lo, c_hi]. The rows are then sorted by the
+  // window's length (a counting sort in LDS), so that the 16 pairs of a wave, which step
+  // through their windows together, have windows of about the same length. The order does
+  // not change any pair's result.
   const int64_t r0 = tile0 * 64;
   const int nr = (int)(min(tile1 * 64, rows) - r0);  // <= LH_ROWS_MAX
   if (threadIdx.x < 128) bins[threadIdx.x] = 0u;
@@ -545,13 +515,37 @@ __global__ void __launch_bounds__(256)
     const int i = (int)threadIdx.x + 256 * k;
     key[k] = -1;
     if (i < nr) {
+      const int64_t blk = (batch * rows + r0 + i) * nb + b;
+      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const unsigned char *>(w) + blk * VB);
+      uint4 *dst = reinterpret_cast<uint4 *>(wv + i * VB);
       float vv[16];
-      load16<DT>(w, (batch * rows + r0 + i) * nb + b, vv);
+#pragma unroll
+      for (int j = 0; j < VB / 16; ++j) {
+        const uint4 r = src[j];
+        dst[j] = r;
+        if (DT == NVFP4_DTYPE_BF16) {
+          vv[8 * j + 0] = bf16_lo(r.x); vv[8 * j + 1] = bf16_hi(r.x);
+          vv[8 * j + 2] = bf16_lo(r.y); vv[8 * j + 3] = bf16_hi(r.y);
+          vv[8 * j + 4] = bf16_lo(r.z); vv[8 * j + 5] = bf16_hi(r.z);
+          vv[8 * j + 6] = bf16_lo(r.w); vv[8 * j + 7] = bf16_hi(r.w);
+        } else {
+          vv[4 * j + 0] = __uint_as_float(r.x); vv[4 * j + 1] = __uint_as_float(r.y);
+          vv[4 * j + 2] = __uint_as_float(r.z); vv[4 * j + 3] = __uint_as_float(r.w);
+        }
+      }
       float am = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(vv[j]));
-      const float qb = fminf(am * cand[1].rlo * 0x1p-9f * (1.0f / 6.0f), 448.0f);
-      key[k] = (int)(__builtin_amdgcn_cvt_pk_fp8_f32(qb, qb, 0, false) & 0x7F);
+      int li = 16;
+#pragma unroll
+      for (int j = 15; j >= 0; --j) li = fabsf(vv[j]) == am ? j : li;
+      int cz = 127, cb = 0;
+      if (am != 0.0f) window_bounds(am, cand, S, cz, cb);
+      const int c_hi = cz <= 126 ? cz : 126, c_lo = cb >= 1 ? cb : 1;
+      const int n_up = am != 0.0f ? c_hi - c_lo + 1 : 0;
+      amx[i] = am;
+      meta[i] = c_lo | (c_hi << 8) | (li << 16);
+      key[k] = n_up < 0 ? 0 : (n_up > 127 ? 127 : n_up);
       pos[k] = (int)atomicAdd(&bins[key[k]], 1u);
     }
   }
@@ -590,32 +584,22 @@ __global__ void __launch_bounds__(256)
   const bool valid = idx < nr;
   const int64_t row = r0 + (valid ? ord[idx] : 0);
   const int64_t blk = (batch * rows + (valid ? row : 0)) * nb + b;
+  const int ri = valid ? ord[idx] : 0;  // the row's slot in LDS
   float v[4];
   if (DT == NVFP4_DTYPE_BF16) {
     uint2 u = make_uint2(0u, 0u);
-    if (valid) u = reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(w) + blk * 16)[q];
+    if (valid) u = reinterpret_cast<const uint2 *>(wv + ri * VB)[q];
     v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
   } else {
     float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (valid) u = reinterpret_cast<const float4 *>(static_cast<const float *>(w) + blk * 16)[q];
+    if (valid) u = reinterpret_cast<const float4 *>(wv + ri * VB)[q];
     v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
   }
-  float lmax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  LanePair t = swap16(lmax, lmax);
-  lmax = fmaxf(t.r0, t.r1);
-  t = swap32(lmax, lmax);
-  const float amax = fmaxf(t.r0, t.r1);
-  int li = 16;
-#pragma unroll
-  for (int r = 3; r >= 0; --r) li = (fabsf(v[r]) == amax) ? 4 * q + r : li;
-  li = min(li, xor16(li));
-  const int m = min(li, xor32(li));  // first index of the block max
-
+  const float amax = valid ? amx[ri] : 0.0f;
+  const int mt = meta[ri];
+  const int m = mt >> 16;  // first index of the block max
   const bool live = valid && amax != 0.0f;
-  int cz = 127, cb = 0;
-  if (live) window_bounds(amax, cand, S, cz, cb);
-  const int c_hi = cz <= 126 ? cz : 126;
-  const int c_lo = cb >= 1 ? cb : 1;
+  const int c_lo = live ? (mt & 0xFF) : 1, c_hi = live ? ((mt >> 8) & 0xFF) : 126;
   const bool fast_ok = fast_path_ok(amax, cand) && amax >= 0x1p-60f;
   const double gm = gw[m < 16 ? m : 0];
 
@@ -629,19 +613,22 @@ __global__ void __launch_bounds__(256)
   const bool screen_ok = fast_ok && hmax * da * da < 0x1p100f;
   bool screen = live && screen_ok;
   Screen z = {INFINITY, INFINITY, INFINITY, INFINITY, 0, 0};
-  auto step4 = [&](const int cs[4], const bool acts[4]) {
+  // a step: slot k scores byte base + dir k for the pairs whose bit k of `am` is set
+  auto step4 = [&](int base, int dir, unsigned am) {
     typedef float v4f __attribute__((ext_vector_type(4)));
     float P[4], B[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       P[k] = 0.0f;
       B[k] = 0.0f;
-      if (!__any(acts[k])) continue;  // a slot no pair of the wave uses
+      const bool act = (am >> k) & 1u;
+      if (!__any(act)) continue;  // a slot no pair of the wave uses
+      const int ck = act ? base + dir * k : 1;
       // every lane forms d (an inactive lane with byte 1: finite, since fast_ok holds for
       // every byte); column p of the product depends only on pair p's d, and an inactive
       // pair's objective is not used
       float d[4];
-      lh_delta4(v, cs[k], cand[cs[k]], S, true, d, acts[k]);
+      lh_delta4(v, ck, cand[ck], S, true, d, act);
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[t], d[t], acc, 0, 0, 0);
@@ -676,26 +663,17 @@ __global__ void __launch_bounds__(256)
       const float bb = t.r0 + t.r1;
       er = 1e-5f * bb * bb + tiny;
     }
-    const int c01 = (q & 1) ? cs[1] : cs[0], c23 = (q & 1) ? cs[3] : cs[2];
-    const bool a01 = (q & 1) ? acts[1] : acts[0], a23 = (q & 1) ? acts[3] : acts[2];
-    const int cq = (q & 2) ? c23 : c01;
-    const bool aq = (q & 2) ? a23 : a01;
+    const int cq = base + dir * q;  // (arithmetic, not an indexed array: no private memory)
+    const bool aq = (am >> q) & 1u;
     screen_add(z, aq ? o - er : INFINITY, aq ? o + er : INFINITY, cq);
     if (STATS) st_screened += aq ? 1u : 0u;
   };
   for (int j = 0;; j += 4) {
-    int cs[4];
-    bool acts[4];
-    bool any = false;
+    unsigned am = 0u;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = c_lo + j + k;
-      acts[k] = screen && c <= c_hi;
-      cs[k] = acts[k] ? c : 1;
-      any = any || acts[k];
-    }
-    if (!__any(any)) break;
-    step4(cs, acts);
+    for (int k = 0; k < 4; ++k) am |= (screen && c_lo + j + k <= c_hi) ? 1u << k : 0u;
+    if (!__any(am != 0u)) break;
+    step4(c_lo + j, 1, am);
   }
   // downward: the bound uses the pair's theta so far (merged over its four lanes)
   bool down = screen;
@@ -704,9 +682,7 @@ __global__ void __launch_bounds__(256)
     float th = fminf(t.r0, t.r1);
     t = swap32(th, th);
     th = fminf(t.r0, t.r1);
-    int cs[4];
-    bool acts[4];
-    bool any = false;
+    unsigned am = 0u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = c0 - k;
@@ -716,27 +692,61 @@ __global__ void __launch_bounds__(256)
         if (gm * e7 * e7 > (double)th * margin) a = false;
       }
       down = a;  // the bound is monotone: once pruned, every smaller byte is too
-      acts[k] = a;
-      cs[k] = a ? c : 1;
-      any = any || a;
+      am |= a ? 1u << k : 0u;
     }
-    if (!__any(any)) break;
-    step4(cs, acts);
+    if (!__any(am != 0u)) break;
+    step4(c0, -1, am);
   }
-  screen_merge<16>(z);
-  screen_merge<32>(z);
-  const float theta = z.theta, L2 = z.L2, L3 = z.L3;
-  const int c1 = z.c1, c2 = z.c2;
+  // ---- the pair's screening result. Each candidate was scored by exactly one of the pair's
+  // four lanes, so their lists are disjoint: theta is the smallest upper bound, c1 the byte
+  // of the smallest lower bound (ties to the smaller byte), and n the number of listed lower
+  // bounds <= theta (a lane lists its three smallest, so n >= 3 means three or more
+  // candidates can still be the exact argmin).
+  float theta = z.theta, n_le;
+  {
+    LanePair t = swap16(theta, theta);
+    theta = fminf(t.r0, t.r1);
+    t = swap32(theta, theta);
+    theta = fminf(t.r0, t.r1);
+    n_le = (float)((z.L1 <= theta ? 1 : 0) + (z.L2 <= theta ? 1 : 0) + (z.L3 <= theta ? 1 : 0));
+    t = swap16(n_le, n_le);
+    n_le = t.r0 + t.r1;
+    t = swap32(n_le, n_le);
+    n_le = t.r0 + t.r1;
+  }
+  // (L, c) := the smaller of the pair's four (L, c) entries, ties to the smaller byte; the
+  // two halves of a swap come in the same order in both lanes, so every lane agrees
+  auto pair_min = [](float &L, int &c) {
+    LanePair tl = swap16(L, L), tc = swap16(__int_as_float(c), __int_as_float(c));
+    bool o = tl.r1 < tl.r0 || (tl.r1 == tl.r0 && __float_as_int(tc.r1) < __float_as_int(tc.r0));
+    L = o ? tl.r1 : tl.r0;
+    c = __float_as_int(o ? tc.r1 : tc.r0);
+    tl = swap32(L, L);
+    tc = swap32(__int_as_float(c), __int_as_float(c));
+    o = tl.r1 < tl.r0 || (tl.r1 == tl.r0 && __float_as_int(tc.r1) < __float_as_int(tc.r0));
+    L = o ? tl.r1 : tl.r0;
+    c = __float_as_int(o ? tc.r1 : tc.r0);
+  };
+  float L1m = z.L1;
+  int c1 = z.c1;
+  pair_min(L1m, c1);
 
   // ---- exact decision
-  const bool overflow = screen && L3 <= theta;
+  const bool overflow = screen && n_le >= 3.0f;
   const bool slow = live && (!screen_ok || overflow);
   int best_c = 0;
   double best_o = 0.0;
   // (all cross-lane steps below run with the whole wave active; the four lanes of a pair
   // always agree on every per-pair flag)
   const bool sel = screen && !overflow;
-  const bool two = sel && L2 <= theta;
+  const bool two = sel && n_le >= 2.0f;
+  int c2 = 0;
+  if (__any(two)) {  // the second smallest: c1's lane offers its next entry, the others their first
+    const bool own = z.c1 == c1;
+    float L2m = own ? z.L2 : z.L1;
+    c2 = own ? z.c2 : z.c1;
+    pair_min(L2m, c2);
+  }
   const bool need = sel && (two || obj != nullptr);
   if (sel) best_c = c1;
   if (__any(need)) {
