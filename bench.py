@@ -214,6 +214,10 @@ def main():
     w1c, x1c = synth.tiny(0)
     w1, x1 = w1c.to(dev), x1c.to(dev)
     r1, c1 = w1.shape
+    # workspace of the two-launch tensor scale (per-workgroup partial maxima)
+    wsS_n = max(L.nvfp4_global_scale_workspace_size(b_, n_)
+                for b_, n_ in ((1, r3 * c3), (1, r4 * c4), (E, r5 * c5), (1, r1 * c1)))
+    wsS = torch.empty(wsS_n, dtype=torch.uint8, device=dev)
     t1 = x1.shape[0]
     S1 = torch.empty(1, dtype=torch.float32, device=dev)
     y1 = torch.empty_like(w1)
@@ -253,7 +257,7 @@ def main():
                                                           P(gx2), sptr), "ste backward"),
                                   ok(L.nvfp4_scale_ema(P(S2run), P(S2), 1, ctypes.c_float(0.9), sptr),
                                      "scale ema")))
-        stage("scale_mlp", lambda: ok(L.nvfp4_global_scale(P(w3), BF16, 1, r3 * c3, P(S3), sptr), "scale"))
+        stage("scale_mlp", lambda: ok(L.nvfp4_global_scale_ws(P(w3), BF16, 1, r3 * c3, P(S3), P(wsS), wsS_n, sptr), "scale"))
         stage("mse_mlp", lambda: ok(L.nvfp4_scale_search_mse(
             P(w3), BF16, 1, r3, c3, P(S3), P(sc3), None, sptr), "mse"))
         stage("four_over_six_mlp", lambda: ok(L.nvfp4_scale_search_four_over_six(
@@ -262,7 +266,7 @@ def main():
             P(w3), BF16, 1, r3, c3, P(S3), P(sc3), P(codes3), None, sptr), "quantize"))
         stage("hessian_proj", lambda: ok(L.nvfp4_block_hessian(
             P(x4), BF16, t4, c4, 1, None, None, 0, P(H4), 0, P(ws4), ws4_n, sptr), "hessian"))
-        stage("scale_proj", lambda: ok(L.nvfp4_global_scale(P(w4), BF16, 1, r4 * c4, P(S4), sptr), "scale"))
+        stage("scale_proj", lambda: ok(L.nvfp4_global_scale_ws(P(w4), BF16, 1, r4 * c4, P(S4), P(wsS), wsS_n, sptr), "scale"))
         stage("lh_proj", lambda: ok(L.nvfp4_scale_search_local_hessian(
             P(w4), BF16, 1, r4, c4, P(S4), P(H4), P(sc4), None, sptr), "lh"))
         stage("quantize_proj", lambda: ok(L.nvfp4_quantize(
@@ -278,14 +282,14 @@ def main():
         stage("hessian_moe", lambda: ok(L.nvfp4_block_hessian(
             P(x5), BF16, t5, c5, E, P(off5), P(tok5), t5 * topk, P(H5), 0, P(ws5), ws5_n, sptr),
             "hessian"))
-        stage("scale_moe", lambda: ok(L.nvfp4_global_scale(P(w5), BF16, E, r5 * c5, P(S5), sptr), "scale"))
+        stage("scale_moe", lambda: ok(L.nvfp4_global_scale_ws(P(w5), BF16, E, r5 * c5, P(S5), P(wsS), wsS_n, sptr), "scale"))
         stage("lh_moe", lambda: ok(L.nvfp4_scale_search_local_hessian(
             P(w5), BF16, E, r5, c5, P(S5), P(H5), P(sc5), None, sptr), "lh"))
         stage("quantize_moe", lambda: ok(L.nvfp4_quantize(
             P(w5), BF16, E, r5, c5, P(S5), P(sc5), P(codes5), None, sptr), "quantize"))
 
         def tiny_all():
-            ok(L.nvfp4_global_scale(P(w1), F32, 1, r1 * c1, P(S1), sptr), "scale")
+            ok(L.nvfp4_global_scale_ws(P(w1), F32, 1, r1 * c1, P(S1), P(wsS), wsS_n, sptr), "scale")
             ok(L.nvfp4_fakequant(P(w1), F32, 1, r1, c1, P(S1), None, P(y1), P(codes1), P(sc1), sptr),
                "fakequant")
             ok(L.nvfp4_scale_search_mse(P(w1), F32, 1, r1, c1, P(S1), P(sc1m), None, sptr), "mse")

@@ -86,6 +86,17 @@ NVFP4_API int nvfp4_global_scale(const void *x, int dtype, int64_t batch, int64_
                        void *stream);
 
 /*
+ * The same S in two launches instead of three, with a caller workspace of at least
+ * nvfp4_global_scale_workspace_size(batch, n) bytes, 4-byte aligned, that receives one
+ * partial maximum per workgroup (no initialisation needed; its contents after the call are
+ * unspecified). Calls that share a workspace must not overlap. Same arguments and errors as
+ * nvfp4_global_scale, plus NVFP4_ERR_WORKSPACE.
+ */
+NVFP4_API size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t n);
+NVFP4_API int nvfp4_global_scale_ws(const void *x, int dtype, int64_t batch, int64_t n, float *S,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Max scaling ([QAD] 2.3, [LH] default selector): block byte = E4M3 nearest to
  * amax_b / (6 S[b]). w: [batch][rows][cols]; S: [batch]; scales: [batch][rows][cols/16].
  */

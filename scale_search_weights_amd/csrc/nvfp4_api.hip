@@ -93,16 +93,47 @@ const char *nvfp4_status_string(int status) {
 
 int nvfp4_version(void) { return 100; }
 
-int nvfp4_global_scale(const void *x, int dtype, int64_t batch, int64_t n, float *S, void *stream) {
+static int check_global_scale(const void *x, int dtype, int64_t batch, int64_t n, float *S,
+                              bool *empty) {
+  *empty = false;
   if (dtype != NVFP4_DTYPE_F32 && dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
   if (batch < 0 || n < 0 || (n % 8) != 0 || batch > kMaxGridY) return NVFP4_ERR_SHAPE;
   int64_t tot, bytes;
   if (!mul_ok(batch, n, &tot) || !mul_ok(tot, 4, &bytes)) return NVFP4_ERR_SHAPE;
-  if (batch == 0) return NVFP4_OK;
+  if (batch == 0) {
+    *empty = true;
+    return NVFP4_OK;
+  }
   if (!S || (n > 0 && !x)) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(S, 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+int nvfp4_global_scale(const void *x, int dtype, int64_t batch, int64_t n, float *S, void *stream) {
+  bool empty;
+  const int rc = check_global_scale(x, dtype, batch, n, S, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
   debug_check_finite(x, dtype, batch * n, as_stream(stream));
   return launch_global_scale(x, dtype, batch, n, S, as_stream(stream));
+}
+
+size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t n) {
+  int64_t tot, bytes;
+  if (batch <= 0 || n < 0 || (n % 8) != 0 || batch > kMaxGridY) return 0;
+  if (!mul_ok(batch, n, &tot) || !mul_ok(tot, 4, &bytes)) return 0;
+  return scale_workspace_size(batch, n);
+}
+
+int nvfp4_global_scale_ws(const void *x, int dtype, int64_t batch, int64_t n, float *S,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  bool empty;
+  const int rc = check_global_scale(x, dtype, batch, n, S, &empty);
+  if (rc != NVFP4_OK || empty) return rc;
+  if (!workspace || workspace_bytes < nvfp4_global_scale_workspace_size(batch, n))
+    return NVFP4_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return NVFP4_ERR_ALIGN;
+  debug_check_finite(x, dtype, batch * n, as_stream(stream));
+  return launch_global_scale_ws(x, dtype, batch, n, S, workspace, as_stream(stream));
 }
 
 int nvfp4_scale_search_max(const void *w, int dtype, int64_t batch, int64_t rows, int64_t cols,

@@ -12,6 +12,9 @@ namespace nvfp4 {
 
 int launch_global_scale(const void *x, int dtype, int64_t batch, int64_t n, float *S,
                         hipStream_t st);
+size_t scale_workspace_size(int64_t batch, int64_t n);
+int launch_global_scale_ws(const void *x, int dtype, int64_t batch, int64_t n, float *S,
+                             void *workspace, hipStream_t st);
 int launch_quant(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
                  const float *S, const uint8_t *scales_in, uint8_t *codes, uint8_t *scales_out,
                  void *y, hipStream_t st);

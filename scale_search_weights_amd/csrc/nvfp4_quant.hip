@@ -115,6 +115,87 @@ int launch_global_scale(const void *x, int dtype, int64_t batch, int64_t n, floa
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+// Workspace form: the amax pass writes each workgroup's maximum to its own slot (plain
+// stores, no atomics, no initialisation), and one workgroup per batch entry reduces the
+// slots and writes S (the launch boundary makes the slots visible). Two launches instead of
+// three, and about 512 workgroups with sixteen 16-byte loads in flight per lane instead of
+// 256 with four (the single-word atomicMax form must keep its same-address atomics few;
+// 512 x 16 was the fastest of 512..4096 workgroups x 4..16 loads on the 4096x4096 and
+// 12288x4096 weights, within 8% of the best on the 128-expert stack).
+static inline int64_t scale_ws_wgs(int64_t batch, int64_t n) {
+  const int64_t nvec = n / 8, per = 256 * 16;  // vectors a workgroup takes per round
+  int64_t g = (nvec + per - 1) / per;
+  int64_t cap = 512 / (batch > 0 ? batch : 1);  // about 512 workgroups in all
+  if (cap < 2) cap = 2;
+  if (g > cap) g = cap;
+  return g < 1 ? 1 : g;
+}
+
+// workspace: one uint32 slot per workgroup, [batch][G]
+size_t scale_workspace_size(int64_t batch, int64_t n) {
+  return (size_t)4 * (size_t)batch * (size_t)scale_ws_wgs(batch, n);
+}
+
+__device__ __forceinline__ unsigned wg_max256(unsigned m, unsigned *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256)
+    k_scale_slots(const void *__restrict__ x, int64_t n, int64_t G, unsigned *__restrict__ slot) {
+  __shared__ unsigned red[4];
+  const int64_t batch = blockIdx.y, wg = blockIdx.x;
+  const int64_t nvec = n / 8, stride = G * 256, base = batch * n;
+  unsigned m = 0u;
+  int64_t v = wg * 256 + threadIdx.x;
+  for (; v + 15 * stride < nvec; v += 16 * stride) {
+    unsigned a[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a[k] = vec_amax_bits<DT>(x, base + (v + k * stride) * 8);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = max(m, a[k]);
+  }
+  for (; v < nvec; v += stride) m = max(m, vec_amax_bits<DT>(x, base + v * 8));
+  m = wg_max256(m, red);
+  if (threadIdx.x == 0) slot[batch * G + wg] = m;
+}
+
+// one workgroup per batch entry: the maximum of its slots, then S as in k_scale_finalize
+__global__ void __launch_bounds__(256)
+    k_scale_slots_finalize(const unsigned *__restrict__ slot, int64_t G, float *__restrict__ S) {
+  __shared__ unsigned red[4];
+  const int64_t batch = blockIdx.x;
+  unsigned m = 0u;
+  for (int64_t i = threadIdx.x; i < G; i += 256) m = max(m, slot[batch * G + i]);
+  m = wg_max256(m, red);
+  if (threadIdx.x == 0) {
+    const float amax = __uint_as_float(m);
+    float s = 1.0f;
+    if (amax != 0.0f) {
+      s = __fdiv_rn(amax, 2688.0f);
+      if (s < 1.17549435e-38f) s = 1.17549435e-38f;
+    }
+    S[batch] = s;
+  }
+}
+
+int launch_global_scale_ws(const void *x, int dtype, int64_t batch, int64_t n, float *S,
+                           void *workspace, hipStream_t st) {
+  const int64_t G = scale_ws_wgs(batch, n);
+  unsigned *slot = static_cast<unsigned *>(workspace);
+  const dim3 g((unsigned)G, (unsigned)batch), b(256);
+  if (dtype == NVFP4_DTYPE_BF16)
+    hipLaunchKernelGGL(k_scale_slots<NVFP4_DTYPE_BF16>, g, b, 0, st, x, n, G, slot);
+  else
+    hipLaunchKernelGGL(k_scale_slots<NVFP4_DTYPE_F32>, g, b, 0, st, x, n, G, slot);
+  hipLaunchKernelGGL(k_scale_slots_finalize, dim3((unsigned)batch), b, 0, st, slot, G, S);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 // ------------------------------------------------------------------ block load / store
 
 template <int DT>
@@ -235,12 +316,15 @@ __global__ void __launch_bounds__(256)
   const int64_t off = (int64_t)blockIdx.y * n_half;  // the entry's first half block
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t l0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // the first load (clamped to a valid index) is in flight while the table is built
-  const Raw8 first = load_raw8<DT>(x, off + (l0 < n_half ? l0 : n_half - 1));
+  // the first loads (clamped to a valid index), values and a given byte, are in flight
+  // while the table is built
+  const int64_t hb0 = off + (l0 < n_half ? l0 : n_half - 1);
+  const Raw8 first = load_raw8<DT>(x, hb0);
+  const int first_given = (FLAGS & F_SCALES_IN) ? (int)scales_in[hb0 >> 1] : 0;
   __shared__ Cand tab[127];
   build_cands(tab, S);
   lds_barrier();
-  auto block = [&](int64_t hb, const Raw8 &raw) {
+  auto block = [&](int64_t hb, const Raw8 &raw, int given) {
     const int64_t blk = hb >> 1;
     float v[8];
     unpack_raw8<DT>(raw, v);
@@ -250,7 +334,7 @@ __global__ void __launch_bounds__(256)
     // the two lanes of a block are lanes 2k and 2k+1 (both active): DPP quad_perm [1,0,3,2]
     amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1,
                                                                    0xF, 0xF, false)));
-    const int byte = (FLAGS & F_SCALES_IN) ? given_byte(scales_in[blk])
+    const int byte = (FLAGS & F_SCALES_IN) ? given_byte(given)
                                            : max_scale_byte_fast(amax, tab[0].rlo, tab[0].rhi, S);
     unsigned c = 0u;
     float s = 0.0f;
@@ -286,8 +370,10 @@ __global__ void __launch_bounds__(256)
       }
     }
   };
-  if (l0 < n_half) block(off + l0, first);
-  for (int64_t l = l0 + stride; l < n_half; l += stride) block(off + l, load_raw8<DT>(x, off + l));
+  if (l0 < n_half) block(off + l0, first, first_given);
+  for (int64_t l = l0 + stride; l < n_half; l += stride)
+    block(off + l, load_raw8<DT>(x, off + l),
+          (FLAGS & F_SCALES_IN) ? (int)scales_in[(off + l) >> 1] : 0);
 }
 
 static unsigned grid_for(int64_t n) {

@@ -40,6 +40,15 @@ int main() {
   EXPECT(nvfp4_global_scale(Fc + 2, 1, 1, 16, (float *)F, nullptr), NVFP4_ERR_ALIGN);
   EXPECT(nvfp4_global_scale(F, 1, 1, 16, nullptr, nullptr), NVFP4_ERR_NULL);
   EXPECT(nvfp4_global_scale(nullptr, 1, 0, 16, nullptr, nullptr), NVFP4_OK);
+  {
+    const size_t need = nvfp4_global_scale_workspace_size(1, 1 << 20);
+    EXPECT(nvfp4_global_scale_ws(F, 1, 1, 12, (float *)F, F, need, nullptr), NVFP4_ERR_SHAPE);
+    EXPECT(nvfp4_global_scale_ws(F, 1, big, big, (float *)F, F, need, nullptr), NVFP4_ERR_SHAPE);
+    EXPECT(nvfp4_global_scale_ws(F, 1, 1, 1 << 20, (float *)F, nullptr, need, nullptr), NVFP4_ERR_WORKSPACE);
+    EXPECT(nvfp4_global_scale_ws(F, 1, 1, 1 << 20, (float *)F, F, need - 1, nullptr), NVFP4_ERR_WORKSPACE);
+    EXPECT(nvfp4_global_scale_ws(F, 1, 1, 1 << 20, (float *)F, Fc + 2, need, nullptr), NVFP4_ERR_ALIGN);
+    EXPECT(nvfp4_global_scale_ws(nullptr, 1, 0, 16, nullptr, nullptr, 0, nullptr), NVFP4_OK);
+  }
 
   // searches and quantisation: shapes, dtypes, nulls, alignment, overflow, empty tensors
   const int64_t shapes[][3] = {{1, 4, 17}, {neg, 4, 16}, {1, neg, 16}, {1, 4, neg},
@@ -99,6 +108,7 @@ int main() {
       (void)nvfp4_route_groups_workspace_size(a, 8, b);
       (void)nvfp4_gptq_workspace_size(a, b);
       (void)nvfp4_gptq_factor_workspace_size(b);
+      (void)nvfp4_global_scale_workspace_size(a, b);
     }
 
   // block Hessian (workspace and allocation-free forms)

@@ -18,7 +18,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = nvfp4.declared_symbols()
-    assert len(names) == 28
+    assert len(names) == 30
     for n in names:
         assert hasattr(L, n), n
     assert L.nvfp4_version() == 100
@@ -61,6 +61,23 @@ def test_empty_tensors_return_ok_without_launch(L):
     assert L.nvfp4_global_scale(None, 1, 0, 16, None, None) == OK
     assert L.nvfp4_quantize(None, 1, 1, 0, 16, None, None, None, None, None) == OK
     assert L.nvfp4_dequantize(None, None, None, 1, 0, 16, None, 1, None) == OK
+
+
+def test_global_scale_workspace_checks(L):
+    f = L.nvfp4_global_scale_ws
+    need = L.nvfp4_global_scale_workspace_size(1, 4096 * 4096)
+    assert need > 0
+    assert L.nvfp4_global_scale_workspace_size(1, 12) == 0        # n % 8
+    assert L.nvfp4_global_scale_workspace_size(0, 16) == 0        # nothing to do
+    assert L.nvfp4_global_scale_workspace_size(-1, 16) == 0
+    assert L.nvfp4_global_scale_workspace_size(1 << 40, 1 << 40) == 0
+    assert f(P(FAKE), 1, 1, 12, P(FAKE), P(FAKE), need, None) == ESHAPE
+    assert f(P(FAKE), 9, 1, 16, P(FAKE), P(FAKE), need, None) == EDTYPE
+    assert f(P(FAKE), 1, 1, 4096 * 4096, P(FAKE), None, need, None) == EWS
+    assert f(P(FAKE), 1, 1, 4096 * 4096, P(FAKE), P(FAKE), need - 1, None) == EWS
+    assert f(P(FAKE), 1, 1, 4096 * 4096, P(FAKE), P(FAKE + 2), need, None) == EALIGN
+    assert f(P(FAKE), 1, 1, 4096 * 4096, None, P(FAKE), need, None) == ENULL
+    assert f(None, 1, 0, 16, None, None, 0, None) == OK             # empty: no launch
 
 
 def test_each_entry_point_validates(L):

@@ -76,6 +76,30 @@ def test_global_scale(orc, tiny):
         assert S[b] == orc.tensor_scale(f32(e[b])), b
 
 
+def test_global_scale_workspace_form(orc, tiny):
+    """The workspace form against the oracle, one workspace reused across calls of
+    different sizes and first filled with 0xFF (its contents must not matter): 1024
+    workgroups, a ragged last round, a batch of experts with an all-zero entry, and the
+    maximum in the very last vector of the tensor."""
+    ws = torch.full((1 << 20,), 0xFF, dtype=torch.uint8, device=DEV)
+    w, _ = tiny
+    case("global_scale_ws tiny fp32")
+    assert nvfp4.global_scale(w.to(DEV), workspace=ws).item() == orc.tensor_scale(w.numpy())
+    for rows, cols, seed in ((8192, 4096, 1), (1000, 1040, 2), (4096, 4096, 3), (3, 16, 4)):
+        case(f"global_scale_ws activation bf16 {rows}x{cols}")
+        a = synth.activation(seed, rows, cols)
+        if seed == 3:
+            a[-1, -1] = 1e4  # the largest value in the last vector
+        assert nvfp4.global_scale_workspace_size(1, rows * cols) <= ws.numel()
+        assert nvfp4.global_scale(a.to(DEV), workspace=ws).item() == orc.tensor_scale(f32(a))
+    case("global_scale_ws batch of 7 experts, one all-zero")
+    e = synth.moe(3, experts=7, rows=512, cols=256, tokens=16, topk=2)[0]
+    e[5] *= 0
+    S = nvfp4.global_scale(e.to(DEV), workspace=ws).cpu().numpy()
+    for b in range(7):
+        assert S[b] == orc.tensor_scale(f32(e[b])), b
+
+
 # ------------------------------------------------------------------ max scaling / fake-quant
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
