@@ -77,7 +77,11 @@ def load_traffic(kernel_key: str, source_file: str):
 COUNTER_SOURCES = {
     "fakequant_act": "scale_search_weights_amd/csrc/nvfp4_quant.hip",
     "scale_mlp": "scale_search_weights_amd/csrc/nvfp4_quant.hip",
+    "scale_proj": "scale_search_weights_amd/csrc/nvfp4_quant.hip",
+    "scale_moe": "scale_search_weights_amd/csrc/nvfp4_quant.hip",
     "quantize_mlp": "scale_search_weights_amd/csrc/nvfp4_quant.hip",
+    "quantize_proj": "scale_search_weights_amd/csrc/nvfp4_quant.hip",
+    "quantize_moe": "scale_search_weights_amd/csrc/nvfp4_quant.hip",
     "mse_mlp": "scale_search_weights_amd/csrc/nvfp4_search.hip",
     "four_over_six_mlp": "scale_search_weights_amd/csrc/nvfp4_search.hip",
     "lh_proj": "scale_search_weights_amd/csrc/nvfp4_search.hip",
