@@ -603,12 +603,30 @@ int64_t oracle_gptq_factor(const double *H, int64_t n, double damp, double *U)
     return rc;
 }
 
+/* The other rounding of v at a near-tie: the grid neighbour of `code` on the side of |v|
+ * (a value within a hair of a midpoint may round either way once the sums that made it are
+ * reordered). Same sign as v; a zero magnitude carries none (R6); saturated codes and an
+ * all-zero block keep their code. */
+static int oracle_other_rounding(double v, int code, int byte, float S)
+{
+    if (byte == 0) return code;
+    double sS = oracle_e4m3_value(byte) * (double)S;
+    double ax = fabs(v), g = E2M1_MAG[code & 7] * sS;
+    int k = code & 7, alt = k;
+    if (ax > g && k < 7) alt = k + 1;
+    else if (ax < g && k > 0) alt = k - 1;
+    return alt == 0 ? 0 : (alt | (v < 0 ? 8 : 0));
+}
+
 /* GPTQ's column loop for each row (rows are independent): v = w; for j = 0..n-1 the code
  * of v_j is taken at the block's byte and S, e = (v_j - q_j) / U_jj with q_j the exact
  * dequantised value, and v_k -= e U_jk for every k > j. codes use the packed layout;
- * vout (optional) receives each v_j as it was rounded. */
-void oracle_gptq_rows(const float *w, int64_t rows, int64_t n, float S, const uint8_t *scales,
-                      const double *U, uint8_t *codes, double *vout)
+ * vout (optional) receives each v_j as it was rounded. flips (optional, [rows][nflip],
+ * -1 = unused) names columns where the row takes the other rounding instead (test use:
+ * following a row past a near-tie that was resolved the other way). */
+void oracle_gptq_rows_flip(const float *w, int64_t rows, int64_t n, float S,
+                           const uint8_t *scales, const double *U, uint8_t *codes, double *vout,
+                           const int64_t *flips, int64_t nflip)
 {
     int64_t nb = n / 16;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -618,6 +636,9 @@ void oracle_gptq_rows(const float *w, int64_t rows, int64_t n, float S, const ui
         for (int64_t j = 0; j < n; ++j) {
             int byte = given_byte(scales[r * nb + j / 16]);
             int code = oracle_e2m1_code_d(v[j], byte, S);
+            if (flips)
+                for (int64_t f = 0; f < nflip; ++f)
+                    if (flips[r * nflip + f] == j) code = oracle_other_rounding(v[j], code, byte, S);
             if (vout) vout[r * n + j] = v[j];
             double q = E2M1_MAG[code & 7] * oracle_e4m3_value(byte) * (double)S; /* exact */
             if (code & 8) q = -q;
@@ -629,4 +650,10 @@ void oracle_gptq_rows(const float *w, int64_t rows, int64_t n, float S, const ui
         }
         free(v);
     }
+}
+
+void oracle_gptq_rows(const float *w, int64_t rows, int64_t n, float S, const uint8_t *scales,
+                      const double *U, uint8_t *codes, double *vout)
+{
+    oracle_gptq_rows_flip(w, rows, n, S, scales, U, codes, vout, NULL, 0);
 }

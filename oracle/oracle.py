@@ -95,6 +95,8 @@ def lib():
         L.oracle_gptq_factor.argtypes = [P, i64, ctypes.c_double, P]
         L.oracle_gptq_rows.restype = None
         L.oracle_gptq_rows.argtypes = [P, i64, i64, f32, P, P, P, P]
+        L.oracle_gptq_rows_flip.restype = None
+        L.oracle_gptq_rows_flip.argtypes = [P, i64, i64, f32, P, P, P, P, P, i64]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_set_num_threads.restype = None
@@ -324,9 +326,11 @@ def gptq_factor(H, damp: float = 0.01) -> np.ndarray:
     return U
 
 
-def gptq(w, S, scales, H=None, damp: float = 0.01, U=None, return_v: bool = False):
+def gptq(w, S, scales, H=None, damp: float = 0.01, U=None, return_v: bool = False, flips=None):
     """GPTQ codes [rows, cols/2] of w at the given block bytes and S (and the values each
-    column was rounded from, if asked). Pass U from gptq_factor to reuse it."""
+    column was rounded from, if asked). Pass U from gptq_factor to reuse it. flips
+    ([rows, k] int, -1 = unused): columns where a row takes the other rounding (the grid
+    neighbour across the nearer midpoint) instead of the nearest."""
     a = _f32(w)
     rows, cols = a.shape
     if U is None:
@@ -334,6 +338,13 @@ def gptq(w, S, scales, H=None, damp: float = 0.01, U=None, return_v: bool = Fals
     sc = np.ascontiguousarray(scales, dtype=np.uint8)
     codes = np.empty((rows, cols // 2), dtype=np.uint8)
     v = np.empty((rows, cols), dtype=np.float64) if return_v else None
-    lib().oracle_gptq_rows(_p(a), rows, cols, float(np.float32(S)), _p(sc),
-                           _p(np.ascontiguousarray(U)), _p(codes), _p(v) if return_v else None)
+    Uc = np.ascontiguousarray(U)
+    if flips is None:
+        lib().oracle_gptq_rows(_p(a), rows, cols, float(np.float32(S)), _p(sc), _p(Uc), _p(codes),
+                               _p(v) if return_v else None)
+    else:
+        fl = np.ascontiguousarray(flips, dtype=np.int64)
+        assert fl.ndim == 2 and fl.shape[0] == rows
+        lib().oracle_gptq_rows_flip(_p(a), rows, cols, float(np.float32(S)), _p(sc), _p(Uc),
+                                    _p(codes), _p(v) if return_v else None, _p(fl), fl.shape[1])
     return (codes, v) if return_v else codes

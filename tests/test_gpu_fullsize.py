@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from gptq_check import check_rows
 from scale_search_weights_amd import nvfp4, synth
 
 pytestmark = pytest.mark.gpu
@@ -185,14 +186,8 @@ def test_projection_full_hessian_and_gptq(orc):
     codes = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV),
                        torch.from_numpy(Ur).to(DEV)).cpu().numpy()
     rows = np.concatenate([[0, 4095], rng.choice(np.arange(1, 4095), 30, replace=False)])
-    want, v_ref = orc.gptq(wn[rows], S, sc[rows], U=Ur, return_v=True)
-    g = np.stack([codes[rows] & 15, codes[rows] >> 4], -1).reshape(len(rows), -1)
-    r_ = np.stack([want & 15, want >> 4], -1).reshape(len(rows), -1)
-    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
-    for i in np.flatnonzero((g != r_).any(axis=1)):
-        j = int(np.flatnonzero(g[i] != r_[i])[0])
-        sS = orc.e4m3_value(int(sc[rows[i], j // 16])) * float(S)
-        assert np.min(np.abs(abs(v_ref[i, j]) - mids * sS)) <= 1e-9 * sS, (rows[i], j)
+    ties = check_rows(codes[rows], wn[rows], S, sc[rows], Ur, orc, tie_tol=1e-9)
+    print(f"[info] near-ties followed: {ties}", flush=True)
 
 
 def test_moe_routing_hessian_local_hessian_full(orc):

@@ -4,20 +4,20 @@ the CPU oracle.
 Bar: H within 1e-4 relative Frobenius error per 16x16 block (fp32 accumulation against the
 oracle's fp64 sums), exactly symmetric and bitwise reproducible; the factor U within 1e-8
 of the oracle's (both in double; relative to max |U|); GPTQ codes identical to the oracle's
-when both start from the same fp32 H. Codes are decided on double-precision values whose
-last bits depend on summation order, so a row may differ from some column on only if the
-oracle's value there lies within 1e-9 (relative to the block scale) of a rounding midpoint;
-the end-to-end case (GPU H against the oracle's fp64 H) allows 1e-4 there.
+when both start from the same fp32 H, checked on every column of every row
+(tests/gptq_check.py): a row may take the other rounding only at a value within 1e-9 of a
+rounding midpoint (relative to the block scale), after which the oracle follows the same
+rounding; the end-to-end case (GPU H against the oracle's fp64 H) allows 1e-4 there.
 """
 import numpy as np
 import pytest
 import torch
 
+from gptq_check import check_rows
 from scale_search_weights_amd import nvfp4, synth
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 
 def case(msg):
@@ -35,24 +35,6 @@ def block_rel_frob(Hg: np.ndarray, Hr: np.ndarray) -> float:
     num = np.linalg.norm((a - b).reshape(-1, 256), axis=1)
     den = np.linalg.norm(b.reshape(-1, 256), axis=1)
     return float(np.where(den > 0, num / np.where(den > 0, den, 1), num).max())
-
-
-def unpack(codes: np.ndarray) -> np.ndarray:
-    return np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
-
-
-def check_codes(got, want, v_ref, scales, S, orc, tie_tol, max_rows_frac=0.0):
-    """Identical codes, except that a row may diverge from a column where the oracle's
-    value sits within tie_tol * s * S of a rounding midpoint."""
-    g, w = unpack(got), unpack(want)
-    bad_rows = np.flatnonzero((g != w).any(axis=1))
-    for r in bad_rows:
-        j = int(np.flatnonzero(g[r] != w[r])[0])
-        byte = int(scales[r, j // 16])
-        sS = orc.e4m3_value(byte) * float(S)
-        dist = np.min(np.abs(abs(v_ref[r, j]) - MIDS * sS)) / sS
-        assert dist <= tie_tol, f"row {r} col {j}: codes {g[r, j]} vs {w[r, j]}, {dist:.3g} from a midpoint"
-    assert len(bad_rows) <= max_rows_frac * g.shape[0], f"{len(bad_rows)} rows differ"
 
 
 # ------------------------------------------------------------------ full Gram matrix
@@ -243,10 +225,10 @@ def test_gptq_rows_same_factor(orc, which):
     H = orc.full_hessian(f32(x)).astype(np.float32)
     sc = orc.scales_local_hessian(wn, S, orc.block_hessian(f32(x)))
     Ur = orc.gptq_factor(H.astype(np.float64), 0.01)
-    want, v_ref = orc.gptq(wn, S, sc, U=Ur, return_v=True)
     got = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV),
                      torch.from_numpy(Ur).to(DEV))
-    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9)
+    ties = check_rows(got.cpu().numpy(), wn, S, sc, Ur, orc, tie_tol=1e-9)
+    print(f"[info] near-ties followed: {ties}", flush=True)
 
 
 def test_gptq_rows_wide_and_narrow_outer_updates(orc):
@@ -259,10 +241,10 @@ def test_gptq_rows_wide_and_narrow_outer_updates(orc):
     S = orc.tensor_scale(wn)
     sc = orc.scales_max(wn, S)
     Ur = orc.gptq_factor(orc.full_hessian(f32(x)).astype(np.float32).astype(np.float64), 0.01)
-    want, v_ref = orc.gptq(wn, S, sc, U=Ur, return_v=True)
     got = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV),
                      torch.from_numpy(Ur).to(DEV))
-    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9, max_rows_frac=0.002)
+    ties = check_rows(got.cpu().numpy(), wn, S, sc, Ur, orc, tie_tol=1e-9)
+    print(f"[info] near-ties followed: {ties}", flush=True)
 
 
 def test_gptq_rows_workspace_contents_unread(orc):
@@ -293,12 +275,15 @@ def test_gptq_end_to_end(orc):
     S = orc.tensor_scale(wn)
     sc = orc.scales_local_hessian(wn, S, orc.block_hessian(xn))
     Href = orc.full_hessian(xn)
-    want, v_ref = orc.gptq(wn, S, sc, Href, 0.01, return_v=True)
+    Uref = orc.gptq_factor(Href, 0.01)
     Hd = nvfp4.full_hessian(x.to(DEV))
     U, status = nvfp4.gptq_factor(Hd, 0.01)
     assert status.item() == 0
     got = nvfp4.gptq(w.to(DEV), torch.tensor([S], device=DEV), torch.from_numpy(sc).to(DEV), U)
-    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-4, max_rows_frac=0.1)
+    # the GPU's H (fp32 sums) and factor differ from the oracle's fp64 chain in the last
+    # bits, so near-ties are looser here (1e-4 s S); every column of every row is checked
+    ties = check_rows(got.cpu().numpy(), wn, S, sc, Uref, orc, tie_tol=1e-4)
+    print(f"[info] near-ties followed: {ties}", flush=True)
     # GPTQ lowers the layer-output error against plain rounding at the same bytes
     rows, cols = wn.shape
     deq = lambda c: orc.dequantize(c, sc, S, rows, cols).astype(np.float64) - wn
@@ -316,10 +301,9 @@ def test_gptq_rows_extreme_magnitudes(orc, scale):
     H = orc.full_hessian(f32(x)).astype(np.float32)
     sc = orc.scales_mse(wn, S)
     Ur = orc.gptq_factor(H.astype(np.float64), 0.01)
-    want, v_ref = orc.gptq(wn, S, sc, U=Ur, return_v=True)
     got = nvfp4.gptq(torch.from_numpy(wn).to(DEV), torch.tensor([S], device=DEV),
                      torch.from_numpy(sc).to(DEV), torch.from_numpy(Ur).to(DEV))
-    check_codes(got.cpu().numpy(), want, v_ref, sc, S, orc, tie_tol=1e-9)
+    check_rows(got.cpu().numpy(), wn, S, sc, Ur, orc, tie_tol=1e-9)
 
 
 def test_full_hessian_smallest_shapes(orc):

@@ -87,6 +87,53 @@ def test_diagonal_or_zero_hessian_is_plain_rounding(orc):
     assert not orc.gptq(zero, S, sc, orc.full_hessian(X)).any()
 
 
+def test_flip_takes_the_other_grid_neighbour(orc):
+    """The flip option (used to follow a row past a near-tie resolved the other way): with a
+    diagonal H there is no error feedback, so flipping column j changes only code j, to the
+    grid neighbour on the side of |w_j| (one magnitude step, same sign, no signed zero);
+    with a full H the columns before j are untouched and column j is that neighbour of the
+    value it was rounded from. Saturated codes (|w| beyond 6 sS) keep their code."""
+    w, X = _problem(9, rows=8, cols=64)
+    S = orc.tensor_scale(w)
+    sc = orc.scales_max(w, S)
+    D = np.diag(np.random.default_rng(9).uniform(0.5, 3.0, 64))
+    U = orc.gptq_factor(D, 0.01)
+    plain = _unpack(orc.gptq(w, S, sc, U=U))
+    for j in (0, 5, 31, 63):
+        fl = np.full((8, 2), -1, np.int64)
+        fl[:, 0] = j
+        got = _unpack(orc.gptq(w, S, sc, U=U, flips=fl))
+        others = np.delete(np.arange(64), j)
+        assert np.array_equal(got[:, others], plain[:, others])
+        for r in range(8):
+            sS = orc.e4m3_value(int(sc[r, j // 16])) * float(S)
+            k0, k1 = plain[r, j] & 7, got[r, j] & 7
+            a, g0 = abs(float(w[r, j])), [0, .5, 1, 1.5, 2, 3, 4, 6][k0] * sS
+            if a > g0 and k0 < 7:
+                assert k1 == k0 + 1
+            elif a < g0:
+                assert k1 == k0 - 1
+            else:
+                assert k1 == k0
+            if k1:
+                assert (got[r, j] >> 3) == (1 if w[r, j] < 0 else 0)
+            else:
+                assert got[r, j] == 0
+    H = orc.full_hessian(X)
+    U = orc.gptq_factor(H, 0.01)
+    base, v = orc.gptq(w, S, sc, U=U, return_v=True)
+    base = _unpack(base)
+    fl = np.full((8, 1), 20, np.int64)
+    got, v2 = orc.gptq(w, S, sc, U=U, return_v=True, flips=fl)
+    got = _unpack(got)
+    assert np.array_equal(got[:, :20], base[:, :20]) and np.array_equal(v2[:, :21], v[:, :21])
+    assert (got[:, 20] != base[:, 20]).any()
+
+
+def _unpack(c):
+    return np.stack([c & 15, c >> 4], -1).reshape(c.shape[0], -1)
+
+
 def test_two_column_update_closed_form(orc):
     """Column 2 is rounded from w2 + (w1 - q1) H12 / H22 (damped H)."""
     rng = np.random.default_rng(6)
