@@ -16,7 +16,10 @@
 //    K ordering the hardware uses pairs the same token on both sides;
 //  * partial sums per (token chunk, block) go to the workspace and a second kernel adds
 //    them in ascending chunk order, so results are deterministic without atomics.
-// bf16 x bf16 products are exact in fp32; only the accumulation rounds.
+// The grouped form in bf16 (per-expert H from routed token lists) normally runs its own
+// kernels, k_hess_plan and k_hess_grouped (below), which serve the rows the experts share
+// from L2; k_hess_bf16's gathered form remains for inputs too large for their 32-bit
+// offsets. bf16 x bf16 products are exact in fp32; only the accumulation rounds.
 #include <utility>
 
 #include "nvfp4_internal.h"
@@ -407,11 +410,13 @@ __global__ void __launch_bounds__(256)
 }
 
 // One workgroup per (64-channel chunk, piece group): wave w owns block w of the chunk and one
-// 16x16 accumulator per piece of the group. The workgroup walks window after window; in
-// each window it takes, piece by piece, the piece's positions that fall in the window (its
-// next 1/NW, rounded to whole 32-token steps). Workgroups are numbered so that one XCD runs all the piece groups of its chunks:
-// they walk the token range in step, so a token row's chunk segment is read from memory once
-// and served to its other experts from that XCD's L2.
+// 16x16 accumulator per piece of the group (one live, swapped in registers when the piece
+// changes). The workgroup walks window after window; in each window it takes, piece by
+// piece, the piece's positions that fall in the window (its next 1/NW, rounded to whole
+// 32-token steps; a segment table in LDS holds each window's share of each piece).
+// Workgroups are numbered so that one XCD runs all the piece groups of its chunks: they walk
+// the token range in step, so a token row's chunk segment is read from memory once and
+// served to its other experts from that XCD's L2.
 //
 // Loads go straight into LDS (raw buffer loads with an LDS destination, no registers), so
 // several steps are in flight without the register moves that would make the compiler wait

@@ -275,8 +275,12 @@ int launch_four_over_six(const void *w, int dtype, int64_t batch, int64_t rows, 
 
 // ------------------------------------------------------------------ Local-Hessian
 //
-// Grid: x = chunks of 64 rows, y = block column b, z = batch entry. All rows of block
-// column b share H_b (the block-diagonal approximation), held in LDS as doubles.
+// Grid: x = groups of up to 8 tiles of 64 rows, y = block column b, z = batch entry. All
+// rows of block column b share H_b (the block-diagonal approximation), held in LDS as
+// doubles. A workgroup first stages its rows' blocks in LDS (one thread per row, with the
+// block max, the first index of the max and the candidate window) and sorts the rows by
+// window length, so that the 16 pairs of a wave step through windows of about the same
+// length; it then takes its rows 64 at a time in that order.
 //
 // The chosen byte and its objective equal those of the definition evaluated exactly as it
 // is written (fp64, ascending indices, one fma per term), bit for bit. Only candidates that
@@ -299,8 +303,9 @@ int launch_four_over_six(const void *w, int dtype, int64_t batch, int64_t rows, 
 // adds; t = 2^-138 (1 + amax) covers roundings in the denormal range (the fp32 MFMA keeps
 // denormals). A <= (sum |d_i| a_i)^2 with a_i^2 >= max_j max(|H_ij|, |H_ji|); when every
 // g_i > 0 (below), also A <= kappa d H d^T, so for kappa <= 1e4 the bound is relative to the
-// objective. Per pair the kernel keeps theta = min(obj + err) and the three smallest
-// (obj - err): every candidate that can still be the exact argmin has obj - err <= theta.
+// objective. Each lane keeps theta = min(obj + err) and the three smallest (obj - err) of
+// the candidates it scored (a candidate is scored by one lane of its pair); every
+// candidate that can still be the exact argmin has obj - err <= theta (the pair's theta).
 // If at most two do, they are re-evaluated in the exact fp64 order (split over the pair's
 // four lanes) and the smaller wins; if three or more do, or values are too small or large
 // for the fast path or for fp32, the pair is rescanned exactly. The downward pruning
