@@ -465,6 +465,12 @@ def main():
     for key, ent in load_counters().items():
         if key in rooflines:
             rooflines[key]["counters"] = ent
+            evals = rooflines[key].get("evaluations")
+            if evals and ent.get("valu_instructions"):
+                # lane-ops per (element, candidate) actually issued, against the evaluation
+                # cost model's MSE_OPS_PER_EVAL (wave instructions x 64 lanes / 16 elements)
+                rooflines[key]["valu_lane_ops_per_element_candidate"] = round(
+                    ent["valu_instructions"] * 64 / (evals * 16), 2)
 
     out = {
         "metric": "NVFP4 fake-quant GB/s + Local-Hessian blocks/s, % of MI355X roofline",
