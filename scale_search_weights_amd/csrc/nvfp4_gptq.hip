@@ -457,60 +457,67 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-__device__ __forceinline__ double quad_bcast(double x, int src) {
-  // value of lane `src` of this lane's quad; src is a compile-time constant at every call
+// value of lane `src` (0 or 1, a compile-time constant at every call) of this lane's pair
+__device__ __forceinline__ double pair_bcast(double x, int src) {
   int lo = __double2loint(x), hi = __double2hiint(x);
-  switch (src) {
-    case 0:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x00, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x00, 0xF, 0xF, false);
-      break;
-    case 1:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0x55, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0x55, 0xF, 0xF, false);
-      break;
-    case 2:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0xAA, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0xAA, 0xF, 0xF, false);
-      break;
-    default:
-      lo = __builtin_amdgcn_mov_dpp(lo, 0xFF, 0xF, 0xF, false);
-      hi = __builtin_amdgcn_mov_dpp(hi, 0xFF, 0xF, 0xF, false);
-      break;
+  if (src == 0) {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0xA0, 0xF, 0xF, false);  // quad_perm [0,0,2,2]
+    hi = __builtin_amdgcn_mov_dpp(hi, 0xA0, 0xF, 0xF, false);
+  } else {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0xF5, 0xF, 0xF, false);  // quad_perm [1,1,3,3]
+    hi = __builtin_amdgcn_mov_dpp(hi, 0xF5, 0xF, 0xF, false);
   }
   return __hiloint2double(hi, lo);
 }
 
-// Step k of the blocked Cholesky factorisation. Workgroups of four waves: wave 0 of every
+// Waits (s_sleep between reads) until the LDS word at f is above j. The read and its wait
+// are in one asm block, and the loop stays out of the compiler's view, so the unrolled column
+// loop around it remains one straight-line block (a loop inside it spilled to scratch).
+__device__ __forceinline__ void lds_wait_above(int *f, int j) {
+  int seen, tmp;
+  const unsigned addr = (unsigned)(uintptr_t)f;
+  asm volatile(
+      "1:\n\t"
+      "ds_read_b32 %1, %2\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_readfirstlane_b32 %0, %1\n\t"
+      "s_cmp_gt_i32 %0, %3\n\t"
+      "s_cbranch_scc1 2f\n\t"
+      "s_sleep 1\n\t"
+      "s_branch 1b\n\t"
+      "2:"
+      : "=&s"(seen), "=&v"(tmp)
+      : "v"(addr), "s"(j)
+      : "scc", "memory");
+}
+
+// Step k of the blocked Cholesky factorisation. Workgroups of three waves. Wave 0 of every
 // workgroup factors diagonal block k (lane i holds row i in registers; the pivot comes by
-// readlane and each scaled column is broadcast through LDS); workgroup 0 stores it, and
-// workgroup b >= 1 then solves the 64 rows of panel block k + b, x L_kk^T = a, by forward
-// substitution: four lanes per row, 16 columns each, x_j broadcast in the quad by DPP.
+// readlane, and each scaled column goes to LDS), and publishes column j by setting an LDS
+// counter to j + 1 once the column and 1 / L_jj are written. Workgroup 0 stores L_kk;
+// in workgroup b >= 1, waves 1 and 2 meanwhile solve the 64 rows of panel block k + b,
+// x L_kk^T = a, by forward substitution, one column behind the factorisation: two lanes per
+// row, 32 columns each, x_j shared in the pair by DPP. Every element sees the same fma
+// sequence as in a solve after the factorisation. The waits end: wave 0 runs all 64 columns
+// unconditionally (a bad pivot only sets the status), and waits only on itself. LDS
+// operations of one wave are performed in order, so a panel wave that reads the counter
+// above j then reads column j and 1 / L_jj as written.
 // L_kk goes to the same place in X, not back into A: with more workgroups than fit on the
 // device at once, a late workgroup still reads A_kk itself (the triangular inverse reads
 // the diagonal blocks from X).
-__global__ void __launch_bounds__(256)
+constexpr int CHOL_THREADS = 192;
+__global__ void __launch_bounds__(CHOL_THREADS)
     k_chol_step(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t k,
                 int32_t *__restrict__ status) {
   __shared__ __attribute__((aligned(16))) double Lt[DB * DB];  // Lt[j * 64 + m] = L_kk[m][j]
   __shared__ double rinv[DB];
+  __shared__ int ready;  // columns published
   const int t = threadIdx.x;
-  double *blk = A + k * DB * np + k * DB;
-  // this thread's part of the panel block, read now so that the read overlaps the diagonal
-  // block's factorisation (four lanes per row, 16 columns each)
-  const int p = t & 3;
-  double *ar = A + ((k + (blockIdx.x ? blockIdx.x : 1)) * DB + (t >> 2)) * np + k * DB + 16 * p;
-  double a[16];
-  if (blockIdx.x != 0) {
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const double2 v = *reinterpret_cast<const double2 *>(ar + j);
-      a[j] = v.x;
-      a[j + 1] = v.y;
-    }
-  }
+  if (t == 0) ready = 0;
+  __syncthreads();
   if (t < DB) {
     const int i = t;
+    const double *blk = A + k * DB * np + k * DB;
     double d[DB];
 #pragma unroll
     for (int j = 0; j < DB; j += 2) {
@@ -533,7 +540,11 @@ __global__ void __launch_bounds__(256)
       const double ljj = piv * rl;
       d[j] = i == j ? ljj : d[j] * rl;      // right of the diagonal, d holds unused values
       Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
-      if (i == j) rinv[j] = rl;
+      if (i == j) {  // the pivot's lane: 1 / L_jj, then column j is published
+        rinv[j] = rl;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __hip_atomic_store(&ready, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
       // the next pivot's column first, with L[j+1][j] read from lane j + 1 (off the LDS
       // round trip, which only the rest of the column waits for)
       if (j + 1 < DB) {
@@ -556,22 +567,34 @@ __global__ void __launch_bounds__(256)
         *reinterpret_cast<double2 *>(lk + (int64_t)i * np + j) =
             make_double2(j <= i ? d[j] : 0.0, j + 1 <= i ? d[j + 1] : 0.0);
     }
+    return;
   }
   if (blockIdx.x == 0) return;
-  __syncthreads();
+  // panel: lane h of row r owns columns 32 h .. 32 h + 31 (read now, so that the read
+  // overlaps the first columns of the factorisation)
+  const int tp = t - DB, r = tp >> 1, h = tp & 1;
+  double *ar = A + ((k + blockIdx.x) * DB + r) * np + k * DB + 32 * h;
+  double a[32];
+#pragma unroll
+  for (int j = 0; j < 32; j += 2) {
+    const double2 v = *reinterpret_cast<const double2 *>(ar + j);
+    a[j] = v.x;
+    a[j + 1] = v.y;
+  }
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
-    const int pj = j >> 4, jj = j & 15;
-    const double x_own = a[jj] * rinv[j];
-    const double x = quad_bcast(x_own, pj);
-    const double *lc = Lt + j * DB + 16 * p;  // L_kk[16 p + i][j], zero for 16 p + i < j
+    lds_wait_above(&ready, j);
+    const int pj = j >> 5, jj = j & 31;
+    const double x = pair_bcast(a[jj] * rinv[j], pj);
+    const double *lc = Lt + j * DB + 32 * h;  // L_kk[32 h + i][j], zero for 32 h + i < j
+    // from column 32 on, only the upper lane of a pair has columns right of j
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = fma(-x, lc[i], a[i]);
-    if (p == pj) a[jj] = x;
+    for (int i = (j < 32 ? 0 : jj + 1); i < 32; ++i) a[i] = fma(-x, lc[i], a[i]);
+    if (h == pj) a[jj] = x;
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
+  for (int j = 0; j < 32; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
 }
 
 // column block k + 1 only: A[bi][k+1] -= L[bi][k] L[k+1][k]^T for bi >= k + 1 (what step
@@ -731,10 +754,12 @@ int launch_gptq_factor(const float *H, int64_t n, double damp, double *U, int32_
   // K = 128 over the 128-aligned rest (128 x 128 tiles); an odd last step stands alone
   for (int64_t k = 0; k < nb; k += 2) {
     const int64_t T = nb - k - 1;
-    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(256), 0, st, A, X, np, k, stat);
+    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(T + 1)), dim3(CHOL_THREADS), 0, st, A, X, np, k,
+                       stat);
     if (T == 0) break;
     hipLaunchKernelGGL(k_chol_colupd, dim3((unsigned)T), dim3(256), 0, st, A, np, k);
-    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)T), dim3(256), 0, st, A, X, np, k + 1, stat);
+    hipLaunchKernelGGL(k_chol_step, dim3((unsigned)T), dim3(CHOL_THREADS), 0, st, A, X, np, k + 1,
+                       stat);
     const int64_t c = (k + 2) * DB;
     if (c >= np) break;
     const int64_t t2 = (np - c + T2 - 1) / T2;
