@@ -493,11 +493,11 @@ __device__ __forceinline__ void lds_wait_above(int *f, int j) {
 
 // Step k of the blocked Cholesky factorisation. Workgroups of three waves. Wave 0 of every
 // workgroup factors diagonal block k (lane i holds row i in registers; the pivot comes by
-// readlane, and each scaled column goes to LDS), and publishes column j by setting an LDS
-// counter to j + 1 once the column and 1 / L_jj are written. Workgroup 0 stores L_kk;
+// readlane, one column ahead, and each scaled column goes to LDS), and publishes column j
+// by setting an LDS counter to j + 1 once the column and 1 / L_jj are written. Workgroup 0 stores L_kk;
 // in workgroup b >= 1, waves 1 and 2 meanwhile solve the 64 rows of panel block k + b,
-// x L_kk^T = a, by forward substitution, one column behind the factorisation: two lanes per
-// row, 32 columns each, x_j shared in the pair by DPP. Every element sees the same fma
+// x L_kk^T = a, by forward substitution, a column pair behind the factorisation: two lanes
+// per row, 32 columns each, x_j shared in the pair by DPP. Every element sees the same fma
 // sequence as in a solve after the factorisation. The waits end: wave 0 runs all 64 columns
 // unconditionally (a bad pivot only sets the status), and waits only on itself. LDS
 // operations of one wave are performed in order, so a panel wave that reads the counter
@@ -525,18 +525,25 @@ __global__ void __launch_bounds__(CHOL_THREADS)
       d[j] = j <= i ? v.x : 0.0;
       d[j + 1] = j + 1 <= i ? v.y : 0.0;
     }
-    bool bad = false;
-#pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      const int plo = __builtin_amdgcn_readlane(__double2loint(d[j]), j);
-      const int phi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j);
-      const double piv = __hiloint2double(phi, plo);
-      bad |= !(piv > 0.0);
-      // 1 / sqrt(piv): the hardware estimate and two Newton steps (about 1 ulp), off the
-      // longer sqrt and divide sequences on this step's critical path
+    // 1 / sqrt(piv): the hardware estimate and two Newton steps (about 1 ulp), off the
+    // longer sqrt and divide sequences on this step's critical path
+    auto rsqrt_nr = [](double piv) {
       double rl = __builtin_amdgcn_rsq(piv);
       rl = rl * __builtin_fma(-0.5 * piv * rl, rl, 1.5);
       rl = rl * __builtin_fma(-0.5 * piv * rl, rl, 1.5);
+      return rl;
+    };
+    bool bad = false;
+    double piv, rl;  // pivot of column j and its 1 / sqrt, computed one column ahead
+    {
+      const int plo = __builtin_amdgcn_readlane(__double2loint(d[0]), 0);
+      const int phi = __builtin_amdgcn_readlane(__double2hiint(d[0]), 0);
+      piv = __hiloint2double(phi, plo);
+      bad |= !(piv > 0.0);
+      rl = rsqrt_nr(piv);
+    }
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
       const double ljj = piv * rl;
       d[j] = i == j ? ljj : d[j] * rl;      // right of the diagonal, d holds unused values
       Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
@@ -545,19 +552,27 @@ __global__ void __launch_bounds__(CHOL_THREADS)
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __hip_atomic_store(&ready, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      // the next pivot's column first, with L[j+1][j] read from lane j + 1 (off the LDS
-      // round trip, which only the rest of the column waits for)
+      // the next pivot first, with L[j+1][j] read from lane j + 1: column j + 1's only
+      // missing term, so its pivot and 1 / sqrt overlap the LDS round trip and the rest
+      // of the column's update
+      double pn = 0.0, rn = 0.0;
       if (j + 1 < DB) {
         const int slo = __builtin_amdgcn_readlane(__double2loint(d[j]), j + 1);
         const int shi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j + 1);
         d[j + 1] = fma(-d[j], __hiloint2double(shi, slo), d[j + 1]);
+        const int plo = __builtin_amdgcn_readlane(__double2loint(d[j + 1]), j + 1);
+        const int phi = __builtin_amdgcn_readlane(__double2hiint(d[j + 1]), j + 1);
+        pn = __hiloint2double(phi, plo);
+        bad |= !(pn > 0.0);
+        rn = rsqrt_nr(pn);
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       const double *col = Lt + j * DB;
 #pragma unroll
       for (int l = j + 2; l < DB; ++l) d[l] = fma(-d[j], col[l], d[l]);
-      __builtin_amdgcn_sched_barrier(0);
+      piv = pn;
+      rl = rn;
     }
     if (blockIdx.x == 0) {
       if (bad && i == 0) atomicCAS(status, 0, (int32_t)(1 + k));
@@ -581,9 +596,11 @@ __global__ void __launch_bounds__(CHOL_THREADS)
     a[j] = v.x;
     a[j + 1] = v.y;
   }
+  // columns in pairs: one counter read for both, and the second column's reads can be
+  // issued during the first one's update
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
-    lds_wait_above(&ready, j);
+    if ((j & 1) == 0) lds_wait_above(&ready, j + 1);
     const int pj = j >> 5, jj = j & 31;
     const double x = pair_bcast(a[jj] * rinv[j], pj);
     const double *lc = Lt + j * DB + 32 * h;  // L_kk[32 h + i][j], zero for 32 h + i < j
@@ -591,7 +608,6 @@ __global__ void __launch_bounds__(CHOL_THREADS)
 #pragma unroll
     for (int i = (j < 32 ? 0 : jj + 1); i < 32; ++i) a[i] = fma(-x, lc[i], a[i]);
     if (h == pj) a[jj] = x;
-    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int j = 0; j < 32; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
