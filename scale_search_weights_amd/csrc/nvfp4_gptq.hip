@@ -457,15 +457,26 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// value of lane `src` (0 or 1, a compile-time constant at every call) of this lane's pair
-__device__ __forceinline__ double pair_bcast(double x, int src) {
+// value of lane `src` of this lane's quad; src is a compile-time constant at every call
+__device__ __forceinline__ double quad_bcast(double x, int src) {
   int lo = __double2loint(x), hi = __double2hiint(x);
-  if (src == 0) {
-    lo = __builtin_amdgcn_mov_dpp(lo, 0xA0, 0xF, 0xF, false);  // quad_perm [0,0,2,2]
-    hi = __builtin_amdgcn_mov_dpp(hi, 0xA0, 0xF, 0xF, false);
-  } else {
-    lo = __builtin_amdgcn_mov_dpp(lo, 0xF5, 0xF, 0xF, false);  // quad_perm [1,1,3,3]
-    hi = __builtin_amdgcn_mov_dpp(hi, 0xF5, 0xF, 0xF, false);
+  switch (src) {
+    case 0:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x00, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x00, 0xF, 0xF, false);
+      break;
+    case 1:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0x55, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0x55, 0xF, 0xF, false);
+      break;
+    case 2:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xAA, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xAA, 0xF, 0xF, false);
+      break;
+    default:
+      lo = __builtin_amdgcn_mov_dpp(lo, 0xFF, 0xF, 0xF, false);
+      hi = __builtin_amdgcn_mov_dpp(hi, 0xFF, 0xF, 0xF, false);
+      break;
   }
   return __hiloint2double(hi, lo);
 }
@@ -491,32 +502,38 @@ __device__ __forceinline__ void lds_wait_above(int *f, int j) {
       : "scc", "memory");
 }
 
-// Step k of the blocked Cholesky factorisation. Workgroups of three waves. Wave 0 of every
-// workgroup factors diagonal block k (lane i holds row i in registers; the pivot comes by
-// readlane, one column ahead, and each scaled column goes to LDS), and publishes column j
-// by setting an LDS counter to j + 1 once the column and 1 / L_jj are written. Workgroup 0 stores L_kk;
-// in workgroup b >= 1, waves 1 and 2 meanwhile solve the 64 rows of panel block k + b,
-// x L_kk^T = a, by forward substitution, a column pair behind the factorisation: two lanes
-// per row, 32 columns each, x_j shared in the pair by DPP. Every element sees the same fma
-// sequence as in a solve after the factorisation. The waits end: wave 0 runs all 64 columns
-// unconditionally (a bad pivot only sets the status), and waits only on itself. LDS
-// operations of one wave are performed in order, so a panel wave that reads the counter
-// above j then reads column j and 1 / L_jj as written.
+// Step k of the blocked Cholesky factorisation. Workgroups of five waves. Wave 1 of every
+// workgroup factors diagonal block k (lane i holds row i in registers) in four panels of 16
+// columns: inside a panel column by column (pivot by readlane, its 1 / sqrt one column ahead,
+// each scaled column to LDS, updates only within the panel), then the panel's update of the
+// columns right of it, L_p L_p^T, on the fp64 matrix cores (16 x 16 tiles, K = 16, the same
+// fragments serving as A and B), back into the rows through LDS. It publishes column j by
+// setting an LDS counter to j + 1 once the column and 1 / L_jj are written. Workgroup 0
+// stores L_kk; in workgroup b >= 1 the other four waves meanwhile solve the 64 rows of panel
+// block k + b, x L_kk^T = a, by forward substitution a column pair behind the factorisation:
+// four lanes per row, 16 columns each, x_j shared in the quad by DPP. The waits end: the
+// factorising wave runs all 64 columns unconditionally (a bad pivot only sets the status)
+// and waits only on itself. LDS operations of one wave are performed in order, so a panel
+// wave that reads the counter above j then reads column j and 1 / L_jj as written. The
+// factorisation is on wave 1 because a fifth wave shares a SIMD with wave 0 (here a panel
+// wave); on wave 0 the step took 20.4 instead of 18.9 us.
 // L_kk goes to the same place in X, not back into A: with more workgroups than fit on the
 // device at once, a late workgroup still reads A_kk itself (the triangular inverse reads
 // the diagonal blocks from X).
-constexpr int CHOL_THREADS = 192;
+constexpr int CHOL_THREADS = 320;
+constexpr int CHOL_DIAG_WAVE = 1;
 __global__ void __launch_bounds__(CHOL_THREADS)
     k_chol_step(double *__restrict__ A, double *__restrict__ X, int64_t np, int64_t k,
                 int32_t *__restrict__ status) {
   __shared__ __attribute__((aligned(16))) double Lt[DB * DB];  // Lt[j * 64 + m] = L_kk[m][j]
+  __shared__ __attribute__((aligned(16))) double Ub[DB * DB];  // a panel's update, [row][col]
   __shared__ double rinv[DB];
   __shared__ int ready;  // columns published
   const int t = threadIdx.x;
   if (t == 0) ready = 0;
   __syncthreads();
-  if (t < DB) {
-    const int i = t;
+  if ((t >> 6) == CHOL_DIAG_WAVE) {
+    const int i = t & 63;
     const double *blk = A + k * DB * np + k * DB;
     double d[DB];
 #pragma unroll
@@ -534,64 +551,94 @@ __global__ void __launch_bounds__(CHOL_THREADS)
       return rl;
     };
     bool bad = false;
-    double piv, rl;  // pivot of column j and its 1 / sqrt, computed one column ahead
-    {
-      const int plo = __builtin_amdgcn_readlane(__double2loint(d[0]), 0);
-      const int phi = __builtin_amdgcn_readlane(__double2hiint(d[0]), 0);
+    double piv = 0.0, rl = 0.0;
+    auto pivot_of = [&](int j) {  // column j's pivot (final in lane j's d[j]) and its 1 / sqrt
+      const int plo = __builtin_amdgcn_readlane(__double2loint(d[j]), j);
+      const int phi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j);
       piv = __hiloint2double(phi, plo);
       bad |= !(piv > 0.0);
       rl = rsqrt_nr(piv);
-    }
+    };
 #pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      const double ljj = piv * rl;
-      d[j] = i == j ? ljj : d[j] * rl;      // right of the diagonal, d holds unused values
-      Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
-      if (i == j) {  // the pivot's lane: 1 / L_jj, then column j is published
-        rinv[j] = rl;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __hip_atomic_store(&ready, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-      // the next pivot first, with L[j+1][j] read from lane j + 1: column j + 1's only
-      // missing term, so its pivot and 1 / sqrt overlap the LDS round trip and the rest
-      // of the column's update
-      double pn = 0.0, rn = 0.0;
-      if (j + 1 < DB) {
-        const int slo = __builtin_amdgcn_readlane(__double2loint(d[j]), j + 1);
-        const int shi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j + 1);
-        d[j + 1] = fma(-d[j], __hiloint2double(shi, slo), d[j + 1]);
-        const int plo = __builtin_amdgcn_readlane(__double2loint(d[j + 1]), j + 1);
-        const int phi = __builtin_amdgcn_readlane(__double2hiint(d[j + 1]), j + 1);
-        pn = __hiloint2double(phi, plo);
-        bad |= !(pn > 0.0);
-        rn = rsqrt_nr(pn);
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      const double *col = Lt + j * DB;
+    for (int P = 0; P < 4; ++P) {
+      const int c0 = 16 * P;
+      pivot_of(c0);
 #pragma unroll
-      for (int l = j + 2; l < DB; ++l) d[l] = fma(-d[j], col[l], d[l]);
-      piv = pn;
-      rl = rn;
+      for (int j = c0; j < c0 + 16; ++j) {
+        const double ljj = piv * rl;
+        d[j] = i == j ? ljj : d[j] * rl;      // right of the diagonal, d holds unused values
+        Lt[j * DB + i] = i >= j ? d[j] : 0.0;  // column j of L_kk (zero above the diagonal)
+        if (i == j) {  // the pivot's lane: 1 / L_jj, then column j is published
+          rinv[j] = rl;
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __hip_atomic_store(&ready, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        if (j + 1 < c0 + 16) {
+          // the next pivot first: L[j+1][j] read from lane j + 1 is column j + 1's only
+          // missing term, so its pivot and 1 / sqrt overlap the LDS round trip and the rest
+          // of the panel's update
+          const int slo = __builtin_amdgcn_readlane(__double2loint(d[j]), j + 1);
+          const int shi = __builtin_amdgcn_readlane(__double2hiint(d[j]), j + 1);
+          d[j + 1] = fma(-d[j], __hiloint2double(shi, slo), d[j + 1]);
+          const double dj = d[j];
+          pivot_of(j + 1);
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          const double *col = Lt + j * DB;
+#pragma unroll
+          for (int l = j + 2; l < c0 + 16; ++l) d[l] = fma(-dj, col[l], d[l]);
+        }
+      }
+      if (P < 3) {
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        // fragment (tile t, step s): lane l holds L_kk[16 t + (l & 15)][c0 + 4 s + (l >> 4)]
+        auto frag = [&](int tt, int s) { return Lt[(c0 + 4 * s + (i >> 4)) * DB + 16 * tt + (i & 15)]; };
+#pragma unroll
+        for (int tm = P + 1; tm < 4; ++tm)
+#pragma unroll
+          for (int tn = P + 1; tn <= tm; ++tn) {
+            double fm[4], fn[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              fm[s] = frag(tm, s);
+              fn[s] = tn == tm ? fm[s] : frag(tn, s);
+            }
+            gq_v4d acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(fm[s], fn[s], acc, 0, 0, 0);
+            // D: lane l, register r holds row (l >> 4) + 4 r, column l & 15 of the tile
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ub[(16 * tm + (i >> 4) + 4 * r) * DB + 16 * tn + (i & 15)] = acc[r];
+          }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        // only l <= i matters; the rest of the row holds unused values
+#pragma unroll
+        for (int l = c0 + 16; l < DB; ++l) d[l] -= Ub[i * DB + l];
+      }
     }
     if (blockIdx.x == 0) {
       if (bad && i == 0) atomicCAS(status, 0, (int32_t)(1 + k));
       double *lk = X + k * DB * np + k * DB;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-      for (int j = 0; j < DB; j += 2)
+      for (int j = 0; j < DB; j += 2)  // from LDS (zero above the diagonal), so d dies early
         *reinterpret_cast<double2 *>(lk + (int64_t)i * np + j) =
-            make_double2(j <= i ? d[j] : 0.0, j + 1 <= i ? d[j + 1] : 0.0);
+            make_double2(Lt[j * DB + i], Lt[(j + 1) * DB + i]);
     }
     return;
   }
   if (blockIdx.x == 0) return;
-  // panel: lane h of row r owns columns 32 h .. 32 h + 31 (read now, so that the read
+  // panel: lane p of row r owns columns 16 p .. 16 p + 15 (read now, so that the read
   // overlaps the first columns of the factorisation)
-  const int tp = t - DB, r = tp >> 1, h = tp & 1;
-  double *ar = A + ((k + blockIdx.x) * DB + r) * np + k * DB + 32 * h;
-  double a[32];
+  const int tp = t >= 64 * (CHOL_DIAG_WAVE + 1) ? t - 64 : t;
+  const int p = tp & 3, r = tp >> 2;
+  double *ar = A + ((k + blockIdx.x) * DB + r) * np + k * DB + 16 * p;
+  double a[16];
 #pragma unroll
-  for (int j = 0; j < 32; j += 2) {
+  for (int j = 0; j < 16; j += 2) {
     const double2 v = *reinterpret_cast<const double2 *>(ar + j);
     a[j] = v.x;
     a[j + 1] = v.y;
@@ -601,16 +648,16 @@ __global__ void __launch_bounds__(CHOL_THREADS)
 #pragma unroll
   for (int j = 0; j < DB; ++j) {
     if ((j & 1) == 0) lds_wait_above(&ready, j + 1);
-    const int pj = j >> 5, jj = j & 31;
-    const double x = pair_bcast(a[jj] * rinv[j], pj);
-    const double *lc = Lt + j * DB + 32 * h;  // L_kk[32 h + i][j], zero for 32 h + i < j
-    // from column 32 on, only the upper lane of a pair has columns right of j
+    const int pj = j >> 4, jj = j & 15;
+    const double x = quad_bcast(a[jj] * rinv[j], pj);
+    const double *lc = Lt + j * DB + 16 * p;  // L_kk[16 p + i][j], zero for 16 p + i < j
+    // from column 48 on, only the last lane of a quad has columns right of j
 #pragma unroll
-    for (int i = (j < 32 ? 0 : jj + 1); i < 32; ++i) a[i] = fma(-x, lc[i], a[i]);
-    if (h == pj) a[jj] = x;
+    for (int i = (j < 48 ? 0 : jj + 1); i < 16; ++i) a[i] = fma(-x, lc[i], a[i]);
+    if (p == pj) a[jj] = x;
   }
 #pragma unroll
-  for (int j = 0; j < 32; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
+  for (int j = 0; j < 16; j += 2) *reinterpret_cast<double2 *>(ar + j) = make_double2(a[j], a[j + 1]);
 }
 
 // column block k + 1 only: A[bi][k+1] -= L[bi][k] L[k+1][k]^T for bi >= k + 1 (what step
