@@ -176,6 +176,23 @@ def test_gptq_factor_workspace_contents_unread(orc, n):
     assert torch.equal(U0, Un)
 
 
+def test_gptq_factor_bitwise_repeatable():
+    """The Cholesky step's waves hand the diagonal block's columns to the panel waves through
+    an LDS counter; a missed handoff would read a column before it is written and show up as
+    run-to-run differences. Sixteen factors of the same H (n = 1040: 17 steps, from 16 panel
+    blocks down to none, the last step without a partner) must agree bit for bit."""
+    n = 1040
+    case(f"gptq factor n={n}: 16 repeated runs, bit for bit")
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((2 * n, 1)) + rng.standard_normal((2 * n, n))
+    H = torch.from_numpy((X.T @ X).astype(np.float32)).to(DEV)
+    U0, s0 = nvfp4.gptq_factor(H, 0.01)
+    assert s0.item() == 0
+    for _ in range(15):
+        U, st = nvfp4.gptq_factor(H, 0.01)
+        assert st.item() == 0 and torch.equal(U, U0)
+
+
 # ------------------------------------------------------------------ GPTQ rows
 
 def test_gptq_factor_more_workgroups_than_fit():
