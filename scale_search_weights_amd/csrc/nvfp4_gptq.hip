@@ -377,30 +377,85 @@ __device__ __forceinline__ void d2_gemm_sub(double *C, int64_t ldc, int mlim, in
 }
 
 // ------------------------------------------------------------------ factor
-// hdr[0] = lambda, hdr[1] = 1 if diag(H) sums to zero (then H + lambda I := I)
+// hdr[0] = lambda, hdr[1] = 1 if diag(H) sums to zero (then H + lambda I := I).
+// lambda takes the diagonal's sum in index order. When every partial sum of it, in any
+// order, is exact in double, a tree sum has the same bits and replaces the 4096-step chain
+// of dependent adds: each diagonal entry is an integer multiple of 2^qlo (its lowest set
+// bit) with magnitude below 2^(qhi + 1), so every partial sum is a multiple of 2^qlo
+// (the smallest qlo) below n 2^(qhi + 1) (the largest qhi); if that is at most 2^53 units
+// of 2^qlo, all of them are exact. Otherwise, or with a non-finite entry, the sum runs in
+// index order.
+__device__ __forceinline__ double block_sum256(double v, double *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
 __global__ void __launch_bounds__(256)
     k_gptq_lambda(const float *__restrict__ H, int64_t n, double damp, double *__restrict__ hdr,
                   int32_t *__restrict__ status) {
   __shared__ double dg[4096];
-  double tr = 0.0;
-  for (int64_t base = 0; base < n; base += 4096) {
-    const int64_t m = n - base < 4096 ? n - base : 4096;
-    float h[16];  // this thread's diagonal entries of the chunk, all reads in flight at once
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int64_t i = s * 256 + threadIdx.x;
-      h[s] = i < m ? H[(base + i) * n + base + i] : 0.0f;
+  __shared__ int qred[3][4];
+  __shared__ double red[4];
+  const int t = threadIdx.x;
+  int qlo = 1 << 20, qhi = -(1 << 20), bad = 0;
+  double part = 0.0;  // this thread's entries, summed in any order (used only when exact)
+  for (int64_t i = t; i < n; i += 256) {
+    const float h = H[i * n + i];
+    const unsigned u = __float_as_uint(h) & 0x7FFFFFFFu;
+    if (u >= 0x7F800000u) {
+      bad = 1;
+    } else if (u != 0u) {
+      const int E = (int)(u >> 23);
+      const unsigned m = E ? ((u & 0x7FFFFFu) | 0x800000u) : u;  // |h| = m 2^(max(E,1) - 150)
+      const int e0 = (E ? E : 1) - 150;
+      qlo = min(qlo, e0 + __builtin_ctz(m));
+      qhi = max(qhi, e0 + 31 - __builtin_clz(m));
     }
-#pragma unroll
-    for (int s = 0; s < 16; ++s) dg[s * 256 + threadIdx.x] = (double)h[s];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-#pragma unroll 16
-      for (int64_t i = 0; i < m; ++i) tr += dg[i];  // index order
-    }
-    __syncthreads();
+    part += (double)h;
   }
-  if (threadIdx.x == 0) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    qlo = min(qlo, __shfl_xor(qlo, off, 64));
+    qhi = max(qhi, __shfl_xor(qhi, off, 64));
+    bad |= __shfl_xor(bad, off, 64);
+  }
+  if ((t & 63) == 0) {
+    qred[0][t >> 6] = qlo;
+    qred[1][t >> 6] = qhi;
+    qred[2][t >> 6] = bad;
+  }
+  __syncthreads();
+  qlo = min(min(qred[0][0], qred[0][1]), min(qred[0][2], qred[0][3]));
+  qhi = max(max(qred[1][0], qred[1][1]), max(qred[1][2], qred[1][3]));
+  bad = qred[2][0] | qred[2][1] | qred[2][2] | qred[2][3];
+  const int lg = n > 1 ? 64 - __builtin_clzll((unsigned long long)(n - 1)) : 0;  // ceil(log2 n)
+  const bool any_order = !bad && (qhi < qlo || lg + qhi + 1 - qlo <= 53);
+  double tr = 0.0;
+  if (any_order) {
+    tr = block_sum256(part, red);
+  } else {
+    for (int64_t base = 0; base < n; base += 4096) {
+      const int64_t m = n - base < 4096 ? n - base : 4096;
+      float h[16];  // this thread's diagonal entries of the chunk, all reads in flight at once
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int64_t i = s * 256 + t;
+        h[s] = i < m ? H[(base + i) * n + base + i] : 0.0f;
+      }
+#pragma unroll
+      for (int s = 0; s < 16; ++s) dg[s * 256 + t] = (double)h[s];
+      __syncthreads();
+      if (t == 0) {
+#pragma unroll 16
+        for (int64_t i = 0; i < m; ++i) tr += dg[i];  // index order
+      }
+      __syncthreads();
+    }
+  }
+  if (t == 0) {
     hdr[0] = damp * (tr / (double)n);
     hdr[1] = tr == 0.0 ? 1.0 : 0.0;
     *status = 0;

@@ -176,6 +176,50 @@ def test_gptq_factor_workspace_contents_unread(orc, n):
     assert torch.equal(U0, Un)
 
 
+def _exact_any_order(diag_f32):
+    """True when every partial sum of these fp32 values, in any order, is exact in double:
+    each is an integer multiple of 2^qlo (its lowest set bit) below 2^(qhi + 1), so partial
+    sums stay below n 2^(qhi + 1) in units of the smallest 2^qlo."""
+    u = diag_f32.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    u = u[u != 0]
+    if u.size == 0:
+        return True
+    E = (u >> np.uint32(23)).astype(np.int64)
+    m = np.where(E > 0, (u & np.uint32(0x7FFFFF)) | np.uint32(0x800000), u).astype(np.int64)
+    e0 = np.maximum(E, 1) - 150
+    lo = np.array([int(x & -x).bit_length() - 1 for x in m]) + e0
+    hi = np.array([int(x).bit_length() - 1 for x in m]) + e0
+    n = diag_f32.size
+    return (n - 1).bit_length() + int(hi.max()) + 1 - int(lo.min()) <= 53
+
+
+@pytest.mark.parametrize("spread", [False, True])
+def test_gptq_factor_damping_in_index_order(orc, spread):
+    """lambda = damp * (sum of diag H in index order) / n, bit for bit, read from the first
+    word of the factor's workspace (where the factor keeps it). A diagonal within a narrow
+    exponent range takes a tree sum (every partial sum exact); a diagonal spread over 2^-80 to
+    2^26 takes the index-order chain. Both must give the index-order sum's bits."""
+    n = 1040
+    case(f"gptq factor n={n}: damping sum, {'wide' if spread else 'narrow'} diagonal range")
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((2 * n, n))
+    H = X.T @ X / (2 * n)
+    if spread:
+        d = np.logspace(-12, 4, n)
+        H = d[:, None] * H * d[None, :]
+    H = H.astype(np.float32)
+    diag = np.ascontiguousarray(np.diagonal(H))
+    assert _exact_any_order(diag) != spread
+    need = int(nvfp4.lib().nvfp4_gptq_factor_workspace_size(n))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    _, status = nvfp4.gptq_factor(torch.from_numpy(H).to(DEV), 0.01, workspace=ws)
+    assert status.item() == 0
+    tr = 0.0
+    for v in diag.tolist():  # index order, in double
+        tr += v
+    assert ws[:8].view(torch.float64).item() == 0.01 * (tr / n)
+
+
 def test_gptq_factor_bitwise_repeatable():
     """The Cholesky step's waves hand the diagonal block's columns to the panel waves through
     an LDS counter; a missed handoff would read a column before it is written and show up as
