@@ -5,12 +5,13 @@
 // This is a dense contraction over tokens (2 T C^2 flops), so it runs on the matrix cores:
 //  * only tiles on or above the diagonal are computed (256 x 256 channels each, eight
 //    waves of 64 x 128); the reduction mirrors them, so H comes out exactly symmetric;
-//  * tokens are split into chunks (16 or 8 for long inputs); each (chunk, tile) writes a
-//    partial tile, and k_gram_reduce adds the partials in chunk order (deterministic);
-//  * each XCD (with its own L2) takes whole chunks and walks their tiles row by row, so
-//    the workgroups running together on it share their row panel and stream the same
-//    token rows (spreading every chunk over all XCDs fetched X twelve times over; this
-//    fetches it about four times).
+//  * tokens are split into chunks (8 to 16 for long inputs: the count whose workgroups fill
+//    whole rounds best); each (chunk, tile) writes a partial tile, and k_gram_reduce adds
+//    the partials in chunk order (deterministic);
+//  * each XCD (with its own L2) takes a contiguous range of (chunk, tile) units and walks
+//    the tiles row by row, so the workgroups running together on it share their row panel
+//    and stream the same token rows (spreading every chunk over all XCDs fetched X twelve
+//    times over; this fetches it about four times).
 //
 // bf16: v_mfma_f32_32x32x16_bf16. A lane's operand is 8 consecutive tokens of one channel,
 // while a token row is contiguous in memory. The token rows go into LDS as they are (raw
@@ -48,9 +49,11 @@ static int gram_cus() {
 
 constexpr int GXCD = 8;  // XCDs; workgroups are dispatched to them round-robin
 
-// Token chunks per tile: 16 or 8 when the tokens allow chunks of at least 2048 (then each
-// XCD takes whole chunks, so its L2 streams only those rows), else as many as fill whole
-// rounds of one workgroup per CU best; one when the tiles alone number four per CU.
+// Token chunks per tile: for long inputs (chunks of at least 2048 tokens possible) the count
+// in 8..16 whose workgroups fill whole rounds of one per CU best (the time is about the
+// rounds times a round's length, which falls as 1/chunks; 15 chunks of 136 tiles make 8
+// full rounds where 16 made 8.5); else as many as fill whole rounds of one workgroup per CU
+// best; one when the tiles alone number four per CU.
 static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   GramGeom g;
   g.nt = (cols + GT - 1) / GT;
@@ -62,38 +65,48 @@ static GramGeom gram_geom(int64_t tokens, int64_t cols, int cus) {
   // would multiply the partial-tile workspace without adding useful parallelism)
   if (g.tiles >= 4 * (int64_t)cus) max_nc = 1;
   if (max_nc < 1) max_nc = 1;
-  const bool by_xcd = max_nc >= 8;
-  int64_t best = max_nc >= 16 ? 16 : (max_nc >= 8 ? 8 : 1);
-  double best_eff = -1.0;
-  for (int64_t nc = 1; nc <= max_nc && !by_xcd; ++nc) {
-    const int64_t wgs = g.tiles * nc;
-    const int64_t rounds = (wgs + cus - 1) / cus;
-    const double eff = (double)wgs / (double)(rounds * cus);
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best = nc;
+  int64_t best = 1;
+  double best_t = -1.0;
+  if (max_nc >= 8) {
+    for (int64_t nc = 8; nc <= max_nc; ++nc) {
+      const double t = (double)((g.tiles * nc + cus - 1) / cus) / (double)nc;
+      if (best_t < 0.0 || t < best_t - 1e-12) {
+        best_t = t;
+        best = nc;
+      }
+    }
+  } else {
+    double best_eff = -1.0;
+    for (int64_t nc = 1; nc <= max_nc; ++nc) {
+      const int64_t wgs = g.tiles * nc;
+      const int64_t rounds = (wgs + cus - 1) / cus;
+      const double eff = (double)wgs / (double)(rounds * cus);
+      if (eff > best_eff + 1e-9) {
+        best_eff = eff;
+        best = nc;
+      }
     }
   }
   const int64_t spc = (steps + best - 1) / best > 0 ? (steps + best - 1) / best : 1;
   g.tc = spc * GK;
   g.nc = tokens > 0 ? (tokens + g.tc - 1) / g.tc : 1;
-  if (by_xcd && g.nc % GXCD != 0) g.nc = (g.nc + GXCD - 1) / GXCD * GXCD;  // empty tail chunks
   return g;
 }
 
-// workgroup -> (token chunk, tile). With nc % 8 == 0, XCD x (= wid % 8) takes chunks
-// x, x + 8, ...; its workgroups walk the tiles row by row, so the ones running together
-// share their row panel. Otherwise chunk-major.
+// workgroup -> (token chunk, tile): the (chunk, tile) units in chunk-major order, tiles row
+// by row, are cut into GXCD contiguous ranges, and XCD x (= wid % GXCD) walks range x, so
+// the workgroups running together on an XCD share their row panel and stream the same token
+// rows. A workgroup past the last unit gets chunk >= nc and returns.
 __device__ __forceinline__ void gram_work(int64_t wid, int64_t tiles, int64_t nc, int64_t &chunk,
                                           int64_t &tile) {
-  if (nc % GXCD == 0) {
-    const int64_t x = wid % GXCD, slot = wid / GXCD;
-    chunk = x + GXCD * (slot / tiles);
-    tile = slot % tiles;
-  } else {
-    chunk = wid / tiles;
-    tile = wid % tiles;
-  }
+  const int64_t per = (nc * tiles + GXCD - 1) / GXCD;
+  const int64_t u = (wid % GXCD) * per + wid / GXCD;
+  chunk = u / tiles;
+  tile = u % tiles;
+}
+
+static int64_t gram_grid(const GramGeom &g) {
+  return GXCD * ((g.nc * g.tiles + GXCD - 1) / GXCD);
 }
 
 size_t gram_workspace_size(int64_t tokens, int64_t cols) {
@@ -132,6 +145,7 @@ __global__ void __launch_bounds__(GTHREADS)
   __shared__ __attribute__((aligned(16))) char st0[GSTAGE], st1[GSTAGE], st2[GSTAGE], st3[GSTAGE];
   int64_t chunk, tile, ti, tj;
   gram_work(blockIdx.x, tiles, nc, chunk, tile);
+  if (chunk >= nc) return;
   gram_tile(tile, nt, ti, tj);
   const int64_t p0 = chunk * tc;
   const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
@@ -252,6 +266,7 @@ __global__ void __launch_bounds__(GTHREADS)
   __shared__ __attribute__((aligned(16))) float lds[2][GKF * GC];
   int64_t chunk, tile, ti, tj;
   gram_work(blockIdx.x, tiles, nc, chunk, tile);
+  if (chunk >= nc) return;
   gram_tile(tile, nt, ti, tj);
   const int64_t p0 = chunk * tc;
   const int64_t p1 = p0 + tc < tokens ? p0 + tc : tokens;
@@ -383,7 +398,7 @@ int launch_full_hessian(const void *x, int dtype, int64_t tokens, int64_t cols, 
                         int accumulate, void *workspace, hipStream_t st) {
   const GramGeom g = gram_geom(tokens, cols, gram_cus());
   float *partial = static_cast<float *>(workspace);
-  const dim3 grid((unsigned)(g.nc * g.tiles));
+  const dim3 grid((unsigned)gram_grid(g));
   if (dtype == NVFP4_DTYPE_BF16)
     hipLaunchKernelGGL(k_gram_bf16, grid, dim3(GTHREADS), 0, st, static_cast<const uint16_t *>(x),
                        tokens, cols, g.nt, g.tiles, g.nc, g.tc, partial);
