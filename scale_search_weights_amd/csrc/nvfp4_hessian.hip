@@ -749,7 +749,8 @@ int launch_block_hessian(const void *x, int dtype, int64_t tokens, int64_t cols,
 //  1. k_route_count: per (chunk, expert) counts, from LDS counters;
 //  2. k_route_scan: one workgroup turns them into per-expert offsets and per-(chunk,
 //     expert) bases (experts in blocks of up to 1024, chunks split into segments);
-//  3. k_route_scatter: every pair writes its token at base + rank.
+//  3. k_route_scatter: every pair writes its token at base + rank (rank: a per-expert
+//     prefix of the chunk's word popcounts plus one popcount).
 
 static inline int route_words(int64_t experts) {
   int64_t w = 16384 / (experts > 0 ? experts : 1);
@@ -862,13 +863,30 @@ __global__ void __launch_bounds__(256)
     if (e >= 0 && e < E) atomicOr(&bm[e * W + (i >> 5)], 1u << (i & 31));
   }
   __syncthreads();
+  // pre[e][w]: the expert's pairs in words 0 .. w - 1 (an exclusive scan of the words'
+  // popcounts), so a pair's rank is one lookup and one popcount; a wave scans floor(64 / W)
+  // experts' rows at a time, lane l holding word l % W of row l / W
+  unsigned *pre = bm + E * W;
+  {
+    const int lane = threadIdx.x & 63, rows = 64 / W, r = lane / W, wl = lane % W;
+    for (int e0 = (threadIdx.x >> 6) * rows; e0 < E; e0 += (blockDim.x >> 6) * rows) {
+      const int e = e0 + r;
+      const bool on = r < rows && e < E;
+      const int c = on ? __popc(bm[e * W + wl]) : 0;
+      int v = c;
+      for (int d = 1; d < W; d <<= 1) {
+        const int o = __shfl_up(v, d, 64);
+        v += wl >= d ? o : 0;
+      }
+      if (on) pre[e * W + wl] = (unsigned)(v - c);
+    }
+  }
+  __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int e = ids[i0 + i];
     if (e < 0 || e >= E) continue;
     const int wd = i >> 5;
-    const unsigned *row = bm + e * W;
-    int rank = __popc(row[wd] & ((1u << (i & 31)) - 1u));
-    for (int w = 0; w < wd; ++w) rank += __popc(row[w]);
+    const int rank = (int)pre[e * W + wd] + __popc(bm[e * W + wd] & ((1u << (i & 31)) - 1u));
     token_ids[base[chunk * E + e] + rank] = (int32_t)((i0 + i) / topk);
   }
 }
@@ -885,8 +903,8 @@ int launch_route_groups(const int32_t *expert_ids, int64_t tokens, int64_t topk,
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, st, counts, chunks, E, offsets);
   if (chunks > 0)
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)chunks), dim3(256),
-                       sizeof(unsigned) * (size_t)E * (size_t)W, st, expert_ids, pairs, (int)topk,
-                       E, W, counts, token_ids);
+                       2 * sizeof(unsigned) * (size_t)E * (size_t)W, st, expert_ids, pairs,
+                       (int)topk, E, W, counts, token_ids);
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
