@@ -802,8 +802,18 @@ __global__ void __launch_bounds__(1024)
     const bool on = sg < SEG && e < E;
     const int64_t c0 = sg * L, c1 = min(chunks, c0 + L);
     int32_t sum = 0;
+    // the segment's first RK counts stay in registers for the write pass below (all read at
+    // once; read again there they were a chain of dependent round trips)
+    constexpr int RK = 32;
+    int32_t keep[RK];
+    int32_t *const seg = counts + (on ? c0 * E + e : 0);  // count c0 + k at seg[k * E]
+    const int nk = on ? (int)min((int64_t)RK, c1 - c0) : 0;
+#pragma unroll
+    for (int k = 0; k < RK; ++k) keep[k] = k < nk ? seg[k * E] : 0;
+#pragma unroll
+    for (int k = 0; k < RK; ++k) sum += keep[k];
     if (on) {
-      int64_t c = c0;
+      int64_t c = c0 + RK;
       for (; c + 8 <= c1; c += 8) {
         int32_t v[8];
 #pragma unroll
@@ -837,7 +847,12 @@ __global__ void __launch_bounds__(1024)
       const int32_t ebase = carry + (el > 0 ? tot[el - 1] : 0);
       if (sg == 0) offsets[e] = ebase;
       int32_t run = ebase + pre;
-      for (int64_t c = c0; c < c1; ++c) {
+#pragma unroll
+      for (int k = 0; k < RK; ++k) {
+        if (k < nk) seg[k * E] = run;
+        run += keep[k];
+      }
+      for (int64_t c = c0 + RK; c < c1; ++c) {
         const int32_t v = counts[c * E + e];
         counts[c * E + e] = run;
         run += v;
